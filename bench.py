@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of one full-shape DeepSeek-V4-Flash MoE layer on one MI355X.
+
+A step is one moe_forward call (route, permute, routed MXFP4 experts, int8
+shared expert, combine) over one batch of T fresh seeded bf16 tokens, with
+every input already resident in HBM. Default workload: single-token decode
+(T=1) on the full-shape layer (hidden 4096, 256 experts, top-6, intermediate
+2048, MXFP4 routed experts, int8 shared expert), 1000 timed steps after 50
+warm-up steps. The weights are replicated ``--copies`` times and the steps
+rotate through the copies, so the 256 MB last-level cache cannot keep the
+shared expert and router warm from one step to the next.
+
+Prints one JSON line: the throughput (tokens/s), the roofline of the dominant
+kernel (its duration measured with HIP events on the launch stream over the
+timed region), and the CPU oracle's rate on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at T=1/64/8192; % of HBM BW (decode) / bf16 MFMA peak"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+
+DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel, bound
+    "decode_t1": (1000, 50, 12, "routed_w13", "hbm"),
+    "decode_t64": (200, 20, 12, "routed_w13", "hbm"),
+    "prefill_t8192": (20, 3, 1, "routed_w13", "mfma"),
+    "hash_t4096": (20, 3, 1, "routed_w13", "mfma"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_t1", choices=sorted(DEFAULTS))
+    ap.add_argument("--copies", type=int, default=None, help="weight copies rotated through")
+    ap.add_argument("--mode", default="graph", choices=["graph", "eager"],
+                    help="graph: steps captured in HIP graphs and replayed; eager: one launch sequence per step")
+    ap.add_argument("--graph-steps", type=int, default=50, help="steps per captured graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark makes itself (events)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        # hipEventDisableSystemFence: a timing-only event; recording it does not
+        # write back and invalidate the caches, so it does not perturb the kernel
+        ev = ctypes.c_void_p()
+        if self.L.hipEventCreateWithFlags(ctypes.byref(ev), 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.L.hipEventDestroy(ev)
+
+
+def algorithmic(wl, ids_np):
+    """Per-step algorithmic work of the layer and of the routed w13 kernel.
+
+    Bytes: every distinct routed expert's MXFP4 codes + scales (w13 and w2),
+    the shared expert's int8 weights + scales, the router weight and bias,
+    the tokens in and the output out. Flops: 2 per multiply-add of the
+    expert GEMMs (routed slots and shared expert), router separately."""
+    H, I, E, k = wl.H, wl.I, wl.E, wl.k
+    w13_exp = 2 * I * (H // 2) + 2 * I * (H // 32)
+    w2_exp = H * (I // 2) + H * (I // 32)
+    shared = 2 * I * H + 2 * I * 4 + H * I + H * 4
+    router = E * H * 4 + E * 4
+    T = ids_np.shape[1]
+    D = [len(set(s.ravel().tolist())) for s in ids_np]
+    Dm = sum(D) / len(D)
+    slots = T * k
+    layer_bytes = Dm * (w13_exp + w2_exp) + shared + router + T * H * 2 + T * H * 2
+    w13_bytes = Dm * w13_exp + slots * H * 2 + slots * I * 2  # weights + gathered x + h out
+    flops_w13 = 2.0 * slots * H * 2 * I
+    flops = 2.0 * slots * (H * 2 * I + I * H) + 2.0 * T * (H * 2 * I + I * H)
+    return dict(distinct_experts=Dm, layer_bytes=layer_bytes, w13_bytes=w13_bytes, w13_flops=flops_w13,
+                layer_flops=flops, router_flops=2.0 * T * E * H)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed counter
+    summaries, if they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(layer, batches, tids, budget_s):
+    """Time the CPU oracle on whole token batches of this workload until the
+    budget is spent (sampled rows for large batches)."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.lib().or_num_threads() if hasattr(oracle.lib(), "or_num_threads") else os.cpu_count()
+    T = batches[0].shape[0]
+    rows = None if T <= 64 else np.linspace(0, T - 1, 8).astype(np.int32)
+    done_tokens, t0, i = 0, time.perf_counter(), 0
+    outs = []
+    while True:
+        xb = batches[i % len(batches)]
+        tb = None if tids is None else tids[i % len(tids)]
+        r = oracle.forward(layer, xb, token_ids=tb, rows=rows)
+        outs.append((i % len(batches), rows, r["out"]))
+        done_tokens += T if rows is None else len(rows)
+        i += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    sample = (f"{done_tokens} tokens: {i} batch(es) of T={T}" +
+              ("" if rows is None else f", {len(rows)} sampled rows each (route + experts + shared)"))
+    return dict(value=done_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
+                seconds=round(dt, 2)), outs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_amd as mx
+    import synth
+
+    steps0, warm0, copies0, kernel, bound = DEFAULTS[args.workload]
+    K = args.steps if args.steps is not None else steps0
+    W = args.warmup if args.warmup is not None else warm0
+    C = max(1, args.copies if args.copies is not None else copies0)
+    wl = synth.WORKLOADS[args.workload]
+    T, H, E, k = wl.T, wl.H, wl.E, wl.k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = mx.config_of(wl)
+    t_gen = time.perf_counter()
+    layer = synth.make_layer(wl)
+    t_gen = time.perf_counter() - t_gen
+    base = mx.DeviceLayer.from_host(layer, dev)
+    copies = [base] + [mx.DeviceLayer(*[None if t is None else t.clone() for t in vars(base).values()])
+                       for _ in range(C - 1)]
+    nb = min(K + W, max(2, (1 << 27) // (T * H)))
+    batches = [synth.make_tokens(wl, rep=r) for r in range(nb)]
+    tids = [synth.make_token_ids(wl, rep=r) for r in range(nb)] if wl.hash_layer else None
+    x_dev = torch.stack([mx.bf16_from_numpy(b, dev) for b in batches])
+    t_dev = torch.stack([torch.from_numpy(t).to(dev) for t in tids]) if tids else None
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ids_all = torch.empty(K, T, k, dtype=torch.int32, device=dev)
+    w_all = torch.empty(K, T, k, dtype=torch.float32, device=dev)
+    ws = mx.Workspace(dev)
+    buf = ws.get(cfg, T)
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+
+    def call_args(step):
+        D = copies[step % C]
+        xb = x_dev[step % nb]
+        tb = None if t_dev is None else t_dev[step % nb]
+        ids = ids_all[step % K]
+        w = w_all[step % K]
+        P = mx._ptr
+        return (ctypes.byref(cfg), T, P(xb), P(D.gate_w), P(D.bias), P(D.logit_offset), P(tb),
+                P(D.tid2eid if tb is not None else None), 0 if D.tid2eid is None else D.tid2eid.shape[0],
+                P(D.w13_codes), P(D.w13_scales), P(D.w2_codes), P(D.w2_scales), P(D.sh_w13), P(D.sh_w13_scale),
+                P(D.sh_w2), P(D.sh_w2_scale), P(out), 0, P(ids), P(w), P(buf), buf.numel(),
+                ctypes.c_void_p(stream.cuda_stream))
+
+    argv = [call_args(s) for s in range(max(K, W))]
+
+    def step(s):
+        rc = L.moe_forward(*argv[s])
+        if rc != 0:
+            raise mx.MoEError(rc, "moe_forward")
+
+    hip = Hip()
+    ev_a = [hip.event() for _ in range(K)]
+    ev_b = [hip.event() for _ in range(K)]
+
+    # warm-up (also checks the path runs)
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize(dev)
+
+    # eager timed pass: kernel events bracket the dominant kernel on every step
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0.record(stream)
+    for s in range(K):
+        mx.set_kernel_events(kernel, ev_a[s], ev_b[s])
+        step(s)
+    t1.record(stream)
+    mx.set_kernel_events(None)
+    torch.cuda.synchronize(dev)
+    eager_ms = t0.elapsed_time(t1)
+    kern_ms = [hip.elapsed_ms(ev_a[s], ev_b[s]) for s in range(K)]
+    kern_avg_ms = sum(kern_ms) / K
+
+    graph_ms = None
+    if args.mode == "graph":
+        G = max(1, min(args.graph_steps, K))
+        graphs = []
+        cs = torch.cuda.Stream(dev)
+        with torch.cuda.stream(cs):
+            argv_g = [list(a) for a in argv]
+            for a in argv_g:
+                a[-1] = ctypes.c_void_p(cs.cuda_stream)
+            for g0 in range(0, K, G):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cs):
+                    for s in range(g0, min(K, g0 + G)):
+                        rc = L.moe_forward(*argv_g[s])
+                        if rc != 0:
+                            raise mx.MoEError(rc, "moe_forward (capture)")
+                graphs.append(gr)
+        torch.cuda.synchronize(dev)
+        for gr in graphs[:1]:  # warm replay
+            gr.replay()
+        torch.cuda.synchronize(dev)
+        t0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        t1.record(stream)
+        torch.cuda.synchronize(dev)
+        graph_ms = t0.elapsed_time(t1)
+
+    total_ms = graph_ms if graph_ms is not None else eager_ms
+    ms_step = total_ms / K
+    ids_np = ids_all.cpu().numpy()
+    alg = algorithmic(wl, ids_np)
+    value = T * K / (total_ms / 1e3)
+    if bound == "hbm":
+        achieved = alg["w13_bytes"] / (kern_avg_ms / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    else:
+        achieved = alg["w13_flops"] / (kern_avg_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    traffic = traffic_from_profiles(args.workload)
+    roof["traffic"] = traffic
+    roof["kernel"] = f"k_skinny<mxfp4,w13> ({kernel})"
+    roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
+    layer_bw = alg["layer_bytes"] / (ms_step / 1e3) / 1e9
+    layer_tf = alg["layer_flops"] / (ms_step / 1e3) / 1e12
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "hidden_size": H, "n_routed_experts": E, "top_k": k,
+                   "moe_intermediate": wl.I, "routed": "mxfp4 (E2M1 + E8M0/32)", "shared": "int8 per-channel",
+                   "weight_copies": C, "mode": args.mode, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"bytes_per_step": int(alg["layer_bytes"]), "hbm_GBps": round(layer_bw, 1),
+                  "hbm_frac": round(layer_bw / PEAK_HBM_GBS, 4), "flops_per_step": alg["layer_flops"],
+                  "mfma_TFLOPs": round(layer_tf, 2), "mfma_frac": round(layer_tf / PEAK_BF16_TFLOPS, 4),
+                  "distinct_experts": round(alg["distinct_experts"], 2), "eager_ms_per_step": round(eager_ms / K, 5),
+                  "graph_ms_per_step": None if graph_ms is None else round(graph_ms / K, 5)},
+        "gen_seconds": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        cb, outs = cpu_baseline(layer, batches, tids, args.cpu_seconds)
+        rec["cpu_baseline"] = cb
+        # parity of the sampled tokens (fp32 output of the same kernels)
+        import oracle as _o  # noqa: F401
+
+        errs = []
+        for bi, rows, ref in outs[:4]:
+            xb = x_dev[bi]
+            tb = None if t_dev is None else t_dev[bi]
+            o32 = mx.forward(cfg, xb, copies[0], token_ids=tb, out_fp32=True, ws=ws)
+            g = o32.cpu().double().numpy()
+            g = g if rows is None else g[rows]
+            errs.append(float(np.linalg.norm(g - ref) / np.linalg.norm(ref)))
+        rec["parity_rel_l2_max"] = max(errs)
+    else:
+        rec["cpu_baseline"] = None
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

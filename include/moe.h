@@ -155,6 +155,27 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernels that moe_set_kernel_events can bracket. */
+enum {
+  MOE_KERNEL_NONE = 0,
+  MOE_KERNEL_ROUTER = 1,       /* router logits (+ top-k, + small-T permutation) */
+  MOE_KERNEL_PERMUTE = 2,      /* multi-block permutation (large T only) */
+  MOE_KERNEL_ROUTED_W13 = 3,   /* routed experts: MXFP4 w13 + clamped SwiGLU */
+  MOE_KERNEL_ROUTED_W2 = 4,    /* routed experts: MXFP4 w2 x routing weight */
+  MOE_KERNEL_SHARED_W13 = 5,   /* shared expert: int8 w13 + clamped SwiGLU */
+  MOE_KERNEL_SHARED_W2 = 6,    /* shared expert: int8 w2 */
+  MOE_KERNEL_COMBINE = 7       /* weighted sum of the slots + shared expert */
+};
+
+/* Diagnostics for measurement (not part of the layer): from now on, every
+ * launch of `kernel_id` made by moe_forward / moe_expert_ffn is bracketed by
+ * hipEventRecord(start_event) and hipEventRecord(stop_event) on the call's
+ * stream, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * start_event/stop_event are hipEvent_t created by the caller; pass
+ * MOE_KERNEL_NONE (or NULL events) to stop. Process-wide setting, not
+ * thread-safe: meant for a benchmark driving one stream. */
+int moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

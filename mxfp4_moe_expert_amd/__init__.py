@@ -21,6 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+KERNELS = {"router": 1, "permute": 2, "routed_w13": 3, "routed_w2": 4, "shared_w13": 5, "shared_w2": 6,
+           "combine": 7}
 
 
 class MoEError(RuntimeError):
@@ -61,6 +63,7 @@ _SIGNATURES = {
     "moe_permute": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "moe_expert_ffn": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                        ctypes.c_int),
+    "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                      _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -120,6 +123,13 @@ def _need(t, dtype, shape, name):
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def set_kernel_events(kernel: str | None, start_event=None, stop_event=None):
+    """Bracket every launch of ``kernel`` (a KERNELS name) with the given
+    hipEvent_t handles (ints or c_void_p); None stops. Measurement only."""
+    kid = 0 if kernel is None else KERNELS[kernel]
+    _check(lib().moe_set_kernel_events(kid, start_event, stop_event), "moe_set_kernel_events")
 
 
 def workspace_size(cfg: MoeConfig, T: int) -> int:

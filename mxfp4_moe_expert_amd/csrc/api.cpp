@@ -13,24 +13,46 @@ namespace {
 using namespace moe;
 
 constexpr int kMaxT = 65536;
-constexpr size_t kLdsBudget = 136 * 1024;  // activation tile bytes per block
+constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, logits, ids, w, offsets, sorted, slot_pos, tile_off, blk_counts, hbuf, hs, ybuf,
+  size_t counters, logits, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
+  int tile_n, max_tiles;
 };
 
 bool cfg_ok(const moe_config* c) {
   if (!c) return false;
   const int H = c->hidden_size, E = c->n_routed_experts, k = c->top_k, I = c->moe_intermediate;
-  if (H < 128 || H % 128 || H > 32768) return false;
-  if (I < 128 || I % 128 || I > 32768) return false;
+  if (H < 128 || H % 128 || H > 16384) return false;
+  if (I < 128 || I % 128 || I > 16384) return false;
   if (k < 1 || k > kMaxTopK || E < k || E > kMaxExperts) return false;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
   if (!(c->swiglu_limit == c->swiglu_limit)) return false;
   return true;
+}
+
+// Largest power-of-two tile width <= want whose activation tile fits the LDS budget.
+int fit_tile(int want, int K) {
+  int tn = 1;
+  while (tn * 2 <= want && (size_t)(tn * 2) * (2 * (size_t)K + 16) <= kActLdsBudget) tn *= 2;
+  return tn;
+}
+
+// Columns per routed expert tile: about the expected tokens per expert, so
+// the LDS activation tile stays small at decode sizes.
+int routed_tile_n(const moe_config& c, int T) {
+  const int want = T <= 1 ? 1 : (T <= kSmallT ? 4 : 16);
+  const int K = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
+  return fit_tile(want, K);
+}
+
+int routed_max_tiles(const moe_config& c, int T, int tile_n) {
+  const long long slots = (long long)T * c.top_k;
+  const long long by_width = (slots + tile_n - 1) / tile_n + (slots < c.n_routed_experts ? slots : c.n_routed_experts);
+  return (int)(by_width < slots ? by_width : slots);
 }
 
 Layout layout(const moe_config& c, int T) {
@@ -38,20 +60,23 @@ Layout layout(const moe_config& c, int T) {
   const size_t slots = (size_t)T * k;
   const size_t nblk = (slots + kPermBlock - 1) / kPermBlock;
   Layout L;
+  L.tile_n = routed_tile_n(c, T);
+  L.max_tiles = routed_max_tiles(c, T, L.tile_n);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
     o = align256(o + bytes);
     return at;
   };
-  L.counters = take(kNumCounters * sizeof(unsigned));
+  L.counters = take(256);
   L.logits = take((size_t)T * E * 4);
   L.ids = take(slots * 4);
   L.w = take(slots * 4);
   L.offsets = take((E + 1) * 4);
   L.sorted = take(slots * 4);
   L.slot_pos = take(slots * 4);
-  L.tile_off = take((E + 1) * 4);
+  L.sorted_tok = take(slots * 4);
+  L.tile_info = take((size_t)L.max_tiles * 16);
   L.blk_counts = take(nblk * E * 4);
   L.hbuf = take(slots * I * 2);
   L.hs = take((size_t)T * I * 2);
@@ -70,115 +95,137 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 int status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// Columns per expert tile: as few as the expected tokens per expert need, so
-// the LDS activation tile stays small at decode sizes.
-int routed_tile_n(const moe_config& c, int T) {
-  int tn = T <= 1 ? 1 : (T <= kSmallT ? 4 : 16);
-  const int maxk = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
-  while (tn > 1 && (size_t)tn * (2 * (size_t)maxk + 16) > kLdsBudget) tn >>= 1;
-  return tn;
+// Measurement hook (moe_set_kernel_events): events recorded around one kernel.
+int g_prof_kernel = MOE_KERNEL_NONE;
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+// Launch `fn` bracketed by the measurement events if `kernel_id` is selected.
+template <class F>
+hipError_t timed(int kernel_id, hipStream_t st, F&& fn) {
+  const bool on = g_prof_kernel == kernel_id && g_prof_start && g_prof_stop;
+  if (on) {
+    hipError_t e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t err = fn();
+  if (err != hipSuccess) return err;
+  if (on) return hipEventRecord(g_prof_stop, st);
+  return hipSuccess;
 }
 
-int shared_tile_n(const moe_config& c, int T) {
-  int tn = T < 16 ? T : 16;
-  const int maxk = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
-  while (tn > 1 && (size_t)tn * (2 * (size_t)maxk + 16) > kLdsBudget) tn >>= 1;
-  return tn < 1 ? 1 : tn;
-}
-
-int routed_max_tiles(const moe_config& c, int T, int tile_n) {
-  const long long slots = (long long)T * c.top_k;
-  long long by_width = (slots + tile_n - 1) / tile_n + (slots < c.n_routed_experts ? slots : c.n_routed_experts);
-  return (int)(by_width < slots ? by_width : slots);
+Perm perm_of(void* ws, const Layout& L, int32_t* offsets, int32_t* sorted, int32_t* slot_pos) {
+  Perm p;
+  p.offsets = offsets;
+  p.sorted_slots = sorted;
+  p.slot_pos = slot_pos;
+  p.sorted_tok = at<int32_t>(ws, L.sorted_tok);
+  p.tile_info = at<int4>(ws, L.tile_info);
+  p.n_tiles = at<int32_t>(ws, L.counters);
+  p.tile_n = L.tile_n;
+  p.max_tiles = L.max_tiles;
+  return p;
 }
 
 SkinnyArgs skinny_common(const moe_config& c, int T) {
   SkinnyArgs a;
   memset(&a, 0, sizeof(a));
   a.T = T;
-  a.topk = c.top_k;
-  a.E = c.n_routed_experts;
   a.limit = c.swiglu_limit;
   return a;
 }
 
-// Routed experts: w13 + SwiGLU -> hbuf (sorted order), w2 x weight -> ybuf (slot order).
-int run_routed(const moe_config& c, int T, const uint16_t* x, const int32_t* offsets,
-               const int32_t* sorted, const int32_t* tile_off, int tile_n, const float* slot_w,
-               const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
-               uint16_t* hbuf, float* ybuf, hipStream_t st) {
+// Routed w13 + SwiGLU: h [sorted position][I] bf16.
+SkinnyArgs routed_w13_args(const moe_config& c, int T, const uint16_t* x, const Perm& p, const uint8_t* w13c,
+                           const uint8_t* w13s, uint16_t* hbuf) {
   const int H = c.hidden_size, I = c.moe_intermediate;
-  const int max_tiles = routed_max_tiles(c, T, tile_n);
   SkinnyArgs a = skinny_common(c, T);
   a.routed = 1;
-  a.offsets = offsets;
-  a.sorted_slots = sorted;
-  a.tile_off = tile_off;
-  a.tile_n = tile_n;
-  a.n_tiles_grid = max_tiles;
-  // w13: K = H, rows [0, I) gate and [I, 2I) up, output h [slots][I]
+  a.tile_info = p.tile_info;
+  a.n_tiles = p.n_tiles;
+  a.tile_n = p.tile_n;
+  a.n_tiles_grid = p.max_tiles;
   a.wq = w13c;
   a.wsc = w13s;
   a.q_expert_stride = (long long)2 * I * (H / 2);
   a.s_expert_stride = (long long)2 * I * (H / 32);
   a.K = H;
   a.half = I;
+  a.n_rowblocks = I / 16;
   a.act = x;
   a.act_ld = H;
-  a.act_is_x = 1;
-  a.n_rowblocks = I / 16;
+  a.act_row = p.sorted_tok;
   a.hout = hbuf;
   a.hout_ld = I;
-  int rc = status(launch_skinny_w13_mxfp4(a, max_tiles, st));
-  if (rc) return rc;
-  // w2: K = I, output rows H, y * w -> ybuf[slot]
+  return a;
+}
+
+// Routed w2 x routing weight: ybuf [slot][H] fp32.
+SkinnyArgs routed_w2_args(const moe_config& c, int T, const Perm& p, const float* slot_w, const uint8_t* w2c,
+                          const uint8_t* w2s, const uint16_t* hbuf, float* ybuf) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  SkinnyArgs a = skinny_common(c, T);
+  a.routed = 1;
+  a.tile_info = p.tile_info;
+  a.n_tiles = p.n_tiles;
+  a.tile_n = p.tile_n;
+  a.n_tiles_grid = p.max_tiles;
   a.wq = w2c;
   a.wsc = w2s;
   a.q_expert_stride = (long long)H * (I / 2);
   a.s_expert_stride = (long long)H * (I / 32);
   a.K = I;
   a.half = 0;
+  a.n_rowblocks = H / 16;
   a.act = hbuf;
   a.act_ld = I;
-  a.act_is_x = 0;
-  a.n_rowblocks = H / 16;
+  a.act_row = nullptr;
   a.yout = ybuf;
   a.yout_ld = H;
+  a.sorted_slots = p.sorted_slots;
   a.slot_w = slot_w;
-  return status(launch_skinny_w2_mxfp4(a, max_tiles, st));
+  return a;
 }
 
-// Shared expert: int8 w13 + SwiGLU -> hs [T][I], int8 w2 -> zbuf [T][H].
-int run_shared(const moe_config& c, int T, const uint16_t* x, const int8_t* q13, const float* s13,
-               const int8_t* q2, const float* s2, uint16_t* hs, float* zbuf, hipStream_t st) {
+// Shared expert w13 + SwiGLU: hs [T][I] bf16.
+SkinnyArgs shared_w13_args(const moe_config& c, int T, const uint16_t* x, const int8_t* q13, const float* s13,
+                           uint16_t* hs, int* blocks) {
   const int H = c.hidden_size, I = c.moe_intermediate;
-  const int tn = shared_tile_n(c, T);
-  const int ntiles = (T + tn - 1) / tn;
   SkinnyArgs a = skinny_common(c, T);
   a.routed = 0;
-  a.tile_n = tn;
-  a.n_tiles_grid = ntiles;
+  a.tile_n = fit_tile(T < 16 ? T : 16, H);
+  a.n_tiles_grid = (T + a.tile_n - 1) / a.tile_n;
   a.wq = reinterpret_cast<const uint8_t*>(q13);
   a.row_scale = s13;
   a.K = H;
   a.half = I;
+  a.n_rowblocks = I / 16;
   a.act = x;
   a.act_ld = H;
-  a.n_rowblocks = I / 16;
   a.hout = hs;
   a.hout_ld = I;
-  int rc = status(launch_skinny_w13_int8(a, ntiles, st));
-  if (rc) return rc;
+  *blocks = a.n_tiles_grid * a.n_rowblocks;
+  return a;
+}
+
+// Shared expert w2: zbuf [T][H] fp32.
+SkinnyArgs shared_w2_args(const moe_config& c, int T, const int8_t* q2, const float* s2, const uint16_t* hs,
+                          float* zbuf, int* blocks) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  SkinnyArgs a = skinny_common(c, T);
+  a.routed = 0;
+  a.tile_n = fit_tile(T < 16 ? T : 16, I);
+  a.n_tiles_grid = (T + a.tile_n - 1) / a.tile_n;
   a.wq = reinterpret_cast<const uint8_t*>(q2);
   a.row_scale = s2;
   a.K = I;
   a.half = 0;
+  a.n_rowblocks = H / 16;
   a.act = hs;
   a.act_ld = I;
-  a.n_rowblocks = H / 16;
   a.yout = zbuf;
   a.yout_ld = H;
-  return status(launch_skinny_w2_int8(a, ntiles, st));
+  *blocks = a.n_tiles_grid * a.n_rowblocks;
+  return a;
 }
 
 int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
@@ -186,6 +233,24 @@ int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EINVAL;
   if (bytes < layout(c, T).total) return MOE_EWORKSPACE;
   return MOE_OK;
+}
+
+RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const float* gate_w, const float* bias,
+                       const float* logit_offset, float* logits, int32_t* ids, float* w) {
+  RouterArgs a;
+  a.T = T;
+  a.H = c.hidden_size;
+  a.E = c.n_routed_experts;
+  a.k = c.top_k;
+  a.scale = c.routed_scaling_factor;
+  a.x = x;
+  a.gate_w = gate_w;
+  a.bias = bias;
+  a.logit_offset = logit_offset;
+  a.logits = logits;
+  a.ids = ids;
+  a.w = w;
+  return a;
 }
 
 }  // namespace
@@ -204,6 +269,14 @@ const char* moe_status_string(int s) {
 }
 
 const char* moe_version(void) { return "0.1.0"; }
+
+int moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
+  if (kernel_id < MOE_KERNEL_NONE || kernel_id > MOE_KERNEL_COMBINE) return MOE_EINVAL;
+  g_prof_kernel = kernel_id;
+  g_prof_start = static_cast<hipEvent_t>(start_event);
+  g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
 
 size_t moe_workspace_size(const moe_config* cfg, int32_t T) {
   if (!cfg_ok(cfg) || T < 0 || T > kMaxT) return 0;
@@ -226,24 +299,18 @@ int moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* 
   if (!aligned16(x) || !aligned16(gate_w) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_EINVAL;
   int rc = check_ws(*cfg, T, workspace, workspace_bytes);
   if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(*cfg, T);
-  RouterArgs a;
-  memset(&a, 0, sizeof(a));
-  a.T = T;
-  a.H = cfg->hidden_size;
-  a.E = cfg->n_routed_experts;
-  a.k = cfg->top_k;
-  a.scale = cfg->routed_scaling_factor;
-  a.x = x;
-  a.gate_w = gate_w;
-  a.bias = bias;
-  a.logit_offset = logit_offset;
-  a.logits = at<float>(workspace, L.logits);
-  a.ids = topk_ids;
-  a.w = topk_w;
-  a.counter = at<unsigned>(workspace, L.counters);
-  a.perm = 0;
-  return status(launch_router(a, static_cast<hipStream_t>(stream)));
+  RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), topk_ids,
+                             topk_w);
+  if (T <= kSmallT) {
+    Perm p = perm_of(workspace, L, at<int32_t>(workspace, L.offsets), at<int32_t>(workspace, L.sorted),
+                     at<int32_t>(workspace, L.slot_pos));
+    rc = status(launch_router_small(a, nullptr, 0, st));
+    if (rc) return rc;
+    return status(launch_topk_permute_small(a, p, st));
+  }
+  return status(launch_router_large(a, st));
 }
 
 int moe_hash_route(const moe_config* cfg, int32_t T, const uint16_t* x, const int32_t* token_ids,
@@ -282,18 +349,9 @@ int moe_permute(const moe_config* cfg, int32_t T, const int32_t* topk_ids, int32
   int rc = check_ws(*cfg, T, workspace, workspace_bytes);
   if (rc) return rc;
   const Layout L = layout(*cfg, T);
-  PermuteArgs a;
-  a.T = T;
-  a.E = cfg->n_routed_experts;
-  a.k = cfg->top_k;
-  a.tile_n = routed_tile_n(*cfg, T);
-  a.ids = topk_ids;
-  a.offsets = expert_offsets;
-  a.sorted_slots = sorted_slots;
-  a.slot_pos = slot_pos;
-  a.tile_off = at<int32_t>(workspace, L.tile_off);
-  a.blk_counts = at<int32_t>(workspace, L.blk_counts);
-  return status(launch_permute(a, static_cast<hipStream_t>(stream)));
+  Perm p = perm_of(workspace, L, expert_offsets, sorted_slots, slot_pos);
+  return status(launch_permute(T, cfg->n_routed_experts, cfg->top_k, topk_ids, p,
+                               at<int32_t>(workspace, L.blk_counts), static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const int32_t* expert_offsets,
@@ -307,28 +365,30 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   if (!x || !expert_offsets || !sorted_slots || !topk_w || !w13_codes || !w13_scales || !w2_codes ||
       !w2_scales || !routed_out)
     return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(w13_codes) || !aligned16(w2_codes) || !aligned16(routed_out))
+  if (!aligned16(x) || !aligned16(w13_codes) || !aligned16(w2_codes) || !aligned16(w13_scales) ||
+      !aligned16(w2_scales) || !aligned16(routed_out))
     return MOE_EINVAL;
   int rc = check_ws(*cfg, T, workspace, workspace_bytes);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(*cfg, T);
-  const int tile_n = routed_tile_n(*cfg, T);
-  int32_t* tile_off = at<int32_t>(workspace, L.tile_off);
-  rc = status(launch_tile_offsets(cfg->n_routed_experts, tile_n, expert_offsets, tile_off, st));
+  Perm p = perm_of(workspace, L, const_cast<int32_t*>(expert_offsets), const_cast<int32_t*>(sorted_slots),
+                   at<int32_t>(workspace, L.slot_pos));
+  rc = status(launch_tiles_from_offsets(T, cfg->n_routed_experts, cfg->top_k, p, st));
   if (rc) return rc;
-  rc = run_routed(*cfg, T, x, expert_offsets, sorted_slots, tile_off, tile_n, topk_w, w13_codes, w13_scales,
-                  w2_codes, w2_scales, at<uint16_t>(workspace, L.hbuf), at<float>(workspace, L.ybuf), st);
+  uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
+  float* ybuf = at<float>(workspace, L.ybuf);
+  const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+  const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
+  rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+    return launch_w13(r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, false, st);
+  }));
   if (rc) return rc;
-  CombineArgs cb;
-  cb.T = T;
-  cb.H = cfg->hidden_size;
-  cb.k = cfg->top_k;
-  cb.ybuf = at<float>(workspace, L.ybuf);
-  cb.zbuf = nullptr;
-  cb.out = routed_out;
-  cb.out_is_fp32 = 1;
-  return status(launch_combine(cb, st));
+  rc = status(timed(MOE_KERNEL_ROUTED_W2, st,
+                    [&] { return launch_w2(r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
+  if (rc) return rc;
+  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, nullptr, routed_out, 1};
+  return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 
 int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w, const float* bias,
@@ -349,92 +409,101 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   if (hash && (!tid2eid || V <= 0)) return MOE_EINVAL;
   if (!hash && !bias) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(gate_w) || !aligned16(w13_codes) || !aligned16(w2_codes) ||
-      !aligned16(sh_w13) || !aligned16(sh_w2) || !aligned16(out))
+      !aligned16(w13_scales) || !aligned16(w2_scales) || !aligned16(sh_w13) || !aligned16(sh_w2) || !aligned16(out))
     return MOE_EINVAL;
   int rc = check_ws(*cfg, T, workspace, workspace_bytes);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(*cfg, T);
-  const int tile_n = routed_tile_n(*cfg, T);
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
   float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
-  int32_t* offsets = at<int32_t>(workspace, L.offsets);
-  int32_t* sorted = at<int32_t>(workspace, L.sorted);
-  int32_t* slot_pos = at<int32_t>(workspace, L.slot_pos);
-  int32_t* tile_off = at<int32_t>(workspace, L.tile_off);
+  Perm p = perm_of(workspace, L, at<int32_t>(workspace, L.offsets), at<int32_t>(workspace, L.sorted),
+                   at<int32_t>(workspace, L.slot_pos));
+  uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
+  uint16_t* hs = at<uint16_t>(workspace, L.hs);
+  float* ybuf = at<float>(workspace, L.ybuf);
+  float* zbuf = at<float>(workspace, L.zbuf);
+  int sh13_blocks = 0, sh2_blocks = 0;
+  const SkinnyArgs s13 = shared_w13_args(*cfg, T, x, sh_w13, sh_w13_scale, hs, &sh13_blocks);
+  const SkinnyArgs s2 = shared_w2_args(*cfg, T, sh_w2, sh_w2_scale, hs, zbuf, &sh2_blocks);
+  const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+  const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
+  const int r13_blocks = p.max_tiles * r13.n_rowblocks, r2_blocks = p.max_tiles * r2.n_rowblocks;
+  const bool tiny = !hash && T * (cfg->top_k + 1) <= 16;
+  const bool decode = !hash && T <= kSmallT;
 
-  bool permuted = false;
-  if (hash) {
-    HashArgs h;
-    h.T = T;
-    h.H = cfg->hidden_size;
-    h.E = cfg->n_routed_experts;
-    h.k = cfg->top_k;
-    h.V = V;
-    h.scale = cfg->routed_scaling_factor;
-    h.x = x;
-    h.token_ids = token_ids;
-    h.tid2eid = tid2eid;
-    h.gate_w = gate_w;
-    h.ids = ids;
-    h.w = w;
-    rc = status(launch_hash_route(h, st));
-  } else {
-    RouterArgs a;
-    memset(&a, 0, sizeof(a));
-    a.T = T;
-    a.H = cfg->hidden_size;
-    a.E = cfg->n_routed_experts;
-    a.k = cfg->top_k;
-    a.scale = cfg->routed_scaling_factor;
-    a.x = x;
-    a.gate_w = gate_w;
-    a.bias = bias;
-    a.logit_offset = logit_offset;
-    a.logits = at<float>(workspace, L.logits);
-    a.ids = ids;
-    a.w = w;
-    a.counter = at<unsigned>(workspace, L.counters);
-    a.perm = T <= kSmallT ? 1 : 0;
-    a.tile_n = tile_n;
-    a.offsets = offsets;
-    a.sorted_slots = sorted;
-    a.slot_pos = slot_pos;
-    a.tile_off = tile_off;
-    permuted = a.perm != 0;
-    rc = status(launch_router(a, st));
+  if (tiny) {
+    // router logits + shared w13 | routed w13 (top-k in each block, one tile
+    // per slot) | routed w2 + shared w2 + combine
+    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, &s13, sh13_blocks, st); }));
+    if (rc) return rc;
+    SkinnyArgs t13 = r13;
+    t13.routed = 2;
+    t13.tile_n = 1;
+    t13.n_tiles_grid = T * cfg->top_k;
+    t13.act_row = nullptr;
+    t13.logits = a.logits;
+    t13.bias = bias;
+    t13.scale = cfg->routed_scaling_factor;
+    t13.E = cfg->n_routed_experts;
+    t13.topk = cfg->top_k;
+    t13.ids_out = ids;
+    t13.w_out = w;
+    const int t13_blocks = t13.n_tiles_grid * t13.n_rowblocks;
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_w13_deep(t13, t13_blocks, st); }));
+    if (rc) return rc;
+    W2CombineArgs c2{T, cfg->hidden_size, cfg->moe_intermediate, cfg->top_k, w2_codes, w2_scales, ids, w, hbuf,
+                     sh_w2, sh_w2_scale, hs, out, out_is_fp32 ? 1 : 0};
+    return status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2_combine_small(c2, st); }));
   }
-  if (rc) return rc;
-  if (!permuted) {
-    PermuteArgs p;
-    p.T = T;
-    p.E = cfg->n_routed_experts;
-    p.k = cfg->top_k;
-    p.tile_n = tile_n;
-    p.ids = ids;
-    p.offsets = offsets;
-    p.sorted_slots = sorted;
-    p.slot_pos = slot_pos;
-    p.tile_off = tile_off;
-    p.blk_counts = at<int32_t>(workspace, L.blk_counts);
-    rc = status(launch_permute(p, st));
+  if (decode) {
+    // router logits + shared w13 | top-k + permutation | routed w13 + shared w2 | routed w2 | combine
+    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, &s13, sh13_blocks, st); }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] { return launch_topk_permute_small(a, p, st); }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st,
+                      [&] { return launch_w13(r13, r13_blocks, &s2, sh2_blocks, true, st); }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2(r2, r2_blocks, nullptr, 0, st); }));
+    if (rc) return rc;
+  } else {
+    // route | permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine
+    if (hash) {
+      HashArgs h;
+      h.T = T;
+      h.H = cfg->hidden_size;
+      h.E = cfg->n_routed_experts;
+      h.k = cfg->top_k;
+      h.V = V;
+      h.scale = cfg->routed_scaling_factor;
+      h.x = x;
+      h.token_ids = token_ids;
+      h.tid2eid = tid2eid;
+      h.gate_w = gate_w;
+      h.ids = ids;
+      h.w = w;
+      rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_hash_route(h, st); }));
+    } else {
+      RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+      rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_large(a, st); }));
+    }
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] {
+      return launch_permute(T, cfg->n_routed_experts, cfg->top_k, ids, p, at<int32_t>(workspace, L.blk_counts),
+                            st);
+    }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st,
+                      [&] { return launch_w13(r13, r13_blocks, &s13, sh13_blocks, false, st); }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2(r2, r2_blocks, &s2, sh2_blocks, st); }));
     if (rc) return rc;
   }
-  rc = run_shared(*cfg, T, x, sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, at<uint16_t>(workspace, L.hs),
-                  at<float>(workspace, L.zbuf), st);
-  if (rc) return rc;
-  rc = run_routed(*cfg, T, x, offsets, sorted, tile_off, tile_n, w, w13_codes, w13_scales, w2_codes, w2_scales,
-                  at<uint16_t>(workspace, L.hbuf), at<float>(workspace, L.ybuf), st);
-  if (rc) return rc;
-  CombineArgs cb;
-  cb.T = T;
-  cb.H = cfg->hidden_size;
-  cb.k = cfg->top_k;
-  cb.ybuf = at<float>(workspace, L.ybuf);
-  cb.zbuf = at<float>(workspace, L.zbuf);
-  cb.out = out;
-  cb.out_is_fp32 = out_is_fp32 ? 1 : 0;
-  return status(launch_combine(cb, st));
+  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, zbuf, out, out_is_fp32 ? 1 : 0};
+  return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 namespace moe {
 
 constexpr int kWave = 64;
+constexpr int kTopKMax = 8;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -79,40 +80,112 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
   return silu(gc) * uc;
 }
 
-// Coherent (L1-bypassing) load of a value another block wrote in this launch.
-__device__ __forceinline__ float load_acquire_f32(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One step of a wave-wide argmax: compare with the value DPP brings in;
+// larger value wins, equal values go to the smaller index. Lanes the DPP
+// pattern leaves without a source see (-inf, INT_MAX) and keep their pair.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL,
+                                                              ROW_MASK, BANK_MASK, false));
+  const int oi = __builtin_amdgcn_update_dpp(0x7fffffff, i, CTRL, ROW_MASK, BANK_MASK, false);
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
 }
 
-// Returns true in exactly one block of a grid of `nblocks`: the last to get
-// here. Each block's global writes made before the call are visible to that
-// block after it returns true. The counter wraps back to 0 after the last
-// arrival (atomicInc with limit nblocks-1), so it is ready for the next launch.
-// Every thread of the block must call it.
-__device__ __forceinline__ bool last_block_arrives(unsigned* counter, unsigned nblocks, int* flag_lds) {
-  __threadfence();  // release this thread's writes at agent scope
-  __syncthreads();
-  if (threadIdx.x == 0) *flag_lds = (atomicInc(counter, nblocks - 1) == nblocks - 1) ? 1 : 0;
-  __syncthreads();
-  bool last = *flag_lds != 0;
-  if (last) __threadfence();  // acquire: see every other block's writes
-  return last;
+// Wave-wide argmax of (v, i) (larger v, ties to the smaller i), returned to
+// every lane: quad swaps, row rotations by 4 and 8 (each 16-lane row then
+// holds its row result), row broadcasts 15 and 31 (lane 63 holds the wave
+// result), read from lane 63.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp_step<0xB1>(v, i);         // quad_perm [1,0,3,2]
+  argmax_dpp_step<0x4E>(v, i);         // quad_perm [2,3,0,1]
+  argmax_dpp_step<0x124>(v, i);        // row_ror:4
+  argmax_dpp_step<0x128>(v, i);        // row_ror:8
+  argmax_dpp_step<0x142, 0xA>(v, i);   // row_bcast:15 -> rows 1, 3
+  argmax_dpp_step<0x143, 0xC>(v, i);   // row_bcast:31 -> rows 2, 3
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
-// Exclusive scan of n <= 256 ints held one per thread (threads >= n hold 0).
-// Returns the exclusive prefix for this thread; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan_256(int v, int* tmp, int* total) {
-  const int tid = threadIdx.x;
+// One wave selects the top-k experts of one token from its E <= 256 logits
+// (fp32): s = sqrt(softplus(logit)), chosen by s + bias, descending, ties to
+// the lower expert id; weights scale * s / sum(s) over the chosen, summed in
+// slot order. Lane l owns experts l, l+64, l+128, l+192; each of the k rounds
+// is one DPP wave argmax. Lane 0 writes ids/weights for slots j = 0..k-1 and,
+// if ids_lds is given, the ids there too.
+__device__ __forceinline__ void wave_topk(const float* logits_row, const float* bias, int E, int k, float scale,
+                          int32_t* ids_out, float* w_out, int32_t* ids_lds) {
+  const int lane = threadIdx.x & 63;
+  float s[4], b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) {
+      s[q] = sqrtf(softplus(logits_row[e]));
+      b[q] = s[q] + bias[e];
+    } else {
+      s[q] = 0.0f;
+      b[q] = -INFINITY;
+    }
+  }
+  unsigned taken = 0;
+  float sel_s[kTopKMax];
+  int sel_id[kTopKMax];
+#pragma unroll
+  for (int j = 0; j < kTopKMax; ++j) {
+    sel_s[j] = 0.0f;
+    sel_id[j] = 0;
+    if (j >= k) continue;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      const bool ok = e < E && !(taken & (1u << q));
+      if (ok && (b[q] > bv || (b[q] == bv && e < bi))) {
+        bv = b[q];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    const int owner = bi & 63, q_of = bi >> 6;
+    const float mys = (q_of == 0) ? s[0] : (q_of == 1) ? s[1] : (q_of == 2) ? s[2] : s[3];
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mys), owner));
+    if (lane == owner) taken |= 1u << q_of;
+    sel_s[j] = ws;
+    sel_id[j] = bi;
+  }
+  if (lane == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j)
+      if (j < k) sum += sel_s[j];
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) {
+      if (j >= k) continue;
+      ids_out[j] = sel_id[j];
+      w_out[j] = scale * sel_s[j] / sum;
+      if (ids_lds) ids_lds[j] = sel_id[j];
+    }
+  }
+}
+
+// Exclusive scan over the block of one int per thread (tmp: blockDim.x ints
+// of LDS). Returns this thread's exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int tid = threadIdx.x, n = blockDim.x;
   tmp[tid] = v;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int add = tid >= o ? tmp[tid - o] : 0;
+  for (int o = 1; o < n; o <<= 1) {
+    const int add = tid >= o ? tmp[tid - o] : 0;
     __syncthreads();
     tmp[tid] += add;
     __syncthreads();
   }
-  int incl = tmp[tid];
-  *total = tmp[255];
+  const int incl = tmp[tid];
+  *total = tmp[n - 1];
   __syncthreads();
   return incl - v;
 }

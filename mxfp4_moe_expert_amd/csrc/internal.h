@@ -7,11 +7,26 @@
 
 namespace moe {
 
-constexpr int kSmallT = 64;         // T at or below this uses the one-launch router
+constexpr int kSmallT = 64;        // T at or below: decode schedule (one-block top-k + permutation)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 256;
-constexpr int kPermBlock = 1024;    // slots per block in the multi-block permutation
-constexpr int kNumCounters = 64;
+constexpr int kPermBlock = 1024;   // slots per block of the multi-block permutation
+constexpr int kThreads = 512;      // threads of every expert / router block (8 waves)
+constexpr int kWaves = kThreads / 64;
+
+// Permutation of the T*k slots by expert, plus the table of expert tiles
+// (groups of at most tile_n consecutive sorted positions of one expert) that
+// the expert kernels take one block column each.
+struct Perm {
+  int32_t* offsets;       // [E+1] first sorted position of each expert
+  int32_t* sorted_slots;  // [T*k] slot (t*k+j) at each sorted position
+  int32_t* slot_pos;      // [T*k] sorted position of each slot
+  int32_t* sorted_tok;    // [T*k] token of each sorted position
+  int4* tile_info;        // [max_tiles] {expert, first position, columns, 0}
+  int32_t* n_tiles;       // [1] tiles in use
+  int tile_n;
+  int max_tiles;
+};
 
 struct RouterArgs {
   int T, H, E, k;
@@ -20,17 +35,9 @@ struct RouterArgs {
   const float* gate_w;
   const float* bias;
   const float* logit_offset;
-  float* logits;       // [T][E] workspace
-  int32_t* ids;        // [T][k]
-  float* w;            // [T][k]
-  unsigned* counter;   // last-block counter (zero between calls)
-  // small-T path only: build the permutation in the same launch
-  int perm;
-  int tile_n;
-  int32_t* offsets;
-  int32_t* sorted_slots;
-  int32_t* slot_pos;
-  int32_t* tile_off;
+  float* logits;  // [T][E]
+  int32_t* ids;   // [T][k]
+  float* w;       // [T][k]
 };
 
 struct HashArgs {
@@ -44,18 +51,9 @@ struct HashArgs {
   float* w;
 };
 
-struct PermuteArgs {
-  int T, E, k, tile_n;
-  const int32_t* ids;
-  int32_t* offsets;
-  int32_t* sorted_slots;
-  int32_t* slot_pos;
-  int32_t* tile_off;
-  int32_t* blk_counts;  // [nblk][E] workspace
-};
-
-// One pass of the small-column ("skinny") expert GEMM: up to 16 activation
-// columns per tile against 16 weight rows per block, MFMA 16x16x32 bf16.
+// One expert GEMM pass on the "skinny" kernel: 16 weight rows per block (for
+// w13, 16 gate rows and the 16 matching up rows) against one tile of at most
+// 16 activation columns; K split over the 8 waves of the block.
 struct SkinnyArgs {
   const uint8_t* wq;          // MXFP4 codes [E][N][K/2] or int8 [N][K]
   const uint8_t* wsc;         // MXFP4 scales [E][N][K/32] (null for int8)
@@ -64,43 +62,76 @@ struct SkinnyArgs {
   long long s_expert_stride;  // bytes between experts of wsc
   int K;                      // input features
   int half;                   // w13: I (up rows start there); w2: 0
+  int n_rowblocks;            // output rows / 16
+  int routed;                 // 1: tiles from perm.tile_info; 0: tiles of consecutive tokens;
+                              // 2: one tile per slot, expert from the top-k computed in the block
+  const int4* tile_info;
+  const int32_t* n_tiles;
+  int tile_n;                 // columns per tile (shared: tokens per tile)
+  int n_tiles_grid;           // tiles per row block in the grid
+  int T;
   const uint16_t* act;        // bf16 activation rows
   int act_ld;
-  int act_is_x;               // routed w13: activation row = token of the slot
-  int T, topk, E;
-  int routed;                 // tiles from tile_off (routed) or 16-token tiles (shared)
-  const int32_t* offsets;
-  const int32_t* sorted_slots;
-  const int32_t* tile_off;
-  int tile_n;                 // columns per tile, 1..16
-  int n_tiles_grid;           // tiles in the grid (block = tile + n_tiles_grid * rowblock)
-  int n_rowblocks;            // output rows / 16
-  uint16_t* hout;             // w13: bf16 h rows
+  const int32_t* act_row;     // row of act for each sorted position (null: the position itself)
+  uint16_t* hout;             // w13: bf16 h rows, by sorted position (routed) or token (shared)
   int hout_ld;
-  float* yout;                // w2: fp32 rows
+  float* yout;                // w2: fp32 rows, by slot (routed) or token (shared)
   int yout_ld;
+  const int32_t* sorted_slots;
   const float* slot_w;        // w2 routed: combine weight of each slot
   float limit;
+  // routed == 2 only: router logits and the routing outputs this pass writes
+  const float* logits;        // [T][E]
+  const float* bias;          // [E]
+  float scale;
+  int E, topk;
+  int32_t* ids_out;           // [T][k]
+  float* w_out;               // [T][k]
+};
+
+// Routed w2 + shared w2 + combine for T*(k+1) <= 16 ("output-stationary"):
+// each block owns 16 output rows of every token; slot j is MFMA column j and
+// token t's shared-expert input is column T*k + t.
+struct W2CombineArgs {
+  int T, H, I, k;
+  const uint8_t* w2c;
+  const uint8_t* w2s;
+  const int32_t* ids;    // [T*k] experts of the slots
+  const float* w;        // [T*k] routing weights
+  const uint16_t* hbuf;  // [T*k][I] bf16 h of each slot
+  const int8_t* sh_w2;   // [H][I] shared expert w2 (int8)
+  const float* sh_w2_scale;  // [H]
+  const uint16_t* hs;    // [T][I] bf16 h of the shared expert
+  void* out;             // [T][H]
+  int out_is_fp32;
 };
 
 struct CombineArgs {
   int T, H, k;
-  const float* ybuf;    // [T*k][H] weighted expert outputs in slot order
-  const float* zbuf;    // [T][H] shared expert or null
-  void* out;            // [T][H]
+  const float* ybuf;  // [T*k][H] weighted expert outputs in slot order
+  const float* zbuf;  // [T][H] shared expert or null
+  void* out;          // [T][H]
   int out_is_fp32;
 };
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t st);
-hipError_t launch_hash_route(const HashArgs& a, hipStream_t st);
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
-hipError_t launch_tile_offsets(int E, int tile_n, const int32_t* offsets, int32_t* tile_off,
+// Routers
+hipError_t launch_router_small(const RouterArgs& r, const SkinnyArgs* shared_w13, int shared_blocks,
                                hipStream_t st);
-hipError_t launch_skinny_w13_mxfp4(const SkinnyArgs& a, int max_tiles, hipStream_t st);
-hipError_t launch_skinny_w2_mxfp4(const SkinnyArgs& a, int max_tiles, hipStream_t st);
-hipError_t launch_skinny_w13_int8(const SkinnyArgs& a, int max_tiles, hipStream_t st);
-hipError_t launch_skinny_w2_int8(const SkinnyArgs& a, int max_tiles, hipStream_t st);
+hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStream_t st);
+hipError_t launch_router_large(const RouterArgs& r, hipStream_t st);
+hipError_t launch_hash_route(const HashArgs& a, hipStream_t st);
+// Permutation and tiles
+hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p, int32_t* blk_counts,
+                          hipStream_t st);
+hipError_t launch_tiles_from_offsets(int T, int E, int k, const Perm& p, hipStream_t st);
+// Expert passes; `b` (optional) runs in the same launch as `a`
+hipError_t launch_w13(const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks, bool b_is_shared_w2,
+                      hipStream_t st);
+hipError_t launch_w2(const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks, hipStream_t st);
+hipError_t launch_shared_w13(const SkinnyArgs& a, int blocks, hipStream_t st);
+hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace moe

@@ -1,15 +1,16 @@
 // Token permutation by expert on gfx950: a stable counting sort of the T*k
-// (token, slot) pairs by expert id, so each expert's activation rows can be
-// gathered into one contiguous group (the dispatch step of the MoE block:
-// page "DeepSeek-V4-Flash-0731", section "Checked in its code", row "Shared
+// (token, slot) pairs by expert id, so each expert's activation rows form one
+// contiguous group (the dispatch step of the MoE block: page
+// "DeepSeek-V4-Flash-0731", section "Checked in its code", row "Shared
 // expert", where the routed experts are called with the flat tokens, the
-// chosen indices and their weights).
+// chosen indices and their weights). It also writes the expert tile table
+// the expert kernels read with one load per block.
 //
-// Three launches for any T (the small-T router builds the same outputs in its
-// own last block):
+// Three launches for any T (decode sizes use the one-block version in
+// route.hip):
 //   k_perm_count   per block of kPermBlock slots, a histogram over experts
-//   k_perm_scan    one block: per-expert exclusive prefix over blocks, expert
-//                  offsets, and the tile prefix used by the expert GEMMs
+//   k_perm_scan    one block: per-expert prefix over blocks, expert offsets,
+//                  the tile table
 //   k_perm_scatter per block, the stable rank of each slot among the block's
 //                  earlier slots of the same expert -> its sorted position
 #include "device.h"
@@ -17,7 +18,28 @@
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void k_perm_count(PermuteArgs a) {
+struct PermArgs {
+  int T, E, k;
+  const int32_t* ids;
+  Perm p;
+  int32_t* blk_counts;  // [nblk][E]
+};
+
+__device__ void write_tiles(int c, int off, int E, const Perm& p, int* scan_tmp) {
+  const int tid = threadIdx.x;
+  const int nt = tid < E ? (c + p.tile_n - 1) / p.tile_n : 0;
+  int total;
+  const int toff = block_exclusive_scan(nt, scan_tmp, &total);
+  if (tid < E) {
+    for (int i = 0; i < nt; ++i) {
+      const int first = i * p.tile_n;
+      p.tile_info[toff + i] = make_int4(tid, off + first, min(p.tile_n, c - first), 0);
+    }
+  }
+  if (tid == 0) *p.n_tiles = total;
+}
+
+__global__ __launch_bounds__(256) void k_perm_count(PermArgs a) {
   __shared__ int hist[kMaxExperts];
   const int tid = threadIdx.x, b = blockIdx.x;
   const int n = a.T * a.k;
@@ -29,34 +51,28 @@ __global__ __launch_bounds__(256) void k_perm_count(PermuteArgs a) {
   if (tid < a.E) a.blk_counts[(size_t)b * a.E + tid] = hist[tid];
 }
 
-__global__ __launch_bounds__(256) void k_perm_scan(PermuteArgs a, int nblk) {
+__global__ __launch_bounds__(256) void k_perm_scan(PermArgs a, int nblk) {
   __shared__ int tmp[256];
   const int tid = threadIdx.x;
   int running = 0;
   if (tid < a.E) {
     for (int b = 0; b < nblk; ++b) {
-      int c = a.blk_counts[(size_t)b * a.E + tid];
+      const int c = a.blk_counts[(size_t)b * a.E + tid];
       a.blk_counts[(size_t)b * a.E + tid] = running;
       running += c;
     }
   }
   int total;
-  int off = block_exclusive_scan_256(tid < a.E ? running : 0, tmp, &total);
-  int nt = tid < a.E ? (running + a.tile_n - 1) / a.tile_n : 0;
-  int ttotal;
-  int toff = block_exclusive_scan_256(nt, tmp, &ttotal);
+  const int off = block_exclusive_scan(tid < a.E ? running : 0, tmp, &total);
   if (tid < a.E) {
-    a.offsets[tid] = off;
-    a.tile_off[tid] = toff;
+    a.p.offsets[tid] = off;
     for (int b = 0; b < nblk; ++b) a.blk_counts[(size_t)b * a.E + tid] += off;
   }
-  if (tid == 0) {
-    a.offsets[a.E] = total;
-    a.tile_off[a.E] = ttotal;
-  }
+  if (tid == 0) a.p.offsets[a.E] = total;
+  write_tiles(running, off, a.E, a.p, tmp);
 }
 
-__global__ __launch_bounds__(256) void k_perm_scatter(PermuteArgs a) {
+__global__ __launch_bounds__(256) void k_perm_scatter(PermArgs a) {
   __shared__ int chunk[256];
   __shared__ int seen[kMaxExperts];
   const int tid = threadIdx.x, b = blockIdx.x;
@@ -72,8 +88,9 @@ __global__ __launch_bounds__(256) void k_perm_scatter(PermuteArgs a) {
       int rank = 0;
       for (int j = 0; j < tid; ++j) rank += (chunk[j] == e);
       const int pos = a.blk_counts[(size_t)b * a.E + e] + seen[e] + rank;
-      a.sorted_slots[pos] = i;
-      a.slot_pos[i] = pos;
+      a.p.sorted_slots[pos] = i;
+      a.p.slot_pos[i] = pos;
+      a.p.sorted_tok[pos] = i / a.k;
     }
     __syncthreads();
     if (e >= 0) atomicAdd(&seen[e], 1);
@@ -81,37 +98,44 @@ __global__ __launch_bounds__(256) void k_perm_scatter(PermuteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_tile_offsets(int E, int tile_n, const int32_t* offsets,
-                                                       int32_t* tile_off) {
+// Tile table and token-of-position from expert offsets and sorted slots given
+// by the caller (moe_expert_ffn): block 0 writes the tiles, every block a
+// slice of sorted_tok.
+__global__ __launch_bounds__(256) void k_tiles_from_offsets(int T, int E, int k, const int32_t* sorted_slots,
+                                                            Perm p) {
   __shared__ int tmp[256];
   const int tid = threadIdx.x;
-  int c = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
-  int total;
-  int toff = block_exclusive_scan_256((c + tile_n - 1) / tile_n, tmp, &total);
-  if (tid < E) tile_off[tid] = toff;
-  if (tid == 0) tile_off[E] = total;
+  if (blockIdx.x == 0) {
+    const int c = tid < E ? p.offsets[tid + 1] - p.offsets[tid] : 0;
+    const int off = tid < E ? p.offsets[tid] : 0;
+    write_tiles(c, off, E, p, tmp);
+  }
+  const int n = T * k;
+  for (int i = blockIdx.x * 256 + tid; i < n; i += gridDim.x * 256) p.sorted_tok[i] = sorted_slots[i] / k;
 }
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
-  const int n = a.T * a.k;
-  if (n <= 0) {  // every expert empty: zero offsets and tiles
-    k_perm_scan<<<1, 256, 0, st>>>(a, 0);
-    return hipGetLastError();
-  }
+hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p, int32_t* blk_counts,
+                          hipStream_t st) {
+  PermArgs a{T, E, k, ids, p, blk_counts};
+  const int n = T * k;
   const int nblk = (n + kPermBlock - 1) / kPermBlock;
-  k_perm_count<<<nblk, 256, 0, st>>>(a);
+  if (nblk > 0) {
+    k_perm_count<<<nblk, 256, 0, st>>>(a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  k_perm_scan<<<1, 256, 0, st>>>(a, nblk);  // nblk == 0: all experts empty
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  k_perm_scan<<<1, 256, 0, st>>>(a, nblk);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || nblk == 0) return err;
   k_perm_scatter<<<nblk, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_offsets(int E, int tile_n, const int32_t* offsets, int32_t* tile_off,
-                               hipStream_t st) {
-  k_tile_offsets<<<1, 256, 0, st>>>(E, tile_n, offsets, tile_off);
+hipError_t launch_tiles_from_offsets(int T, int E, int k, const Perm& p, hipStream_t st) {
+  const int n = T * k;
+  int blocks = (n + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  k_tiles_from_offsets<<<blocks, 256, 0, st>>>(T, E, k, p.sorted_slots, p);
   return hipGetLastError();
 }
 

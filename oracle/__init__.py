@@ -56,6 +56,8 @@ def use_library(path: str | None):
 def _open(path: str):
     L = ctypes.CDLL(path)
     i32, i64, dbl, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    L.or_num_threads.argtypes = []
+    L.or_num_threads.restype = i32
     L.or_e2m1.argtypes = [i32]
     L.or_e2m1.restype = dbl
     L.or_e8m0.argtypes = [i32]

@@ -47,6 +47,7 @@
  * the 6 table experts by their renormalised sqrt-softplus scores, no bias.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -54,13 +55,16 @@
 #define OR_OK 0
 #define OR_EINVAL (-1)
 
+/* Threads the oracle's parallel loops use (OpenMP). */
+int or_num_threads(void) { return omp_get_max_threads(); }
+
 /* ---- exact decoders ------------------------------------------------------ */
 
 /* E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
  * Exponent 0 is subnormal: 0.5 * m. Otherwise 2^(e-1) * (1 + m/2). */
 double or_e2m1(int code) {
   int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
-  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  double mag = (e == 0) ? 0.5 * m : (1.0 + 0.5 * m) * (double)(1 << (e - 1));
   return s ? -mag : mag;
 }
 

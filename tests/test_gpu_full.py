@@ -1,0 +1,101 @@
+"""GPU parity at the layer's real shapes (hidden 4096, 256 experts, top-6,
+intermediate 2048, MXFP4 routed experts, int8 shared expert), through the C
+ABI, in the same configuration the benchmark times:
+
+  decode T=1   several fresh token batches, every row
+  decode T=64  router bias N(0, 0.05) (mild expert skew), every row
+  prefill T=8192, per-expert logit offsets N(0, 0.5): routing of every token,
+               outputs of sampled rows (tokens are independent)
+  hash layer T=4096, Zipf(1.1) token ids: routing exact, sampled rows
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_outputs_close, compare_routing, reference_rows
+
+pytestmark = pytest.mark.gpu
+mx = pytest.importorskip("mxfp4_moe_expert_amd")
+DEV = "cuda"
+
+
+def _variant(L, D, wl):
+    """Same expert weights, the workload's own router bias / offset / table."""
+    bias = synth.normal_f32(wl.seed, synth.S_BIAS, 0, wl.E, wl.bias_sigma)
+    off = synth.normal_f32(wl.seed, synth.S_OFFSET, 0, wl.E, wl.offset_sigma) if wl.offset_sigma > 0 else None
+    t2e = synth.tid2eid(wl.seed, synth.S_TID2EID, 0, wl.V, wl.E, wl.k) if wl.hash_layer else None
+    Lv = dataclasses.replace(L, wl=wl, bias=bias, logit_offset=off, tid2eid=t2e)
+    Dv = dataclasses.replace(D, bias=torch.from_numpy(bias).to(DEV),
+                             logit_offset=None if off is None else torch.from_numpy(off).to(DEV),
+                             tid2eid=None if t2e is None else torch.from_numpy(t2e).to(DEV))
+    return Lv, Dv
+
+
+def _run(wl, Lv, Dv, rep, rows=None, check_all_routing=True):
+    cfg = mx.config_of(wl)
+    xh = synth.make_tokens(wl, rep=rep)
+    x = mx.bf16_from_numpy(xh, DEV)
+    tids_h = synth.make_token_ids(wl, rep=rep) if wl.hash_layer else None
+    tids = None if tids_h is None else torch.from_numpy(tids_h).to(DEV)
+    print(f"[{wl.name} rep={rep}] gpu forward", flush=True)
+    out, (ids, w) = mx.forward(cfg, x, Dv, token_ids=tids, out_fp32=True, return_routing=True)
+    out_bf = mx.forward(cfg, x, Dv, token_ids=tids)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    routing = None
+    print(f"[{wl.name} rep={rep}] oracle routing", flush=True)
+    if wl.hash_layer:
+        oi, ow = oracle.hash_route(xh, tids_h, Lv.tid2eid, Lv.gate_w)
+        assert np.array_equal(ids, oi)
+        assert np.abs(w - ow).max() <= 1e-5
+    else:
+        oi, ow, og, on = oracle.route(xh, Lv.gate_w, Lv.bias, Lv.logit_offset, k=wl.k)
+        routing = compare_routing(ids, w, oi, ow, og, on)
+        print(f"[{wl.name}] near-ties {routing['near_ties']} swapped {routing['swapped']}", flush=True)
+    rows = np.arange(wl.T, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+    print(f"[{wl.name} rep={rep}] oracle outputs for {len(rows)} rows", flush=True)
+    _, ref = reference_rows(Lv, xh, rows, token_ids=tids_h, routing=routing)
+    got = out.cpu().numpy()[rows]
+    e = assert_outputs_close(got, ref, f"{wl.name} rep={rep}")
+    print(f"[{wl.name} rep={rep}] rel L2 {e['rel_l2']:.2e} max abs {e['max_abs']:.2e} rms {e['rms']:.2e}",
+          flush=True)
+    assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
+    return ids
+
+
+@pytest.mark.parametrize("rep", [0, 1, 2])
+def test_decode_t1_full(full_layer, rep):
+    L, D = full_layer
+    wl = synth.WORKLOADS["decode_t1"]
+    Lv, Dv = _variant(L, D, wl)
+    _run(wl, Lv, Dv, rep)
+
+
+def test_decode_t64_full(full_layer):
+    L, D = full_layer
+    wl = synth.WORKLOADS["decode_t64"]
+    Lv, Dv = _variant(L, D, wl)
+    ids = _run(wl, Lv, Dv, 0)
+    assert len(set(ids.ravel().tolist())) > 100
+
+
+def test_prefill_t8192_full_sampled(full_layer):
+    L, D = full_layer
+    wl = synth.WORKLOADS["prefill_t8192"]
+    Lv, Dv = _variant(L, D, wl)
+    rows = np.unique(np.concatenate([[0, 1, 4095, 8190, 8191], np.random.default_rng(0).integers(0, 8192, 11)]))
+    ids = _run(wl, Lv, Dv, 0, rows=rows)
+    counts = np.bincount(ids.ravel(), minlength=256)
+    assert counts.max() > 2 * counts.mean()  # the offsets skew the loads
+
+
+def test_hash_t4096_full_sampled(full_layer):
+    L, D = full_layer
+    wl = synth.WORKLOADS["hash_t4096"]
+    Lv, Dv = _variant(L, D, wl)
+    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(1).integers(0, 4096, 10)]))
+    _run(wl, Lv, Dv, 0, rows=rows)

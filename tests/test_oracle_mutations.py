@@ -24,7 +24,7 @@ MUTATIONS = [
      "int cg = (k & 1) ? (bg & 15) : (bg >> 4);"),
     ("nibble_order_w2", "int c = (i & 1) ? (b >> 4) : (b & 15);",
      "int c = (i & 1) ? (b & 15) : (b >> 4);"),
-    ("e2m1_exponent_bias", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    ("e2m1_exponent_bias", "(1.0 + 0.5 * m) * (double)(1 << (e - 1))", "(1.0 + 0.5 * m) * (double)(1 << e)"),
     ("e2m1_subnormal", "(e == 0) ? 0.5 * m", "(e == 0) ? 1.0 * m"),
     ("e8m0_bias", "ldexp(1.0, b - 127)", "ldexp(1.0, b - 128)"),
     ("scale_group_index", "double sg = or_e8m0(s13[(int64_t)i * (H / 32) + k0 / 32]);",
