@@ -43,8 +43,12 @@ int fit_tile(int want, int K) {
 
 // Columns per routed expert tile: about the expected tokens per expert, so
 // the LDS activation tile stays small at decode sizes.
+// Batches above kSmallT run the grouped GEMMs (256-row output tiles along H).
+bool use_gemm(const moe_config& c, int T) { return T > kSmallT && c.hidden_size % 256 == 0; }
+
 int routed_tile_n(const moe_config& c, int T) {
-  const int want = T <= 1 ? 1 : (T <= kSmallT ? 4 : 16);
+  if (use_gemm(c, T)) return kGemmTokens;
+  const int want = T <= 1 ? 1 : 4;
   const int K = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
   return fit_tile(want, K);
 }
@@ -228,6 +232,106 @@ SkinnyArgs shared_w2_args(const moe_config& c, int T, const int8_t* q2, const fl
   return a;
 }
 
+GemmArgs gemm_common(const moe_config& c, int T) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.T = T;
+  g.topk = c.top_k;
+  g.limit = c.swiglu_limit;
+  return g;
+}
+
+// Routed w13 (+ SwiGLU) as a grouped GEMM: h [sorted position][I].
+GemmArgs gemm_routed_w13(const moe_config& c, int T, const uint16_t* x, const Perm& p, const uint8_t* w13c,
+                         const uint8_t* w13s, uint16_t* hbuf) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  GemmArgs g = gemm_common(c, T);
+  g.fmt = 0;
+  g.mode = kGemmW13;
+  g.wq = w13c;
+  g.wsc = w13s;
+  g.q_expert_stride = (long long)2 * I * (H / 2);
+  g.s_expert_stride = (long long)2 * I * (H / 32);
+  g.K = H;
+  g.half = I;
+  g.routed = 1;
+  g.tile_info = p.tile_info;
+  g.n_tiles = p.n_tiles;
+  g.n_ntiles = I / 128;
+  g.act = x;
+  g.act_ld = H;
+  g.act_row = p.sorted_tok;
+  g.hout = hbuf;
+  g.hout_ld = I;
+  return g;
+}
+
+// Routed w2 x routing weight: ybuf [slot][H].
+GemmArgs gemm_routed_w2(const moe_config& c, int T, const Perm& p, const float* slot_w, const uint8_t* w2c,
+                        const uint8_t* w2s, const uint16_t* hbuf, float* ybuf) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  GemmArgs g = gemm_common(c, T);
+  g.fmt = 0;
+  g.mode = kGemmW2;
+  g.wq = w2c;
+  g.wsc = w2s;
+  g.q_expert_stride = (long long)H * (I / 2);
+  g.s_expert_stride = (long long)H * (I / 32);
+  g.K = I;
+  g.routed = 1;
+  g.tile_info = p.tile_info;
+  g.n_tiles = p.n_tiles;
+  g.n_ntiles = H / 256;
+  g.act = hbuf;
+  g.act_ld = I;
+  g.yout = ybuf;
+  g.yout_ld = H;
+  g.sorted_slots = p.sorted_slots;
+  g.slot_w = slot_w;
+  return g;
+}
+
+// Shared w13 (+ SwiGLU): hs [T][I].
+GemmArgs gemm_shared_w13(const moe_config& c, int T, const uint16_t* x, const int8_t* q13, const float* s13,
+                         uint16_t* hs) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  GemmArgs g = gemm_common(c, T);
+  g.fmt = 1;
+  g.mode = kGemmW13;
+  g.wq = reinterpret_cast<const uint8_t*>(q13);
+  g.row_scale = s13;
+  g.K = H;
+  g.half = I;
+  g.routed = 0;
+  g.n_ntiles = I / 128;
+  g.act = x;
+  g.act_ld = H;
+  g.hout = hs;
+  g.hout_ld = I;
+  return g;
+}
+
+// Shared w2 + the final combine: out[t] = sum_j ybuf[t*k+j] + s2 * (Q2 hs_t).
+GemmArgs gemm_shared_w2_combine(const moe_config& c, int T, const int8_t* q2, const float* s2, const uint16_t* hs,
+                                const float* ybuf, void* out, int out_is_fp32) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  GemmArgs g = gemm_common(c, T);
+  g.fmt = 1;
+  g.mode = kGemmW2Combine;
+  g.wq = reinterpret_cast<const uint8_t*>(q2);
+  g.row_scale = s2;
+  g.K = I;
+  g.routed = 0;
+  g.n_ntiles = H / 256;
+  g.act = hs;
+  g.act_ld = I;
+  g.ybuf = ybuf;
+  g.out = out;
+  g.out_ld = H;
+  g.out_is_fp32 = out_is_fp32;
+  return g;
+}
+
 int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
   if (!ws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EINVAL;
@@ -378,15 +482,24 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   if (rc) return rc;
   uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
   float* ybuf = at<float>(workspace, L.ybuf);
-  const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
-  const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
-  rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
-    return launch_w13(r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, false, st);
-  }));
-  if (rc) return rc;
-  rc = status(timed(MOE_KERNEL_ROUTED_W2, st,
-                    [&] { return launch_w2(r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
-  if (rc) return rc;
+  if (use_gemm(*cfg, T)) {
+    const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+    const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm(g2, p.max_tiles, st); }));
+    if (rc) return rc;
+  } else {
+    const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+    const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+      return launch_w13(r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, false, st);
+    }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st,
+                      [&] { return launch_w2(r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
+    if (rc) return rc;
+  }
   CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, nullptr, routed_out, 1};
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
@@ -496,6 +609,21 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                             st);
     }));
     if (rc) return rc;
+    if (use_gemm(*cfg, T)) {
+      // grouped GEMMs; the shared expert's w2 finishes with the combine
+      const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+      const GemmArgs h13 = gemm_shared_w13(*cfg, T, x, sh_w13, sh_w13_scale, hs);
+      const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
+      const GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybuf, out, out_is_fp32 ? 1 : 0);
+      const int sh_tiles = (T + kGemmTokens - 1) / kGemmTokens;
+      rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
+      if (rc) return rc;
+      rc = status(timed(MOE_KERNEL_SHARED_W13, st, [&] { return launch_gemm(h13, sh_tiles, st); }));
+      if (rc) return rc;
+      rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm(g2, p.max_tiles, st); }));
+      if (rc) return rc;
+      return status(timed(MOE_KERNEL_SHARED_W2, st, [&] { return launch_gemm(h2, sh_tiles, st); }));
+    }
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st,
                       [&] { return launch_w13(r13, r13_blocks, &s13, sh13_blocks, false, st); }));
     if (rc) return rc;

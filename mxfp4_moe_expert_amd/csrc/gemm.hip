@@ -1,0 +1,290 @@
+// Grouped expert GEMM for large token counts on gfx950 (prefill): MXFP4
+// routed experts ("w4a16") and the int8 per-channel shared expert ("w8a16"),
+// page "deepseek-v4-mxfp4-int8 config.json", quantization_config; clamped
+// SwiGLU epilogue on w13 (page "DeepSeek-V4-Flash-0731", section "Checked in
+// its code", row "SwiGLU feed-forward"); the shared expert's w2 epilogue adds
+// the k weighted routed outputs of the token in slot order (row "Shared
+// expert": routed + shared).
+//
+// Block: 8 waves, output tile of 256 weight rows x 128 token positions, K in
+// stages of 128. Wave (wm, wn) = (wave & 1, wave >> 1) owns 64 weight rows (4
+// blocks of 16) x 64 tokens (4 blocks of 16): 16 MFMA 16x16x32 accumulators.
+// For w13 the wave's 4 row blocks are 2 gate blocks and the 2 matching up
+// blocks, so the SwiGLU is computed in registers.
+//   - K runs in stages of 128 (MXFP4) or 64 (int8): each lane reads, per
+//     stage and row block, 16 bytes of its row (the quarter g of the stage's
+//     K-values) straight into registers, two stages ahead. For MXFP4 these 32
+//     values are exactly one group, so one E8M0 byte per row block and stage;
+//     MXFP4 is converted to bf16 with the exact scaled FP4 convert.
+//   - tokens: the 128 gathered activation rows of a stage go global ->
+//     registers -> LDS (rows padded by 16 bytes, conflict-free 16-byte
+//     reads), double-buffered, one stage ahead.
+//   - MFMA k-step kk of a stage takes the lane's K-values 8kk .. +8 of its
+//     quarter on both operands (a fixed permutation of K, so the dot products
+//     are unchanged).
+//   - blocks are ordered so that each XCD (block % 8) walks a contiguous run of
+//     tiles with the N tiles of one token tile adjacent (L2 reuse of tokens).
+#include <type_traits>
+
+#include "device.h"
+#include "internal.h"
+#include "skinny.h"
+
+namespace moe {
+
+constexpr int kBM = 128;  // token positions per tile
+constexpr int kBN = 256;  // weight rows per tile (w13: 128 gate + 128 up)
+
+// Per format: K per stage (each lane's 16 weight bytes per row block are 32
+// E2M1 values or 16 int8 values, a quarter of the stage), MFMA k-steps per
+// stage, padded LDS bytes per token row and 16-byte activation pieces per
+// thread.
+template <int FMT>
+struct GemmCfg {
+  static constexpr int kBK = FMT == kFmtMx ? 128 : 64;
+  static constexpr int kKK = kBK / 32;
+  static constexpr int kArow = kBK * 2 + 16;
+  static constexpr int kAVec = kBK / 32;
+};
+
+// A lane's 16 weight bytes for one row block and stage, converted to bf16
+// eight K-values at a time.
+template <int FMT>
+__device__ __forceinline__ bf16x8_t gemm_conv(const u32x4_t& q, int kk, uint32_t sc) {
+  if constexpr (FMT == kFmtMx) {
+    const uint32_t d = kk == 0 ? q.x : kk == 1 ? q.y : kk == 2 ? q.z : q.w;
+    return fp4x8_to_bf16x8(d, e8m0_scale_operand(sc));
+  } else {
+    return i8x8_to_bf16x8(kk == 0 ? q.x : q.z, kk == 0 ? q.y : q.w);
+  }
+}
+
+// Weights (and, for MXFP4, the E8M0 scale byte of the lane's 32 K-values,
+// byte 4 st + g of the row: those 32 values are exactly one group) of the 4
+// row blocks for stage st.
+template <int FMT>
+__device__ __forceinline__ void gemm_load_w(const uint8_t* const (&qrow)[4], const uint8_t* const (&srow)[4], int st,
+                                            u32x4_t (&w)[4], uint32_t (&sc)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    w[b] = *reinterpret_cast<const u32x4_t*>(qrow[b] + (size_t)st * 64);
+    if (FMT == kFmtMx) sc[b] = srow[b][4 * st];
+  }
+}
+
+// The thread's quarter of one gathered token row for stage st.
+template <int FMT>
+struct GemmA {
+  static constexpr int N = GemmCfg<FMT>::kAVec;
+  u32x4_t v[N];
+  // The empty asm with a memory clobber keeps the loads where they are
+  // issued: otherwise they are sunk past the MFMA work to their LDS store and
+  // their latency is no longer hidden.
+  __device__ __forceinline__ void load(const uint16_t* asrc, int st) {
+    const u32x4_t* s = reinterpret_cast<const u32x4_t*>(asrc + st * GemmCfg<FMT>::kBK);
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = s[j];
+    asm volatile("" ::: "memory");
+  }
+  __device__ __forceinline__ void store(u32x4_t* dst) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) dst[j] = v[j];
+  }
+};
+
+template <int FMT>
+__device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[4][4], const u32x4_t (&w)[4], const uint32_t (&sc)[4],
+                                             const unsigned char* abase) {
+  constexpr int kArow = GemmCfg<FMT>::kArow;
+#pragma unroll
+  for (int kk = 0; kk < GemmCfg<FMT>::kKK; ++kk) {
+    bf16x8_t bt[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bt[m] = *reinterpret_cast<const bf16x8_t*>(abase + m * 16 * kArow + kk * 16);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bf16x8_t wa = gemm_conv<FMT>(w[b], kk, sc[b]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[b][m] = mfma_16x16x32(wa, bt[m], acc[b][m]);
+    }
+  }
+}
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
+  constexpr int kBK = GemmCfg<FMT>::kBK, kArow = GemmCfg<FMT>::kArow;
+  __shared__ __align__(16) unsigned char lds_a[2][kBM * kArow];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware order over the blocks in use: logical tile = (xcd, run
+  // position); N tiles fastest
+  const int nblk = p.routed ? *p.n_tiles * p.n_ntiles : (int)gridDim.x;
+  if ((int)blockIdx.x >= nblk) return;
+  const int xcd = blockIdx.x & 7, inx = blockIdx.x >> 3;
+  const int per = nblk >> 3, extra = nblk & 7;
+  const int logical = xcd * per + min(xcd, extra) + inx;
+  const int nt = logical % p.n_ntiles;
+  const int tg = logical / p.n_ntiles;
+
+  int e = 0, pos0, ncols;
+  if (p.routed) {
+    const int4 ti = p.tile_info[tg];
+    e = ti.x;
+    pos0 = ti.y;
+    ncols = ti.z;
+  } else {
+    pos0 = tg * kBM;
+    if (pos0 >= p.T) return;
+    ncols = min(kBM, p.T - pos0);
+  }
+
+  const int K = p.K;
+  const int nst = K / kBK;
+  // weight rows of the wave's 4 row blocks (w13: gate, gate, up, up)
+  const uint8_t* qrow[4];
+  const uint8_t* srow[4];
+  {
+    const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
+    const uint8_t* se = FMT == kFmtMx ? p.wsc + (long long)e * p.s_expert_stride : p.wq;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int wrow;
+      if (MODE == kGemmW13) wrow = (b < 2 ? 0 : p.half) + nt * (kBN / 2) + wn * 32 + (b & 1) * 16 + r;
+      else wrow = nt * kBN + wn * 64 + b * 16 + r;
+      qrow[b] = qe + (size_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
+      srow[b] = se + (size_t)wrow * (K / 32) + g;
+    }
+  }
+  // this thread's activation loads: token row tid/4, quarter tid%4 of the
+  // row's stage. Rows past the tile re-read its first row: their results are
+  // never stored.
+  const int arow = tid >> 2, apart = tid & 3;
+  const int apos = pos0 + (arow < ncols ? arow : 0);
+  const size_t atrow = p.act_row ? (size_t)p.act_row[apos] : (size_t)apos;
+  const uint16_t* asrc = p.act + atrow * p.act_ld + apart * (kBK / 4);
+  u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][arow * kArow + apart * (kBK / 2)]);
+  u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][arow * kArow + apart * (kBK / 2)]);
+  const unsigned char* abase0 = &lds_a[0][(wm * 64 + r) * kArow + g * (kBK / 2)];
+  const unsigned char* abase1 = &lds_a[1][(wm * 64 + r) * kArow + g * (kBK / 2)];
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  // Software pipeline, branch-free so that every wait counts exactly: stage
+  // st computes from LDS buffer st%2 and weight registers st%2 while the
+  // activations of st+1 wait in registers and the weights of st+2 are in
+  // flight. Loads past the last stage re-read it (clamped, never used).
+  u32x4_t w0[4], w1[4];
+  uint32_t s0[4] = {0, 0, 0, 0}, s1[4] = {0, 0, 0, 0};
+  GemmA<FMT> av;
+  const int last = nst - 1;
+  gemm_load_w<FMT>(qrow, srow, 0, w0, s0);
+  av.load(asrc, 0);
+  av.store(adst0);
+  av.load(asrc, min(1, last));
+  gemm_load_w<FMT>(qrow, srow, min(1, last), w1, s1);
+  for (int st = 0; st + 1 < nst; st += 2) {
+    __syncthreads();
+    av.store(adst1);  // stage st+1
+    av.load(asrc, min(st + 2, last));
+    gemm_compute<FMT>(acc, w0, s0, abase0);
+    gemm_load_w<FMT>(qrow, srow, min(st + 2, last), w0, s0);
+    __syncthreads();
+    av.store(adst0);  // stage st+2
+    av.load(asrc, min(st + 3, last));
+    gemm_compute<FMT>(acc, w1, s1, abase1);
+    gemm_load_w<FMT>(qrow, srow, min(st + 3, last), w1, s1);
+  }
+  if (nst & 1) {  // the last stage (buffer 0, w0)
+    __syncthreads();
+    gemm_compute<FMT>(acc, w0, s0, abase0);
+  }
+
+  // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int tok = wm * 64 + m * 16 + r;  // position within the tile
+    if (tok >= ncols) continue;
+    const int pos = pos0 + tok;
+    if (MODE == kGemmW13) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int hc = nt * (kBN / 2) + wn * 32 + b * 16 + 4 * g;
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float gv = acc[b][m][i], uv = acc[b + 2][m][i];
+          if (FMT == kFmtI8) {
+            gv *= p.row_scale[hc + i];
+            uv *= p.row_scale[p.half + hc + i];
+          }
+          h[i] = f32_to_bf16(swiglu_clamped(gv, uv, p.limit));
+        }
+        uint2 pk;
+        pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
+      }
+    } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot]
+      const int slot = p.sorted_slots[pos];
+      const float wv = p.slot_w[slot];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = nt * kBN + wn * 64 + b * 16 + 4 * g;
+        *reinterpret_cast<float4*>(p.yout + (size_t)slot * p.yout_ld + n) =
+            make_float4(acc[b][m][0] * wv, acc[b][m][1] * wv, acc[b][m][2] * wv, acc[b][m][3] * wv);
+      }
+    } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = nt * kBN + wn * 64 + b * 16 + 4 * g;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < p.topk; ++j) {
+          const float4 y = *reinterpret_cast<const float4*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
+          o.x += y.x;
+          o.y += y.y;
+          o.z += y.z;
+          o.w += y.w;
+        }
+        o.x += p.row_scale[n] * acc[b][m][0];
+        o.y += p.row_scale[n + 1] * acc[b][m][1];
+        o.z += p.row_scale[n + 2] * acc[b][m][2];
+        o.w += p.row_scale[n + 3] * acc[b][m][3];
+        if (p.out_is_fp32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)pos * p.out_ld + n) = o;
+        } else {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16);
+          pk.y = (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (size_t)pos * p.out_ld + n) = pk;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int MODE>
+static hipError_t launch_gemm_t(const GemmArgs& p, int tiles, hipStream_t st) {
+  const long long nblk = (long long)tiles * p.n_ntiles;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  k_gemm<FMT, MODE><<<(unsigned)nblk, kThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st) {
+  if (p.K % 128 || p.K <= 0) return hipErrorInvalidValue;
+  if (p.fmt == kFmtMx) {
+    if (p.mode == kGemmW13) return launch_gemm_t<kFmtMx, kGemmW13>(p, tiles, st);
+    return launch_gemm_t<kFmtMx, kGemmW2>(p, tiles, st);
+  }
+  if (p.mode == kGemmW13) return launch_gemm_t<kFmtI8, kGemmW13>(p, tiles, st);
+  return launch_gemm_t<kFmtI8, kGemmW2Combine>(p, tiles, st);
+}
+
+}  // namespace moe

@@ -106,6 +106,40 @@ struct W2CombineArgs {
   int out_is_fp32;
 };
 
+// Grouped GEMM (gemm.hip) for large T: tiles of 128 token positions x 256
+// weight rows.
+enum { kGemmW13 = 0, kGemmW2 = 1, kGemmW2Combine = 2 };
+struct GemmArgs {
+  int fmt;                    // 0 MXFP4 (routed), 1 int8 (shared)
+  int mode;                   // kGemmW13: SwiGLU -> hout; kGemmW2: x slot weight -> yout[slot];
+                              // kGemmW2Combine: shared w2 + sum of the slots' ybuf -> out
+  const uint8_t* wq;
+  const uint8_t* wsc;
+  const float* row_scale;     // int8 per-row scales
+  long long q_expert_stride, s_expert_stride;
+  int K, half;
+  int routed;                 // tiles from tile_info (routed) or consecutive tokens (shared)
+  const int4* tile_info;
+  const int32_t* n_tiles;
+  int n_ntiles;               // tiles along the weight rows
+  int T;
+  const uint16_t* act;
+  int act_ld;
+  const int32_t* act_row;     // row of act for each position (null: the position)
+  uint16_t* hout;
+  int hout_ld;
+  float* yout;
+  int yout_ld;
+  const int32_t* sorted_slots;
+  const float* slot_w;
+  const float* ybuf;          // combine: [T*k][H]
+  int topk;
+  void* out;
+  int out_ld, out_is_fp32;
+  float limit;
+};
+constexpr int kGemmTokens = 128;  // token positions per GEMM tile
+
 struct CombineArgs {
   int T, H, k;
   const float* ybuf;  // [T*k][H] weighted expert outputs in slot order
@@ -131,6 +165,7 @@ hipError_t launch_w2(const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int
 hipError_t launch_shared_w13(const SkinnyArgs& a, int blocks, hipStream_t st);
 hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
