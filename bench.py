@@ -33,12 +33,23 @@ METRIC = "MoE-layer tokens/s at T=1/64/8192; % of HBM BW (decode) / bf16 MFMA pe
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 
-DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel, bound
+DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), bound
     "decode_t1": (1000, 50, 12, "routed_w13", "hbm"),
     "decode_t64": (200, 20, 12, "routed_w13", "hbm"),
     "prefill_t8192": (20, 3, 1, "routed_w13", "mfma"),
     "hash_t4096": (20, 3, 1, "routed_w13", "mfma"),
 }
+# The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
+# names it, and what it does there.
+DOMINANT = {
+    "decode_t1": ("moe::k_pair<0, 0, 0, 0, 4, 8, 8>",
+                  "routed w13: top-6 in-block + MXFP4 GEMV + clamped SwiGLU, one block per (slot, 16 rows)"),
+    "decode_t64": ("moe::k_pair<0, 0, 1, 1, 8, 4, 4>",
+                   "routed w13 (MXFP4 skinny GEMM + clamped SwiGLU) with the shared expert's int8 w2"),
+    "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
+    "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
+}
+COPY_CAL_BYTES = 1 << 28  # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
 
 def parse():
@@ -54,6 +65,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of %d bytes 5 times (the counters' calibration)"
+                    % COPY_CAL_BYTES)
+    ap.add_argument("--summarize", metavar="OUTDIR", default=None,
+                    help="write the profiles/ summaries of --workload from the rocprofv3 output under OUTDIR "
+                    "(kernel_trace/, pmc_fetch/, pmc_write/, copy_fetch/, copy_write/) and exit")
+    ap.add_argument("--commands", default=None, help="with --summarize: JSON file of the commands that ran")
     return ap.parse_args()
 
 
@@ -120,7 +138,8 @@ def source_hash() -> str:
 def traffic_from_profiles(workload: str):
     """HBM bytes per launch of the dominant kernel from committed counter
     summaries, if they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    short = DOMINANT[workload][0].split("::")[1].split("<")[0]
+    p = os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -128,6 +147,97 @@ def traffic_from_profiles(workload: str):
     if rec.get("source_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_CAL_BYTES, five times: under
+    rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE per dispatch calibrate the
+    counters against a known number of bytes read and written."""
+    import torch
+
+    src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(dst[:4096], src[:4096]))
+    print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "dispatches": 5, "ok": ok}), flush=True)
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(outdir, sub, name):
+    d = os.path.join(outdir, sub)
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(name):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{name} under {d}")
+
+
+def _counter_avg(path, counter, match):
+    """Mean counter value (KiB) per dispatch of the kernels whose name holds
+    `match`."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(path)
+            if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"no {counter} rows for {match} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(workload, outdir, commands):
+    """Turn one workload's rocprofv3 runs into the committed summaries:
+    profiles/moe_forward_<workload>_kernels.md (per-kernel durations) and,
+    when the counter runs exist, profiles/<kernel>_<workload>_traffic.txt
+    (HBM bytes per launch of the dominant kernel, calibrated by a plain copy
+    of known size, stamped with the hash of the kernel sources)."""
+    kname, what = DOMINANT[workload]
+    short = kname.split("::")[1].split("<")[0]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    stats = _csv_rows(_find(outdir, "kernel_trace", "kernel_stats.csv"))
+    lines = [f"# Kernel durations, moe_forward, workload {workload}", "",
+             f"Source hash of the kernels: `{source_hash()}`", "",
+             "Command:", "", "```", commands.get("kernel_trace", "?"), "```", "",
+             f"Dominant kernel: `{kname}` ({what}).", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        nm = r["Name"]
+        if len(nm) > 90:
+            nm = nm[:87] + "..."
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    with open(os.path.join(ROOT, "profiles", f"moe_forward_{workload}_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        fk, nf = _counter_avg(_find(outdir, "pmc_fetch", "counter_collection.csv"), "FETCH_SIZE", kname)
+        wk, nw = _counter_avg(_find(outdir, "pmc_write", "counter_collection.csv"), "WRITE_SIZE", kname)
+        cf, _ = _counter_avg(_find(outdir, "copy_fetch", "counter_collection.csv"), "FETCH_SIZE",
+                             "__amd_rocclr_copyBuffer")
+        cw, _ = _counter_avg(_find(outdir, "copy_write", "counter_collection.csv"), "WRITE_SIZE",
+                             "__amd_rocclr_copyBuffer")
+    except (FileNotFoundError, ValueError) as e:
+        print(f"no traffic summary: {e}")
+        return
+    f_fac = COPY_CAL_BYTES / (cf * 1024.0)
+    w_fac = COPY_CAL_BYTES / (cw * 1024.0)
+    rec = {
+        "workload": workload, "kernel": kname, "source_hash": source_hash(),
+        "fetch_kib_per_dispatch": round(fk, 2), "write_kib_per_dispatch": round(wk, 2),
+        "dispatches": [nf, nw],
+        "copy_bytes": COPY_CAL_BYTES, "copy_fetch_kib": round(cf, 2), "copy_write_kib": round(cw, 2),
+        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+        "bytes_per_launch": int(round(fk * 1024.0 * f_fac + wk * 1024.0 * w_fac)),
+        "commands": {k: v for k, v in commands.items() if k != "kernel_trace"},
+    }
+    with open(os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(layer, batches, tids, budget_s):
@@ -160,9 +270,19 @@ def cpu_baseline(layer, batches, tids, budget_s):
 
 def main():
     args = parse()
+    if args.summarize:
+        cmds = {}
+        if args.commands:
+            with open(args.commands) as f:
+                cmds = json.load(f)
+        summarize(args.workload, args.summarize, cmds)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
+        print(json.dumps({"error": "the layer runs on a single GPU: --gpus must be 1 (there is no multi-GPU path)"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
 
@@ -283,7 +403,7 @@ def main():
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4))
     traffic = traffic_from_profiles(args.workload)
     roof["traffic"] = traffic
-    roof["kernel"] = f"k_skinny<mxfp4,w13> ({kernel})"
+    roof["kernel"] = DOMINANT[args.workload][0]
     roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
     layer_bw = alg["layer_bytes"] / (ms_step / 1e3) / 1e9
     layer_tf = alg["layer_flops"] / (ms_step / 1e3) / 1e12
