@@ -45,8 +45,8 @@
  *   - Device-side values are trusted: expert ids must lie in [0, E), token
  *     ids in [0, V); E8M0 scale bytes should not be 0xFF (NaN).
  *   - `workspace` is device scratch of at least moe_workspace_size() bytes,
- *     256-byte aligned, zero-filled once before its first use (the library
- *     leaves its counters at zero after every call). Calls that share one
+ *     256-byte aligned. Its contents on entry do not matter: every call
+ *     writes each workspace value before reading it. Calls that share one
  *     workspace must be ordered on one stream.
  *   - Supported shapes: H and I multiples of 128, 1 <= top_k <= 8,
  *     top_k <= E <= 256, 0 <= T <= 65536. Device pointers must be 16-byte
@@ -92,7 +92,8 @@ const char* moe_version(void);
 size_t moe_workspace_size(const moe_config* cfg, int32_t T);
 
 /* Zero-fill a workspace on `stream` (with a fill kernel, so it may be
- * captured in a HIP graph). Equivalent to filling it with zero bytes. */
+ * captured in a HIP graph). Optional: no entry point needs it; it gives the
+ * workspace defined contents, e.g. for inspection. */
 int moe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Learned router: scores, bias-assisted top-k, renormalised weights.
