@@ -18,7 +18,7 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, logits, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
+  size_t counters, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
   int tile_n, max_tiles;
 };
@@ -73,7 +73,7 @@ Layout layout(const moe_config& c, int T) {
     return at;
   };
   L.counters = take(256);
-  L.logits = take((size_t)T * E * 4);
+  L.scores = take((size_t)2 * T * E * 4);  // scores, then selection values
   L.ids = take(slots * 4);
   L.w = take(slots * 4);
   L.offsets = take((E + 1) * 4);
@@ -191,8 +191,9 @@ SkinnyArgs routed_w2_args(const moe_config& c, int T, const Perm& p, const float
 }
 
 // Shared expert w13 + SwiGLU: hs [T][I] bf16.
+// slim: blocks of 8 gate + 8 up rows (the router launch); else 16 + 16.
 SkinnyArgs shared_w13_args(const moe_config& c, int T, const uint16_t* x, const int8_t* q13, const float* s13,
-                           uint16_t* hs, int* blocks) {
+                           uint16_t* hs, int* blocks, bool slim) {
   const int H = c.hidden_size, I = c.moe_intermediate;
   SkinnyArgs a = skinny_common(c, T);
   a.routed = 0;
@@ -202,7 +203,7 @@ SkinnyArgs shared_w13_args(const moe_config& c, int T, const uint16_t* x, const 
   a.row_scale = s13;
   a.K = H;
   a.half = I;
-  a.n_rowblocks = I / 16;
+  a.n_rowblocks = slim ? I / 8 : I / 16;
   a.act = x;
   a.act_ld = H;
   a.hout = hs;
@@ -340,7 +341,7 @@ int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
 }
 
 RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const float* gate_w, const float* bias,
-                       const float* logit_offset, float* logits, int32_t* ids, float* w) {
+                       const float* logit_offset, float* scores, int32_t* ids, float* w) {
   RouterArgs a;
   a.T = T;
   a.H = c.hidden_size;
@@ -351,7 +352,8 @@ RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const floa
   a.gate_w = gate_w;
   a.bias = bias;
   a.logit_offset = logit_offset;
-  a.logits = logits;
+  a.scores = scores;
+  a.keys = scores + (size_t)T * c.n_routed_experts;
   a.ids = ids;
   a.w = w;
   return a;
@@ -405,7 +407,7 @@ int moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* 
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(*cfg, T);
-  RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), topk_ids,
+  RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), topk_ids,
                              topk_w);
   if (T <= kSmallT) {
     Perm p = perm_of(workspace, L, at<int32_t>(workspace, L.offsets), at<int32_t>(workspace, L.sorted),
@@ -536,8 +538,9 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   uint16_t* hs = at<uint16_t>(workspace, L.hs);
   float* ybuf = at<float>(workspace, L.ybuf);
   float* zbuf = at<float>(workspace, L.zbuf);
-  int sh13_blocks = 0, sh2_blocks = 0;
-  const SkinnyArgs s13 = shared_w13_args(*cfg, T, x, sh_w13, sh_w13_scale, hs, &sh13_blocks);
+  int sh13_blocks = 0, sh13w_blocks = 0, sh2_blocks = 0;
+  const SkinnyArgs s13 = shared_w13_args(*cfg, T, x, sh_w13, sh_w13_scale, hs, &sh13_blocks, true);
+  const SkinnyArgs s13w = shared_w13_args(*cfg, T, x, sh_w13, sh_w13_scale, hs, &sh13w_blocks, false);
   const SkinnyArgs s2 = shared_w2_args(*cfg, T, sh_w2, sh_w2_scale, hs, zbuf, &sh2_blocks);
   const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
   const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
@@ -548,7 +551,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   if (tiny) {
     // router logits + shared w13 | routed w13 (top-k in each block, one tile
     // per slot) | routed w2 + shared w2 + combine
-    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
     rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, &s13, sh13_blocks, st); }));
     if (rc) return rc;
     SkinnyArgs t13 = r13;
@@ -556,8 +559,8 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     t13.tile_n = 1;
     t13.n_tiles_grid = T * cfg->top_k;
     t13.act_row = nullptr;
-    t13.logits = a.logits;
-    t13.bias = bias;
+    t13.scores = a.scores;
+    t13.keys = a.keys;
     t13.scale = cfg->routed_scaling_factor;
     t13.E = cfg->n_routed_experts;
     t13.topk = cfg->top_k;
@@ -572,7 +575,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   }
   if (decode) {
     // router logits + shared w13 | top-k + permutation | routed w13 + shared w2 | routed w2 | combine
-    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
     rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, &s13, sh13_blocks, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] { return launch_topk_permute_small(a, p, st); }));
@@ -600,7 +603,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       h.w = w;
       rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_hash_route(h, st); }));
     } else {
-      RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.logits), ids, w);
+      RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
       rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_large(a, st); }));
     }
     if (rc) return rc;
@@ -625,7 +628,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       return status(timed(MOE_KERNEL_SHARED_W2, st, [&] { return launch_gemm(h2, sh_tiles, st); }));
     }
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st,
-                      [&] { return launch_w13(r13, r13_blocks, &s13, sh13_blocks, false, st); }));
+                      [&] { return launch_w13(r13, r13_blocks, &s13w, sh13w_blocks, false, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2(r2, r2_blocks, &s2, sh2_blocks, st); }));
     if (rc) return rc;

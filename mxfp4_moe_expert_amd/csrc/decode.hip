@@ -21,7 +21,7 @@
 
 namespace moe {
 
-template <int MAXU, int MAXS>
+template <int MAXU, int MAXS, int MAXA>
 __global__ __launch_bounds__(kThreads) void k_w2_combine_small(W2CombineArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -38,50 +38,66 @@ __global__ __launch_bounds__(kThreads) void k_w2_combine_small(W2CombineArgs a) 
   float* ycol = reinterpret_cast<float*>(red + kWaves * 64);                    // [16 rows][16 columns]
   int32_t* sid = reinterpret_cast<int32_t*>(ycol + 256);                         // [16] expert of each slot
 
-  if (tid < nslots) sid[tid] = a.ids[tid];
+  // Loads are issued in the order they are needed, since a wait for one load
+  // also waits for every load issued before it: the slots' experts, then the
+  // work that does not depend on them (activation columns, shared w2 rows),
+  // then the routed E8M0 scales and weights.
+  const int my_id = tid < nslots ? a.ids[tid] : 0;
+  const int n16 = I >> 3;
+  const int nact = ncols * n16;
+  auto act_src = [&](int i) {
+    const int c = i / n16, o = i - c * n16;
+    const uint16_t* src = c < nslots ? a.hbuf + (size_t)c * I : a.hs + (size_t)(c - nslots) * I;
+    return reinterpret_cast<const u32x4_t*>(src) + o;
+  };
+  auto act_dst = [&](int i) {
+    const int c = i / n16, o = i - c * n16;
+    return reinterpret_cast<u32x4_t*>(lds + c * row_bytes + o * 16);
+  };
+  // (indices past the end are clamped, not skipped: the loads stay
+  // unconditional, so the compiler's waits count them exactly; what a
+  // clamped load returns is never used)
+  u32x4_t av[MAXA];
+#pragma unroll
+  for (int i = 0; i < MAXA; ++i) av[i] = *act_src(min(tid + i * kThreads, nact - 1));
+  const int row = rb * 16 + r;
+  uint4 qs[2 * MAXS];
+  const uint8_t* shrow = reinterpret_cast<const uint8_t*>(a.sh_w2) + (size_t)row * I + g * 32;
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = min(wave + kWaves * i, S - 1);
+    qs[2 * i] = *reinterpret_cast<const uint4*>(shrow + s * 128);
+    qs[2 * i + 1] = *reinterpret_cast<const uint4*>(shrow + s * 128 + 16);
+  }
+  if (tid < nslots) sid[tid] = my_id;
   __syncthreads();
 
-  // every unit's weights are requested first
-  const int row = rb * 16 + r;
-  const long long qstride = (long long)H * (I / 2), sstride = (long long)H * (I / 32);
-  uint4 q[MAXU];
-#pragma unroll
-  for (int i = 0; i < MAXU; ++i) {
-    const int u = wave + kWaves * i;
-    if (u < nunits) {
-      const int j = u / S, s = u - j * S;
-      const int e = sid[j];
-      q[i] = *reinterpret_cast<const uint4*>(a.w2c + e * qstride + (size_t)row * (I / 2) + s * 64 + g * 16);
-    }
-  }
   // the E8M0 scales of every slot's 16 rows (a contiguous run of 16 * I/32
-  // bytes per slot) in 16-byte pieces
+  // bytes per slot) in 16-byte pieces, then every routed unit's weights
+  const long long qstride = (long long)H * (I / 2), sstride = (long long)H * (I / 32);
   const int ppr = I / 32;  // 16-byte pieces per run = scale bytes per row
   const int npieces = nslots * ppr;
   auto sc_src = [&](int ii) {
     const int j = ii / ppr, off = (ii - j * ppr) * 16;
     return reinterpret_cast<const uint4*>(a.w2s + sid[j] * sstride + (size_t)(rb * 16) * ppr + off);
   };
-  uint4 sc0 = make_uint4(0, 0, 0, 0), sc1 = make_uint4(0, 0, 0, 0);
-  if (tid < npieces) sc0 = *sc_src(tid);
-  if (tid + kThreads < npieces) sc1 = *sc_src(tid + kThreads);
-  uint4 qs[2 * MAXS];
-  const uint8_t* shrow = reinterpret_cast<const uint8_t*>(a.sh_w2) + (size_t)row * I + g * 32;
+  const uint4 sc0 = *sc_src(min(tid, npieces - 1));
+  const uint4 sc1 = *sc_src(min(tid + kThreads, npieces - 1));
+  uint4 q[MAXU];
 #pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
-    const int s = wave + kWaves * i;
-    if (s < S) {
-      qs[2 * i] = *reinterpret_cast<const uint4*>(shrow + s * 128);
-      qs[2 * i + 1] = *reinterpret_cast<const uint4*>(shrow + s * 128 + 16);
-    }
+  for (int i = 0; i < MAXU; ++i) {
+    const int u = min(wave + kWaves * i, nunits - 1);
+    const int j = u / S, s = u - j * S;
+    const int e = sid[j];
+    q[i] = *reinterpret_cast<const uint4*>(a.w2c + e * qstride + (size_t)row * (I / 2) + s * 64 + g * 16);
   }
   // activation columns -> LDS: slots' h, then the tokens' shared h
-  const int n16 = I >> 3;
-  for (int i = tid; i < ncols * n16; i += kThreads) {
-    const int c = i / n16, o = i - c * n16;
-    const uint16_t* src = c < nslots ? a.hbuf + (size_t)c * I : a.hs + (size_t)(c - nslots) * I;
-    *reinterpret_cast<uint4*>(lds + c * row_bytes + o * 16) = reinterpret_cast<const uint4*>(src)[o];
+#pragma unroll
+  for (int i = 0; i < MAXA; ++i) {
+    const int ii = tid + i * kThreads;
+    if (ii < nact) *act_dst(ii) = av[i];
   }
+  for (int ii = tid + MAXA * kThreads; ii < nact; ii += kThreads) *act_dst(ii) = *act_src(ii);
   auto sc_store = [&](int ii, const uint4& v) {
     const int j = ii / ppr, off = (ii - j * ppr) * 16;
     const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
@@ -98,27 +114,6 @@ __global__ __launch_bounds__(kThreads) void k_w2_combine_small(W2CombineArgs a) 
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const bf16x8_t zero8 = {};
-  auto routed_unit = [&](const uint4& qq, int u) {
-    const int j = u / S, s = u - j * S;
-    const float scale = e8m0_scale_operand(lds_sc[(size_t)(j * 16 + r) * srow + s * 4 + g]);
-    const unsigned char* bsrc = lds + j * row_bytes + s * 256 + g * 64;
-    const uint32_t d[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const bf16x8_t b = (r == j) ? *reinterpret_cast<const bf16x8_t*>(bsrc + jj * 16) : zero8;
-      acc = mfma_16x16x32(fp4x8_to_bf16x8(d[jj], scale), b, acc);
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < MAXU; ++i) {
-    const int u = wave + kWaves * i;
-    if (u < nunits) routed_unit(q[i], u);
-  }
-  for (int u = wave + kWaves * MAXU; u < nunits; u += kWaves) {  // beyond the register budget
-    const int j = u / S, s = u - j * S;
-    const int e = sid[j];
-    routed_unit(*reinterpret_cast<const uint4*>(a.w2c + e * qstride + (size_t)row * (I / 2) + s * 64 + g * 16), u);
-  }
   auto shared_unit = [&](const uint4& lo, const uint4& hi, int s) {
     const bool mine = r >= nslots && r < ncols;
     const unsigned char* bsrc = lds + (mine ? r : 0) * row_bytes + s * 256 + g * 64;
@@ -140,6 +135,27 @@ __global__ __launch_bounds__(kThreads) void k_w2_combine_small(W2CombineArgs a) 
                 s);
   }
 
+  auto routed_unit = [&](const uint4& qq, int u) {
+    const int j = u / S, s = u - j * S;
+    const float scale = e8m0_scale_operand(lds_sc[(size_t)(j * 16 + r) * srow + s * 4 + g]);
+    const unsigned char* bsrc = lds + j * row_bytes + s * 256 + g * 64;
+    const uint32_t d[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bf16x8_t b = (r == j) ? *reinterpret_cast<const bf16x8_t*>(bsrc + jj * 16) : zero8;
+      acc = mfma_16x16x32(fp4x8_to_bf16x8(d[jj], scale), b, acc);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < MAXU; ++i) {
+    const int u = wave + kWaves * i;
+    if (u < nunits) routed_unit(q[i], u);
+  }
+  for (int u = wave + kWaves * MAXU; u < nunits; u += kWaves) {  // beyond the register budget
+    const int j = u / S, s = u - j * S;
+    const int e = sid[j];
+    routed_unit(*reinterpret_cast<const uint4*>(a.w2c + e * qstride + (size_t)row * (I / 2) + s * 64 + g * 16), u);
+  }
   red[wave * 64 + lane] = acc;
   __syncthreads();
   if (wave == 0) {
@@ -170,7 +186,7 @@ hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st) {
   const size_t lds = (size_t)ncols * (a.I * 2 + 16) + (size_t)a.T * a.k * 16 * (a.I / 32 + 4) +
                      (size_t)kWaves * 64 * 16 + 256 * 4 + 16 * 4;
   const int units_per_wave = (a.T * a.k * (a.I / 128) + kWaves - 1) / kWaves;
-  auto kern = units_per_wave <= 12 ? &k_w2_combine_small<12, 2> : &k_w2_combine_small<24, 2>;
+  auto kern = units_per_wave <= 12 ? &k_w2_combine_small<12, 2, 8> : &k_w2_combine_small<24, 2, 8>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

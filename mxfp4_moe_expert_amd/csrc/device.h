@@ -81,82 +81,78 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
   return silu(gc) * uc;
 }
 
-// One step of a wave-wide argmax: compare with the value DPP brings in;
-// larger value wins, equal values go to the smaller index. Lanes the DPP
-// pattern leaves without a source see (-inf, INT_MAX) and keep their pair.
+// Top-k keys: the fp32 selection value b mapped to an unsigned integer of the
+// same order in the high word, the inverted expert id in the low word, so
+// that one unsigned 64-bit comparison orders by b and then by the lower id.
+// Every valid key is above 0, which marks "no candidate".
+__device__ __forceinline__ uint64_t topk_key(float b, int e) {
+  const uint32_t u = __float_as_uint(b);
+  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)hi << 32) | (uint32_t)~e;
+}
+
+// One step of a wave-wide max of 64-bit keys: the key DPP brings in replaces
+// the lane's if larger. Lanes the pattern leaves without a source see 0.
 template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL,
-                                                              ROW_MASK, BANK_MASK, false));
-  const int oi = __builtin_amdgcn_update_dpp(0x7fffffff, i, CTRL, ROW_MASK, BANK_MASK, false);
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+__device__ __forceinline__ uint64_t keymax_dpp_step(uint64_t key) {
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(key >> 32), CTRL, ROW_MASK, BANK_MASK, false);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)key, CTRL, ROW_MASK, BANK_MASK, false);
+  const uint64_t other = ((uint64_t)hi << 32) | lo;
+  return other > key ? other : key;
 }
 
-// Wave-wide argmax of (v, i) (larger v, ties to the smaller i), returned to
-// every lane: quad swaps, row rotations by 4 and 8 (each 16-lane row then
-// holds its row result), row broadcasts 15 and 31 (lane 63 holds the wave
-// result), read from lane 63.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_dpp_step<0xB1>(v, i);         // quad_perm [1,0,3,2]
-  argmax_dpp_step<0x4E>(v, i);         // quad_perm [2,3,0,1]
-  argmax_dpp_step<0x124>(v, i);        // row_ror:4
-  argmax_dpp_step<0x128>(v, i);        // row_ror:8
-  argmax_dpp_step<0x142, 0xA>(v, i);   // row_bcast:15 -> rows 1, 3
-  argmax_dpp_step<0x143, 0xC>(v, i);   // row_bcast:31 -> rows 2, 3
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+// Wave-wide max of 64-bit keys, returned to every lane: quad swaps, row
+// rotations by 4 and 8 (each 16-lane row then holds its row maximum), row
+// broadcasts 15 and 31 (lane 63 holds the wave maximum), read from lane 63.
+__device__ __forceinline__ uint64_t wave_keymax(uint64_t key) {
+  key = keymax_dpp_step<0xB1>(key);        // quad_perm [1,0,3,2]
+  key = keymax_dpp_step<0x4E>(key);        // quad_perm [2,3,0,1]
+  key = keymax_dpp_step<0x124>(key);       // row_ror:4
+  key = keymax_dpp_step<0x128>(key);       // row_ror:8
+  key = keymax_dpp_step<0x142, 0xA>(key);  // row_bcast:15 -> rows 1, 3
+  key = keymax_dpp_step<0x143, 0xC>(key);  // row_bcast:31 -> rows 2, 3
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(key >> 32), 63);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave selects the top-k experts of one token from its E <= 256 logits
-// (fp32): s = sqrt(softplus(logit)), chosen by s + bias, descending, ties to
-// the lower expert id; weights scale * s / sum(s) over the chosen, summed in
-// slot order. Lane l owns experts l, l+64, l+128, l+192; each of the k rounds
-// is one DPP wave argmax. Lane 0 writes ids/weights for slots j = 0..k-1 and,
-// if ids_lds is given, the ids there too.
-__device__ __forceinline__ void wave_topk(const float* logits_row, const float* bias, int E, int k, float scale,
-                          int32_t* ids_out, float* w_out, int32_t* ids_lds) {
+// One wave selects the top-k experts of one token from its E <= 256 scores
+// s (fp32 sqrt(softplus(logit))) and selection values b = fp32(s + bias):
+// the k largest b, ties to the lower expert id; weights scale * s / sum(s)
+// over the chosen, summed in slot order. Lane l owns experts l, l+64, l+128,
+// l+192; each of the k rounds is one branch-free DPP wave max of 64-bit keys.
+// Lane 0 writes ids/weights for slots j = 0..k-1 and, if ids_lds is given,
+// the ids there too.
+__device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row, int E, int k, float scale,
+                                          int32_t* ids_out, float* w_out, int32_t* ids_lds) {
   const int lane = threadIdx.x & 63;
-  float s[4], b[4];
+  float s[4];
+  uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    if (e < E) {
-      s[q] = sqrtf(softplus(logits_row[e]));
-      b[q] = s[q] + bias[e];
-    } else {
-      s[q] = 0.0f;
-      b[q] = -INFINITY;
-    }
+    const int ec = e < E ? e : E - 1;  // loads stay in bounds; surplus lanes get key 0
+    s[q] = s_row[ec];
+    key[q] = e < E ? topk_key(b_row[ec], e) : 0;
   }
-  unsigned taken = 0;
   float sel_s[kTopKMax];
   int sel_id[kTopKMax];
 #pragma unroll
   for (int j = 0; j < kTopKMax; ++j) {
     sel_s[j] = 0.0f;
     sel_id[j] = 0;
-    if (j >= k) continue;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      const bool ok = e < E && !(taken & (1u << q));
-      if (ok && (b[q] > bv || (b[q] == bv && e < bi))) {
-        bv = b[q];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    const int owner = bi & 63, q_of = bi >> 6;
+    if (j >= k) continue;  // uniform
+    uint64_t m = key[0] > key[1] ? key[0] : key[1];
+    const uint64_t m2 = key[2] > key[3] ? key[2] : key[3];
+    m = m > m2 ? m : m2;
+    m = wave_keymax(m);
+    const int e = (int)~(uint32_t)m;
+    const int owner = e & 63, q_of = e >> 6;
     const float mys = (q_of == 0) ? s[0] : (q_of == 1) ? s[1] : (q_of == 2) ? s[2] : s[3];
-    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mys), owner));
-    if (lane == owner) taken |= 1u << q_of;
-    sel_s[j] = ws;
-    sel_id[j] = bi;
+    sel_s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mys), owner));
+    sel_id[j] = e;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) key[q] = (lane == owner && q == q_of) ? 0 : key[q];
   }
   if (lane == 0) {
     float sum = 0.0f;

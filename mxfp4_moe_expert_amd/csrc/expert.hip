@@ -66,11 +66,39 @@ hipError_t launch_shared_w13(const SkinnyArgs& a, int blocks, hipStream_t st) {
   return launch_pair<kFmtI8, kW13, kFmtI8, kW13>(a, blocks, nullptr, 0, st);
 }
 
-// Routed w13 alone with 4-wave blocks and 8 super-steps per wave in flight:
-// with K = 4096 a whole 16-row slice of a slot's expert is requested at once
-// and the decode grid (slots x I/16 blocks) is resident in one round.
+// One pass alone (EXACT: K = 128 * NPF * WAVES).
+template <int F, int S, int WAVES, int NPF, bool EXACT>
+__global__ __launch_bounds__(WAVES * 64) void k_single(SkinnyArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  skinny_block<F, S, WAVES, NPF, EXACT>(a, blockIdx.x, lds);
+}
+
+template <int F, int S, int WAVES, int NPF, bool EXACT>
+static hipError_t launch_single(const SkinnyArgs& a, int blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  const size_t lds = skinny_lds_bytes(a.tile_n, a.K, S, WAVES);
+  auto kern = &k_single<F, S, WAVES, NPF, EXACT>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  kern<<<(unsigned)blocks, WAVES * 64, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+// Routed w13 alone with 4-wave blocks and up to 8 super-steps per wave in
+// flight: with K <= 4096 a whole 16-row slice of a slot's expert is requested
+// at once and the decode grid (slots x I/16 blocks) is resident in one round.
+// K = 512 .. 4096 (powers of two) take the branch-free block.
 hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st) {
-  return launch_pair<kFmtMx, kW13, kFmtMx, kW13, 4, 8, 8>(a, blocks, nullptr, 0, st);
+  switch (a.K) {
+    case 512: return launch_single<kFmtMx, kW13, 4, 1, true>(a, blocks, st);
+    case 1024: return launch_single<kFmtMx, kW13, 4, 2, true>(a, blocks, st);
+    case 2048: return launch_single<kFmtMx, kW13, 4, 4, true>(a, blocks, st);
+    case 4096: return launch_single<kFmtMx, kW13, 4, 8, true>(a, blocks, st);
+    default: return launch_single<kFmtMx, kW13, 4, 8, false>(a, blocks, st);
+  }
 }
 
 // ---------------------------------------------------------------- combine

@@ -35,7 +35,8 @@ struct RouterArgs {
   const float* gate_w;
   const float* bias;
   const float* logit_offset;
-  float* logits;  // [T][E]
+  float* scores;  // [T][E] s = sqrt(softplus(logit)), fp32
+  float* keys;    // [T][E] selection values fp32(s + bias)
   int32_t* ids;   // [T][k]
   float* w;       // [T][k]
 };
@@ -80,9 +81,10 @@ struct SkinnyArgs {
   const int32_t* sorted_slots;
   const float* slot_w;        // w2 routed: combine weight of each slot
   float limit;
-  // routed == 2 only: router logits and the routing outputs this pass writes
-  const float* logits;        // [T][E]
-  const float* bias;          // [E]
+  // routed == 2 only: router scores and selection values, and the routing
+  // outputs this pass writes
+  const float* scores;        // [T][E]
+  const float* keys;          // [T][E]
   float scale;
   int E, topk;
   int32_t* ids_out;           // [T][k]

@@ -15,7 +15,7 @@
 // fp32 values s + bias; equal values go to the lower expert id.
 //
 // Decode sizes (T <= kSmallT) use two launches: k_router_small computes the
-// logits, one block per expert, and shares its launch with the shared
+// logits and from them the scores and selection values, one block per expert, and shares its launch with the shared
 // expert's w13 blocks (that work does not depend on the routing); then one
 // block (k_topk_permute_small) selects the experts of every token and builds
 // the permutation and the expert tile table.
@@ -27,7 +27,59 @@ namespace moe {
 
 // ---------------------------------------------------------------- small-T router
 
+// Score and selection value of (token t, expert e) from its logit, computed
+// once here so that every top-k reader only compares.
+__device__ __forceinline__ void store_score(const RouterArgs& a, int t, int e, float logit) {
+  const float sc = sqrtf(softplus(logit));
+  a.scores[(size_t)t * a.E + e] = sc;
+  a.keys[(size_t)t * a.E + e] = sc + a.bias[e];
+}
+
+// Logits of expert e for 8 < T <= kSmallT tokens, H <= 4096: wave w takes
+// tokens w, w + 8, ...; lane l holds elements 512 c + 8 l .. +8 (c < H/512)
+// of the expert's router row in registers and reduces one token at a time.
+__device__ __forceinline__ void router_logits_waves(const RouterArgs& a, int e) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int H = a.H;
+  const float* we = a.gate_w + (size_t)e * H;
+  float4 w[16];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int k0 = c * 512 + lane * 8;
+    const bool ok = k0 < H;
+    w[2 * c] = ok ? *reinterpret_cast<const float4*>(we + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    w[2 * c + 1] = ok ? *reinterpret_cast<const float4*>(we + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float off = a.logit_offset ? a.logit_offset[e] : 0.0f;
+  for (int t = wave; t < a.T; t += kWaves) {
+    const uint16_t* xt = a.x + (size_t)t * H;
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int k0 = c * 512 + lane * 8;
+      if (k0 < H) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xt + k0);
+        const float4 w0 = w[2 * c], w1 = w[2 * c + 1];
+        acc += bf16_to_f32(xv.x & 0xffff) * w0.x;
+        acc += bf16_to_f32(xv.x >> 16) * w0.y;
+        acc += bf16_to_f32(xv.y & 0xffff) * w0.z;
+        acc += bf16_to_f32(xv.y >> 16) * w0.w;
+        acc += bf16_to_f32(xv.z & 0xffff) * w1.x;
+        acc += bf16_to_f32(xv.z >> 16) * w1.y;
+        acc += bf16_to_f32(xv.w & 0xffff) * w1.z;
+        acc += bf16_to_f32(xv.w >> 16) * w1.w;
+      }
+    }
+    const float v = wave_sum(acc);
+    if (lane == 0) store_score(a, t, e, v + off);
+  }
+}
+
 __device__ __forceinline__ void router_logits_block(const RouterArgs& a, int e, unsigned char* lds) {
+  if (a.T > 8 && a.H <= 4096) {
+    router_logits_waves(a, e);
+    return;
+  }
   float* red = reinterpret_cast<float*>(lds);  // [kWaves][kSmallT]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = a.H;
@@ -70,19 +122,22 @@ __device__ __forceinline__ void router_logits_block(const RouterArgs& a, int e, 
     const float* v = red + t;
     const float sum = ((v[0] + v[kSmallT]) + (v[2 * kSmallT] + v[3 * kSmallT])) +
                       ((v[4 * kSmallT] + v[5 * kSmallT]) + (v[6 * kSmallT] + v[7 * kSmallT]));
-    a.logits[(size_t)t * a.E + e] = sum + off;
+    store_score(a, t, e, sum + off);
   }
 }
 
 // Blocks [0, E): router logits of expert blockIdx.x for all T <= kSmallT
-// tokens; blocks [E, E + shared_blocks): shared-expert w13 + SwiGLU.
+// tokens; blocks [E, E + shared_blocks): shared-expert w13 + SwiGLU in slim
+// blocks (8 gate + 8 up rows), so that with E = 256 every CU gets about the
+// same bytes. NS super-steps per wave; EXACT when K = 128 * NS * kWaves.
+template <int NS, bool EXACT>
 __global__ __launch_bounds__(kThreads) void k_router_small(RouterArgs a, SkinnyArgs sh, int has_shared) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int b = blockIdx.x;
   if (b < a.E) {
     router_logits_block(a, b, lds);
   } else if (has_shared) {
-    skinny_block<kFmtI8, kW13, kWaves, 4>(sh, b - a.E, lds);
+    skinny_block<kFmtI8, kW13, kWaves, NS, EXACT, true>(sh, b - a.E, lds);
   }
 }
 
@@ -103,38 +158,54 @@ __device__ void block_write_tiles(int c, int off, int E, const Perm& p, int* sca
   if (tid == 0) *p.n_tiles = total;
 }
 
-// One block: top-k of every token (one wave per token), then the stable
-// counting sort of the T*k slots and the expert tile table.
-__global__ __launch_bounds__(kThreads) void k_topk_permute_small(RouterArgs a, Perm p) {
+// One block of 1024 threads: top-k of every token (16 waves, one token at a
+// time each), then the stable counting sort of the T*k <= 512 slots and the
+// expert tile table. Stable ranks come from per-expert slot bitmasks: the
+// rank of slot i among the slots of its expert is the number of set bits
+// below bit i of that expert's mask.
+constexpr int kTopkThreads = 1024;
+constexpr int kMaskWords = kSmallT * kMaxTopK / 64;  // 64-bit words per expert mask
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_permute_small(RouterArgs a, Perm p) {
   __shared__ int32_t ids_lds[kSmallT * kMaxTopK];
-  __shared__ int cnt[kThreads];
-  __shared__ int scan_tmp[kThreads];
+  __shared__ unsigned long long mask[kMaxExperts][kMaskWords];
+  __shared__ int first[kMaxExperts];
+  __shared__ int scan_tmp[kTopkThreads];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int t = wave; t < a.T; t += kWaves)
-    wave_topk(a.logits + (size_t)t * a.E, a.bias, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
+  for (int t = wave; t < a.T; t += kTopkThreads / 64)
+    wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
               a.w + (size_t)t * a.k, ids_lds + t * a.k);
-  cnt[tid] = 0;
+  unsigned long long* mflat = &mask[0][0];
+  for (int i = tid; i < kMaxExperts * kMaskWords; i += kTopkThreads) mflat[i] = 0ull;
   __syncthreads();
   const int n = a.T * a.k;
-  for (int i = tid; i < n; i += kThreads) atomicAdd(&cnt[ids_lds[i]], 1);
+  const int words = (n + 63) >> 6;
+  int e_i = 0;
+  if (tid < n) {
+    e_i = ids_lds[tid];
+    atomicOr(&mask[e_i][tid >> 6], 1ull << (tid & 63));
+  }
   __syncthreads();
-  const int c = tid < a.E ? cnt[tid] : 0;
+  int c = 0;
+  if (tid < a.E)
+    for (int w = 0; w < words; ++w) c += __popcll(mask[tid][w]);
   int total;
   const int off = block_exclusive_scan(c, scan_tmp, &total);
-  if (tid < a.E) p.offsets[tid] = off;
+  if (tid < a.E) {
+    p.offsets[tid] = off;
+    first[tid] = off;
+  }
   if (tid == 0) p.offsets[a.E] = total;
   block_write_tiles(c, off, a.E, p, scan_tmp);
   __syncthreads();
-  if (tid < a.E) cnt[tid] = off;  // first position of each expert
-  __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
-    const int e = ids_lds[i];
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += (ids_lds[j] == e);
-    const int pos = cnt[e] + rank;
-    p.sorted_slots[pos] = i;
-    p.slot_pos[i] = pos;
-    p.sorted_tok[pos] = i / a.k;
+  if (tid < n) {
+    const int wi = tid >> 6;
+    int rank = __popcll(mask[e_i][wi] & ((1ull << (tid & 63)) - 1ull));
+    for (int w = 0; w < wi; ++w) rank += __popcll(mask[e_i][w]);
+    const int pos = first[e_i] + rank;
+    p.sorted_slots[pos] = tid;
+    p.slot_pos[tid] = pos;
+    p.sorted_tok[pos] = tid / a.k;
   }
 }
 
@@ -202,16 +273,16 @@ __global__ __launch_bounds__(256) void k_router_tiled(RouterArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < a.E) a.logits[(size_t)t * a.E + e] = acc[i][j] + (a.logit_offset ? a.logit_offset[e] : 0.0f);
+      if (e < a.E) store_score(a, t, e, acc[i][j] + (a.logit_offset ? a.logit_offset[e] : 0.0f));
     }
   }
 }
 
-// One wave per token: top-k of the logits written by k_router_tiled.
+// One wave per token: top-k of the scores written by k_router_tiled.
 __global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  wave_topk(a.logits + (size_t)t * a.E, a.bias, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
+  wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
             a.w + (size_t)t * a.k, nullptr);
 }
 
@@ -278,15 +349,20 @@ hipError_t launch_router_small(const RouterArgs& r, const SkinnyArgs* sh, int sh
   } else {
     shared_blocks = 0;
   }
-  hipError_t e = allow_lds(k_router_small, lds);
+  auto kern = s.K == 1024   ? &k_router_small<1, true>
+              : s.K == 2048 ? &k_router_small<2, true>
+              : s.K == 4096 ? &k_router_small<4, true>
+                            : &k_router_small<4, false>;
+  hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
-  k_router_small<<<r.E + shared_blocks, kThreads, lds, st>>>(r, s, sh ? 1 : 0);
+  kern<<<r.E + shared_blocks, kThreads, lds, st>>>(r, s, sh ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStream_t st) {
   if (r.T <= 0) return hipSuccess;
-  k_topk_permute_small<<<1, kThreads, 0, st>>>(r, p);
+  if (r.T > kSmallT || r.k > kMaxTopK || r.E > kMaxExperts) return hipErrorInvalidValue;
+  k_topk_permute_small<<<1, kTopkThreads, 0, st>>>(r, p);
   return hipGetLastError();
 }
 

@@ -100,11 +100,18 @@ __device__ __forceinline__ const uint4* act_ptr(const SkinnyArgs& p, int pos0, i
   return reinterpret_cast<const uint4*>(p.act + row * p.act_ld) + o;
 }
 
-template <int FMT, int STAGE, int WAVES, int NPF>
+// EXACT: K = 128 * NPF * WAVES, so every wave takes exactly NPF super-steps,
+// all requested at once, and the code has no per-step guards (the compiler's
+// load waits then count exactly and the MFMAs consume each super-step as it
+// arrives). SLIM (int8 w13 only): the block's 16 MFMA rows are 8 gate rows
+// (r < 8) and the matching 8 up rows (r >= 8), so the block reads half as
+// many bytes and twice as many blocks spread a pass over the chip.
+template <int FMT, int STAGE, int WAVES, int NPF, bool EXACT = false, bool SLIM = false>
 __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsigned char* lds) {
+  static_assert(!SLIM || (FMT == kFmtI8 && STAGE == kW13), "slim blocks are int8 w13 only");
   constexpr int THREADS = WAVES * 64;
   constexpr int QV = (FMT == kFmtMx) ? 1 : 2;
-  constexpr int NACC = (STAGE == kW13) ? 2 : 1;
+  constexpr int NACC = (STAGE == kW13 && !SLIM) ? 2 : 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int tg = bid % p.n_tiles_grid;  // tiles fastest: the blocks of one row block
@@ -140,9 +147,9 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
   const int nact = ncols * n16;
   const bool act_in_regs = nact <= 2 * THREADS;
   uint4 act0 = make_uint4(0, 0, 0, 0), act1 = make_uint4(0, 0, 0, 0);
-  if (act_in_regs) {
-    if (tid < nact) act0 = *act_ptr(p, pos0, tid, n16, act_div);
-    if (tid + THREADS < nact) act1 = *act_ptr(p, pos0, tid + THREADS, n16, act_div);
+  if (act_in_regs) {  // indices clamped so that the loads are unconditional; surplus values are unused
+    act0 = *act_ptr(p, pos0, min(tid, nact - 1), n16, act_div);
+    act1 = *act_ptr(p, pos0, min(tid + THREADS, nact - 1), n16, act_div);
   }
 
   // 3. slot tiles: the expert is the top-k choice tg % k of token tg / k
@@ -150,7 +157,8 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
     int32_t* sel = reinterpret_cast<int32_t*>(lds_red + (size_t)WAVES * NACC * 64 * 16);
     float* selw = reinterpret_cast<float*>(sel + kTopKMax);
     const int t = tg / p.topk, j = tg - t * p.topk;
-    if (wave == 0) wave_topk(p.logits + (size_t)t * p.E, p.bias, p.E, p.topk, p.scale, sel, selw, nullptr);
+    if (wave == 0)
+      wave_topk(p.scores + (size_t)t * p.E, p.keys + (size_t)t * p.E, p.E, p.topk, p.scale, sel, selw, nullptr);
     __syncthreads();
     e = sel[j];
     if (rb == 0 && tid == 0) {
@@ -159,9 +167,10 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
     }
   }
 
-  // 4. the block's weights: every wave requests its NPF super-steps, then the
-  //    block's E8M0 scales (two contiguous 16-row runs) in 16-byte pieces
-  const int rowA = rb * 16 + r;
+  // 4. the block's E8M0 scales (two contiguous 16-row runs, 16-byte pieces),
+  //    then its weights: every wave requests its NPF super-steps. The scales
+  //    go first so that waiting for them does not wait for the weights.
+  const int rowA = SLIM ? (r < 8 ? rb * 8 + r : p.half + rb * 8 + (r - 8)) : rb * 16 + r;
   const int rowB = p.half + rb * 16 + r;
   const uint8_t *qA, *qB = nullptr;
   const uint8_t* se = nullptr;
@@ -172,18 +181,36 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
     if (STAGE == kW13) qB = qe + (size_t)rowB * (K / 2) + g * 16;
   } else {
     qA = p.wq + (size_t)rowA * K + g * 32;
-    if (STAGE == kW13) qB = p.wq + (size_t)rowB * K + g * 32;
+    if (STAGE == kW13 && !SLIM) qB = p.wq + (size_t)rowB * K + g * 32;
   }
-  uint4 qa[NPF * QV], qb[NPF * QV];
-  int s0 = wave;
-  prefetch_rows<FMT, QV, NPF, WAVES>(qA, s0, S, qa);
-  if (STAGE == kW13) prefetch_rows<FMT, QV, NPF, WAVES>(qB, s0, S, qb);
   const int nsc16 = NACC * K / 32;  // 16-byte pieces of the block's scales (16 rows x K/32 per run)
   const int pieces_per_run = K / 32;
   uint4 sc0 = make_uint4(0, 0, 0, 0), sc1 = make_uint4(0, 0, 0, 0);
   if (FMT == kFmtMx) {
-    if (tid < nsc16) sc0 = *scale_ptr(se, tid, pieces_per_run, rb, p.half);
-    if (tid + THREADS < nsc16) sc1 = *scale_ptr(se, tid + THREADS, pieces_per_run, rb, p.half);
+    sc0 = *scale_ptr(se, min(tid, nsc16 - 1), pieces_per_run, rb, p.half);
+    sc1 = *scale_ptr(se, min(tid + THREADS, nsc16 - 1), pieces_per_run, rb, p.half);
+  }
+  uint4 qa[NPF * QV], qb[NPF * QV];
+  int s0 = wave;
+  if (EXACT) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int s = s0 + WAVES * i;
+      if (FMT == kFmtMx) {
+        qa[i] = *reinterpret_cast<const uint4*>(qA + (size_t)s * 64);
+        if (STAGE == kW13) qb[i] = *reinterpret_cast<const uint4*>(qB + (size_t)s * 64);
+      } else {
+        qa[2 * i] = *reinterpret_cast<const uint4*>(qA + (size_t)s * 128);
+        qa[2 * i + 1] = *reinterpret_cast<const uint4*>(qA + (size_t)s * 128 + 16);
+        if (STAGE == kW13 && !SLIM) {
+          qb[2 * i] = *reinterpret_cast<const uint4*>(qB + (size_t)s * 128);
+          qb[2 * i + 1] = *reinterpret_cast<const uint4*>(qB + (size_t)s * 128 + 16);
+        }
+      }
+    }
+  } else {
+    prefetch_rows<FMT, QV, NPF, WAVES>(qA, s0, S, qa);
+    if (STAGE == kW13 && !SLIM) prefetch_rows<FMT, QV, NPF, WAVES>(qB, s0, S, qb);
   }
 
   // 5. activations and scales -> LDS
@@ -215,7 +242,7 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
       const int s = s0 + WAVES * i;
-      if (s < S) {
+      if (EXACT || s < S) {
         bf16x8_t bj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -223,24 +250,46 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
         const float sA = FMT == kFmtMx ? e8m0_scale_operand(scA[s * 4]) : 1.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) accA = mfma_16x16x32(weight_frag<FMT>(&qa[i * QV], sA, j), bj[j], accA);
-        if (STAGE == kW13) {
+        if (STAGE == kW13 && !SLIM) {
           const float sB = FMT == kFmtMx ? e8m0_scale_operand(scB[s * 4]) : 1.0f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) accB = mfma_16x16x32(weight_frag<FMT>(&qb[i * QV], sB, j), bj[j], accB);
         }
       }
     }
+    if (EXACT) break;
     s0 += WAVES * NPF;
     if (s0 < S) {
       prefetch_rows<FMT, QV, NPF, WAVES>(qA, s0, S, qa);
-      if (STAGE == kW13) prefetch_rows<FMT, QV, NPF, WAVES>(qB, s0, S, qb);
+      if (STAGE == kW13 && !SLIM) prefetch_rows<FMT, QV, NPF, WAVES>(qB, s0, S, qb);
     }
   }
 
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_red);
   red[(wave * NACC) * 64 + lane] = accA;
-  if (STAGE == kW13) red[(wave * NACC + 1) * 64 + lane] = accB;
+  if (STAGE == kW13 && !SLIM) red[(wave * NACC + 1) * 64 + lane] = accB;
   __syncthreads();
+  if (SLIM) {
+    // lanes (r, g < 2) hold gate rows rb*8 + 4g + i of column r; the up rows
+    // of the same outputs sit at lane + 32
+    if (wave != 0 || r >= ncols || g >= 2) return;
+    f32x4_t G = red[lane], U = red[lane + 32];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      G += red[w * 64 + lane];
+      U += red[w * 64 + lane + 32];
+    }
+    const int hc = rb * 8 + 4 * g;
+    uint16_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      h[i] = f32_to_bf16(swiglu_clamped(G[i] * p.row_scale[hc + i], U[i] * p.row_scale[p.half + hc + i], p.limit));
+    uint2 packed;
+    packed.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    packed.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    *reinterpret_cast<uint2*>(p.hout + (size_t)(pos0 + r) * p.hout_ld + hc) = packed;
+    return;
+  }
   if (wave != 0 || r >= ncols) return;
 
   auto wsum = [&](int q) {
