@@ -491,6 +491,18 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm(g2, p.max_tiles, st); }));
     if (rc) return rc;
+  } else if (T <= kSmallT) {
+    SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+    SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
+    r13.n_rowblocks = cfg->moe_intermediate / 64;
+    r2.n_rowblocks = cfg->hidden_size / 128;
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+      return launch_stream(kW13, r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, st);
+    }));
+    if (rc) return rc;
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st,
+                      [&] { return launch_stream(kW2, r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
+    if (rc) return rc;
   } else {
     const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
     const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
@@ -574,16 +586,28 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     return status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2_combine_small(c2, st); }));
   }
   if (decode) {
-    // router logits + shared w13 | top-k + permutation | routed w13 + shared w2 | routed w2 | combine
+    // router | top-k + permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine,
+    // the expert passes as streaming blocks
     RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
-    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, &s13, sh13_blocks, st); }));
+    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, nullptr, 0, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] { return launch_topk_permute_small(a, p, st); }));
     if (rc) return rc;
-    rc = status(timed(MOE_KERNEL_ROUTED_W13, st,
-                      [&] { return launch_w13(r13, r13_blocks, &s2, sh2_blocks, true, st); }));
+    const int H = cfg->hidden_size, I = cfg->moe_intermediate;
+    SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;
+    g13.n_rowblocks = h13.n_rowblocks = I / 64;
+    g2.n_rowblocks = h2.n_rowblocks = H / 128;
+    h13.tile_n = fit_tile(T < 4 ? T : 4, H);
+    h13.n_tiles_grid = (T + h13.tile_n - 1) / h13.tile_n;
+    h2.tile_n = fit_tile(T < 4 ? T : 4, I);
+    h2.n_tiles_grid = (T + h2.tile_n - 1) / h2.tile_n;
+    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+      return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks, st);
+    }));
     if (rc) return rc;
-    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2(r2, r2_blocks, nullptr, 0, st); }));
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] {
+      return launch_stream(kW2, g2, p.max_tiles * g2.n_rowblocks, &h2, h2.n_tiles_grid * h2.n_rowblocks, st);
+    }));
     if (rc) return rc;
   } else {
     // route | permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine

@@ -123,17 +123,34 @@ __device__ __forceinline__ uint64_t wave_keymax(uint64_t key) {
 // l+192; each of the k rounds is one branch-free DPP wave max of 64-bit keys.
 // Lane 0 writes ids/weights for slots j = 0..k-1 and, if ids_lds is given,
 // the ids there too.
-__device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row, int E, int k, float scale,
-                                          int32_t* ids_out, float* w_out, int32_t* ids_lds) {
+struct TopkRow {
+  float s[4];
+  float b[4];
+};
+
+// The lane's four (score, selection value) pairs of one token.
+__device__ __forceinline__ TopkRow topk_load(const float* s_row, const float* b_row, int E) {
+  const int lane = threadIdx.x & 63;
+  TopkRow t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = min(lane + 64 * q, E - 1);  // loads stay in bounds; surplus lanes get key 0 below
+    t.s[q] = s_row[e];
+    t.b[q] = b_row[e];
+  }
+  return t;
+}
+
+__device__ __forceinline__ void wave_topk_row(const TopkRow& row, int E, int k, float scale, int32_t* ids_out,
+                                              float* w_out, int32_t* ids_lds) {
   const int lane = threadIdx.x & 63;
   float s[4];
   uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    const int ec = e < E ? e : E - 1;  // loads stay in bounds; surplus lanes get key 0
-    s[q] = s_row[ec];
-    key[q] = e < E ? topk_key(b_row[ec], e) : 0;
+    s[q] = row.s[q];
+    key[q] = e < E ? topk_key(row.b[q], e) : 0;
   }
   float sel_s[kTopKMax];
   int sel_id[kTopKMax];
@@ -167,6 +184,11 @@ __device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row
       if (ids_lds) ids_lds[j] = sel_id[j];
     }
   }
+}
+
+__device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row, int E, int k, float scale,
+                                          int32_t* ids_out, float* w_out, int32_t* ids_lds) {
+  wave_topk_row(topk_load(s_row, b_row, E), E, k, scale, ids_out, w_out, ids_lds);
 }
 
 // Exclusive scan over the block of one int per thread (tmp: blockDim.x ints

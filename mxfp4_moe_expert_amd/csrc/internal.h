@@ -28,6 +28,9 @@ struct Perm {
   int max_tiles;
 };
 
+enum { kFmtMx = 0, kFmtI8 = 1 };  // routed MXFP4 / shared int8 weights
+enum { kW13 = 0, kW2 = 1 };        // expert stage
+
 struct RouterArgs {
   int T, H, E, k;
   float scale;
@@ -168,6 +171,11 @@ hipError_t launch_shared_w13(const SkinnyArgs& a, int blocks, hipStream_t st);
 hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st);
+// Streaming expert pass (batched decode): routed MXFP4 pass a and int8 shared
+// pass b of stage `mode` (kW13 / kW2) in one grid; n_rowblocks of each holds
+// its row groups (w13: I/64, w2: H/128).
+hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks,
+                         hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -172,9 +172,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_permute_small(RouterArgs 
   __shared__ int first[kMaxExperts];
   __shared__ int scan_tmp[kTopkThreads];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int t = wave; t < a.T; t += kTopkThreads / 64)
-    wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
-              a.w + (size_t)t * a.k, ids_lds + t * a.k);
+  {  // each wave's (at most 4) tokens: every score load first, then the selections
+    constexpr int kW = kTopkThreads / 64;
+    TopkRow rows[kSmallT / kW];
+#pragma unroll
+    for (int i = 0; i < kSmallT / kW; ++i) {
+      const int t = min(wave + kW * i, a.T - 1);
+      rows[i] = topk_load(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E);
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallT / kW; ++i) {
+      const int t = wave + kW * i;
+      if (t < a.T)
+        wave_topk_row(rows[i], a.E, a.k, a.scale, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, ids_lds + t * a.k);
+    }
+  }
   unsigned long long* mflat = &mask[0][0];
   for (int i = tid; i < kMaxExperts * kMaskWords; i += kTopkThreads) mflat[i] = 0ull;
   __syncthreads();

@@ -27,8 +27,6 @@
 
 namespace moe {
 
-enum { kFmtMx = 0, kFmtI8 = 1 };
-enum { kW13 = 0, kW2 = 1 };
 
 // LDS layout of a skinny block: [activation tile: tile_n rows of 2K+16 bytes]
 // [E8M0 scales of the block's rows: NACC x 16 rows of K/32+4 bytes]
@@ -220,9 +218,17 @@ __device__ __forceinline__ void skinny_block(const SkinnyArgs& p, int bid, unsig
       const int ii = tid + THREADS;
       *reinterpret_cast<uint4*>(lds + (ii / n16) * row_bytes + (ii % n16) * 16) = act1;
     }
-  } else {
-    for (int i = tid; i < nact; i += THREADS)
-      *reinterpret_cast<uint4*>(lds + (i / n16) * row_bytes + (i % n16) * 16) = *act_ptr(p, pos0, i, n16, act_div);
+  } else {  // batches of 8 pieces per thread in flight (clamped loads, guarded stores)
+    for (int base = 0; base < nact; base += 8 * THREADS) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *act_ptr(p, pos0, min(base + tid + j * THREADS, nact - 1), n16, act_div);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = base + tid + j * THREADS;
+        if (i < nact) *reinterpret_cast<uint4*>(lds + (i / n16) * row_bytes + (i % n16) * 16) = v[j];
+      }
+    }
   }
   if (FMT == kFmtMx) {
     if (tid < nsc16) store_scales16(lds_sc, srow, pieces_per_run, tid, sc0);
