@@ -6,11 +6,13 @@
 // the k weighted routed outputs of the token in slot order (row "Shared
 // expert": routed + shared).
 //
-// Block: 8 waves, output tile of 256 weight rows x 128 token positions, K in
-// stages of 128. Wave (wm, wn) = (wave & 1, wave >> 1) owns 64 weight rows (4
-// blocks of 16) x 64 tokens (4 blocks of 16): 16 MFMA 16x16x32 accumulators.
-// For w13 the wave's 4 row blocks are 2 gate blocks and the 2 matching up
-// blocks, so the SwiGLU is computed in registers.
+// Block: 8 waves, output tile of 256 weight rows x 128 token positions.
+// Wave w owns 32 weight rows (2 blocks of 16) x all 128 positions (8 blocks
+// of 16): 16 MFMA 16x16x32 accumulators, so each weight fragment converted
+// to bf16 feeds 8 MFMAs (on gfx950 VALU work and MFMAs share a SIMD's issue
+// time, so converts per MFMA matter). For w13 the wave's 2 row blocks are 16
+// gate rows and the matching 16 up rows, so the SwiGLU is computed in
+// registers.
 //   - K runs in stages of 128 (MXFP4) or 64 (int8): each lane reads, per
 //     stage and row block, 16 bytes of its row (the quarter g of the stage's
 //     K-values) straight into registers, two stages ahead. For MXFP4 these 32
@@ -34,6 +36,9 @@ namespace moe {
 
 constexpr int kBM = 128;  // token positions per tile
 constexpr int kBN = 256;  // weight rows per tile (w13: 128 gate + 128 up)
+constexpr int kGemmThreads = 512;  // 8 waves
+constexpr int kMB = kBM / 16;       // token blocks per wave (the whole tile)
+constexpr int kRB = 2;              // 16-row weight blocks per wave
 
 // Per format: K per stage (each lane's 16 weight bytes per row block are 32
 // E2M1 values or 16 int8 values, a quarter of the stage), MFMA k-steps per
@@ -63,14 +68,16 @@ __device__ __forceinline__ bf16x8_t gemm_conv(const u32x4_t& q, int kk, uint32_t
 // byte 4 st + g of the row: those 32 values are exactly one group) of the 4
 // row blocks for stage st.
 template <int FMT>
-__device__ __forceinline__ void gemm_load_w(const uint8_t* const (&qrow)[4], const uint8_t* const (&srow)[4], int st,
-                                            u32x4_t (&w)[4], uint32_t (&sc)[4]) {
+__device__ __forceinline__ void gemm_load_w(const uint8_t* qe, const uint8_t* se, const uint32_t (&qoff)[kRB],
+                                            const uint32_t (&soff)[kRB], int st, u32x4_t (&w)[kRB],
+                                            uint32_t (&sc)[kRB]) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    w[b] = *reinterpret_cast<const u32x4_t*>(qrow[b] + (size_t)st * 64);
-    if (FMT == kFmtMx) sc[b] = srow[b][4 * st];
+  for (int b = 0; b < kRB; ++b) {
+    w[b] = *reinterpret_cast<const u32x4_t*>(qe + (qoff[b] + (uint32_t)st * 64));
+    if (FMT == kFmtMx) sc[b] = se[soff[b] + (uint32_t)st * 4];
   }
 }
+
 
 // The thread's quarter of one gathered token row for stage st.
 template <int FMT>
@@ -92,31 +99,33 @@ struct GemmA {
   }
 };
 
+// For each MFMA k-step: the wave's weight fragments converted once, then
+// each activation fragment read from LDS and used for kRB MFMAs.
 template <int FMT>
-__device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[4][4], const u32x4_t (&w)[4], const uint32_t (&sc)[4],
-                                             const unsigned char* abase) {
+__device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][kMB], const u32x4_t (&w)[kRB],
+                                             const uint32_t (&sc)[kRB], const unsigned char* abase) {
   constexpr int kArow = GemmCfg<FMT>::kArow;
 #pragma unroll
   for (int kk = 0; kk < GemmCfg<FMT>::kKK; ++kk) {
-    bf16x8_t bt[4];
+    bf16x8_t wa[kRB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) bt[m] = *reinterpret_cast<const bf16x8_t*>(abase + m * 16 * kArow + kk * 16);
+    for (int b = 0; b < kRB; ++b) wa[b] = gemm_conv<FMT>(w[b], kk, sc[b]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bf16x8_t wa = gemm_conv<FMT>(w[b], kk, sc[b]);
+    for (int m = 0; m < kMB; ++m) {
+      const bf16x8_t bt = *reinterpret_cast<const bf16x8_t*>(abase + m * 16 * kArow + kk * 16);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[b][m] = mfma_16x16x32(wa, bt[m], acc[b][m]);
+      for (int b = 0; b < kRB; ++b) acc[b][m] = mfma_16x16x32(wa[b], bt, acc[b][m]);
     }
   }
 }
 
 template <int FMT, int MODE>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr int kBK = GemmCfg<FMT>::kBK, kArow = GemmCfg<FMT>::kArow;
   __shared__ __align__(16) unsigned char lds_a[2][kBM * kArow];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wn = wave;  // the wave's 32 weight rows; every wave covers all 128 positions
 
   // XCD-aware order over the blocks in use: logical tile = (xcd, run
   // position); N tiles fastest
@@ -142,20 +151,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
 
   const int K = p.K;
   const int nst = K / kBK;
-  // weight rows of the wave's 4 row blocks (w13: gate, gate, up, up)
-  const uint8_t* qrow[4];
-  const uint8_t* srow[4];
-  {
-    const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
-    const uint8_t* se = FMT == kFmtMx ? p.wsc + (long long)e * p.s_expert_stride : p.wq;
+  // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
+  // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
+  const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
+  const uint8_t* se = FMT == kFmtMx ? p.wsc + (long long)e * p.s_expert_stride : p.wq;
+  uint32_t qoff[kRB], soff[kRB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int wrow;
-      if (MODE == kGemmW13) wrow = (b < 2 ? 0 : p.half) + nt * (kBN / 2) + wn * 32 + (b & 1) * 16 + r;
-      else wrow = nt * kBN + wn * 64 + b * 16 + r;
-      qrow[b] = qe + (size_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
-      srow[b] = se + (size_t)wrow * (K / 32) + g;
-    }
+  for (int b = 0; b < kRB; ++b) {
+    int wrow;
+    if (MODE == kGemmW13) wrow = (b == 0 ? 0 : p.half) + nt * (kBN / 2) + wn * 16 + r;
+    else wrow = nt * kBN + wn * 32 + b * 16 + r;
+    qoff[b] = (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
+    soff[b] = (uint32_t)wrow * (K / 32) + g;
   }
   // this thread's activation loads: token row tid/4, quarter tid%4 of the
   // row's stage. Rows past the tile re-read its first row: their results are
@@ -166,39 +173,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
   const uint16_t* asrc = p.act + atrow * p.act_ld + apart * (kBK / 4);
   u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][arow * kArow + apart * (kBK / 2)]);
   u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][arow * kArow + apart * (kBK / 2)]);
-  const unsigned char* abase0 = &lds_a[0][(wm * 64 + r) * kArow + g * (kBK / 2)];
-  const unsigned char* abase1 = &lds_a[1][(wm * 64 + r) * kArow + g * (kBK / 2)];
+  const unsigned char* abase0 = &lds_a[0][r * kArow + g * (kBK / 2)];
+  const unsigned char* abase1 = &lds_a[1][r * kArow + g * (kBK / 2)];
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[kRB][kMB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < kMB; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   // Software pipeline, branch-free so that every wait counts exactly: stage
   // st computes from LDS buffer st%2 and weight registers st%2 while the
   // activations of st+1 wait in registers and the weights of st+2 are in
   // flight. Loads past the last stage re-read it (clamped, never used).
-  u32x4_t w0[4], w1[4];
-  uint32_t s0[4] = {0, 0, 0, 0}, s1[4] = {0, 0, 0, 0};
+  u32x4_t w0[kRB], w1[kRB];
+  uint32_t s0[kRB] = {}, s1[kRB] = {};
   GemmA<FMT> av;
   const int last = nst - 1;
-  gemm_load_w<FMT>(qrow, srow, 0, w0, s0);
+  gemm_load_w<FMT>(qe, se, qoff, soff, 0, w0, s0);
   av.load(asrc, 0);
   av.store(adst0);
   av.load(asrc, min(1, last));
-  gemm_load_w<FMT>(qrow, srow, min(1, last), w1, s1);
+  gemm_load_w<FMT>(qe, se, qoff, soff, min(1, last), w1, s1);
   for (int st = 0; st + 1 < nst; st += 2) {
     __syncthreads();
     av.store(adst1);  // stage st+1
     av.load(asrc, min(st + 2, last));
     gemm_compute<FMT>(acc, w0, s0, abase0);
-    gemm_load_w<FMT>(qrow, srow, min(st + 2, last), w0, s0);
+    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 2, last), w0, s0);
     __syncthreads();
     av.store(adst0);  // stage st+2
     av.load(asrc, min(st + 3, last));
     gemm_compute<FMT>(acc, w1, s1, abase1);
-    gemm_load_w<FMT>(qrow, srow, min(st + 3, last), w1, s1);
+    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 3, last), w1, s1);
   }
   if (nst & 1) {  // the last stage (buffer 0, w0)
     __syncthreads();
@@ -207,42 +214,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs p) {
 
   // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int tok = wm * 64 + m * 16 + r;  // position within the tile
+  for (int m = 0; m < kMB; ++m) {
+    const int tok = m * 16 + r;  // position within the tile
     if (tok >= ncols) continue;
     const int pos = pos0 + tok;
-    if (MODE == kGemmW13) {
+    if (MODE == kGemmW13) {  // block 0: gate rows, block 1: the matching up rows
+      const int hc = nt * (kBN / 2) + wn * 16 + 4 * g;
+      uint16_t h[4];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int hc = nt * (kBN / 2) + wn * 32 + b * 16 + 4 * g;
-        uint16_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float gv = acc[b][m][i], uv = acc[b + 2][m][i];
-          if (FMT == kFmtI8) {
-            gv *= p.row_scale[hc + i];
-            uv *= p.row_scale[p.half + hc + i];
-          }
-          h[i] = f32_to_bf16(swiglu_clamped(gv, uv, p.limit));
+      for (int i = 0; i < 4; ++i) {
+        float gv = acc[0][m][i], uv = acc[1][m][i];
+        if (FMT == kFmtI8) {
+          gv *= p.row_scale[hc + i];
+          uv *= p.row_scale[p.half + hc + i];
         }
-        uint2 pk;
-        pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
+        h[i] = f32_to_bf16(swiglu_clamped(gv, uv, p.limit));
       }
+      uint2 pk;
+      pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
     } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot]
       const int slot = p.sorted_slots[pos];
       const float wv = p.slot_w[slot];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = nt * kBN + wn * 64 + b * 16 + 4 * g;
+      for (int b = 0; b < kRB; ++b) {
+        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
         *reinterpret_cast<float4*>(p.yout + (size_t)slot * p.yout_ld + n) =
             make_float4(acc[b][m][0] * wv, acc[b][m][1] * wv, acc[b][m][2] * wv, acc[b][m][3] * wv);
       }
     } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = nt * kBN + wn * 64 + b * 16 + 4 * g;
+      for (int b = 0; b < kRB; ++b) {
+        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int j = 0; j < p.topk; ++j) {
           const float4 y = *reinterpret_cast<const float4*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
@@ -273,7 +277,7 @@ static hipError_t launch_gemm_t(const GemmArgs& p, int tiles, hipStream_t st) {
   const long long nblk = (long long)tiles * p.n_ntiles;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_gemm<FMT, MODE><<<(unsigned)nblk, kThreads, 0, st>>>(p);
+  k_gemm<FMT, MODE><<<(unsigned)nblk, kGemmThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
