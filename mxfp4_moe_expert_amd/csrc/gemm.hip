@@ -101,8 +101,8 @@ struct GemmA {
 
 // For each MFMA k-step: the wave's weight fragments converted once, then
 // each activation fragment read from LDS and used for kRB MFMAs.
-template <int FMT>
-__device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][kMB], const u32x4_t (&w)[kRB],
+template <int FMT, int MB>
+__device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x4_t (&w)[kRB],
                                              const uint32_t (&sc)[kRB], const unsigned char* abase) {
   constexpr int kArow = GemmCfg<FMT>::kArow;
 #pragma unroll
@@ -111,10 +111,113 @@ __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][kMB], const u32
 #pragma unroll
     for (int b = 0; b < kRB; ++b) wa[b] = gemm_conv<FMT>(w[b], kk, sc[b]);
 #pragma unroll
-    for (int m = 0; m < kMB; ++m) {
+    for (int m = 0; m < MB; ++m) {
       const bf16x8_t bt = *reinterpret_cast<const bf16x8_t*>(abase + m * 16 * kArow + kk * 16);
 #pragma unroll
       for (int b = 0; b < kRB; ++b) acc[b][m] = mfma_16x16x32(wa[b], bt, acc[b][m]);
+    }
+  }
+}
+
+// The K loop and epilogue of one block over its first MB*16 positions.
+template <int FMT, int MODE, int MB>
+__device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, const uint8_t* se,
+                                          const uint32_t (&qoff)[kRB], const uint32_t (&soff)[kRB],
+                                          const uint16_t* asrc, u32x4_t* adst0, u32x4_t* adst1,
+                                          const unsigned char* abase0, const unsigned char* abase1, int nst,
+                                          int ncols, int pos0, int nt, int wn, int g, int r) {
+  f32x4_t acc[kRB][MB];
+#pragma unroll
+  for (int b = 0; b < kRB; ++b)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  // Software pipeline, branch-free so that every wait counts exactly: stage
+  // st computes from LDS buffer st%2 and weight registers st%2 while the
+  // activations of st+1 wait in registers and the weights of st+2 are in
+  // flight. Loads past the last stage re-read it (clamped, never used).
+  u32x4_t w0[kRB], w1[kRB];
+  uint32_t s0[kRB] = {}, s1[kRB] = {};
+  GemmA<FMT> av;
+  const int last = nst - 1;
+  gemm_load_w<FMT>(qe, se, qoff, soff, 0, w0, s0);
+  av.load(asrc, 0);
+  av.store(adst0);
+  av.load(asrc, min(1, last));
+  gemm_load_w<FMT>(qe, se, qoff, soff, min(1, last), w1, s1);
+  for (int st = 0; st + 1 < nst; st += 2) {
+    __syncthreads();
+    av.store(adst1);  // stage st+1
+    av.load(asrc, min(st + 2, last));
+    gemm_compute<FMT, MB>(acc, w0, s0, abase0);
+    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 2, last), w0, s0);
+    __syncthreads();
+    av.store(adst0);  // stage st+2
+    av.load(asrc, min(st + 3, last));
+    gemm_compute<FMT, MB>(acc, w1, s1, abase1);
+    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 3, last), w1, s1);
+  }
+  if (nst & 1) {  // the last stage (buffer 0, w0)
+    __syncthreads();
+    gemm_compute<FMT, MB>(acc, w0, s0, abase0);
+  }
+
+  // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int tok = m * 16 + r;  // position within the tile
+    if (tok >= ncols) continue;
+    const int pos = pos0 + tok;
+    if (MODE == kGemmW13) {  // block 0: gate rows, block 1: the matching up rows
+      const int hc = nt * (kBN / 2) + wn * 16 + 4 * g;
+      uint16_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float gv = acc[0][m][i], uv = acc[1][m][i];
+        if (FMT == kFmtI8) {
+          gv *= p.row_scale[hc + i];
+          uv *= p.row_scale[p.half + hc + i];
+        }
+        h[i] = f32_to_bf16(swiglu_clamped(gv, uv, p.limit));
+      }
+      uint2 pk;
+      pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
+    } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot]
+      const int slot = p.sorted_slots[pos];
+      const float wv = p.slot_w[slot];
+#pragma unroll
+      for (int b = 0; b < kRB; ++b) {
+        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
+        *reinterpret_cast<float4*>(p.yout + (size_t)slot * p.yout_ld + n) =
+            make_float4(acc[b][m][0] * wv, acc[b][m][1] * wv, acc[b][m][2] * wv, acc[b][m][3] * wv);
+      }
+    } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
+#pragma unroll
+      for (int b = 0; b < kRB; ++b) {
+        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < p.topk; ++j) {
+          const float4 y = *reinterpret_cast<const float4*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
+          o.x += y.x;
+          o.y += y.y;
+          o.z += y.z;
+          o.w += y.w;
+        }
+        o.x += p.row_scale[n] * acc[b][m][0];
+        o.y += p.row_scale[n + 1] * acc[b][m][1];
+        o.z += p.row_scale[n + 2] * acc[b][m][2];
+        o.w += p.row_scale[n + 3] * acc[b][m][3];
+        if (p.out_is_fp32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)pos * p.out_ld + n) = o;
+        } else {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16);
+          pk.y = (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (size_t)pos * p.out_ld + n) = pk;
+        }
+      }
     }
   }
 }
@@ -176,100 +279,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const unsigned char* abase0 = &lds_a[0][r * kArow + g * (kBK / 2)];
   const unsigned char* abase1 = &lds_a[1][r * kArow + g * (kBK / 2)];
 
-  f32x4_t acc[kRB][kMB];
-#pragma unroll
-  for (int b = 0; b < kRB; ++b)
-#pragma unroll
-    for (int m = 0; m < kMB; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-  // Software pipeline, branch-free so that every wait counts exactly: stage
-  // st computes from LDS buffer st%2 and weight registers st%2 while the
-  // activations of st+1 wait in registers and the weights of st+2 are in
-  // flight. Loads past the last stage re-read it (clamped, never used).
-  u32x4_t w0[kRB], w1[kRB];
-  uint32_t s0[kRB] = {}, s1[kRB] = {};
-  GemmA<FMT> av;
-  const int last = nst - 1;
-  gemm_load_w<FMT>(qe, se, qoff, soff, 0, w0, s0);
-  av.load(asrc, 0);
-  av.store(adst0);
-  av.load(asrc, min(1, last));
-  gemm_load_w<FMT>(qe, se, qoff, soff, min(1, last), w1, s1);
-  for (int st = 0; st + 1 < nst; st += 2) {
-    __syncthreads();
-    av.store(adst1);  // stage st+1
-    av.load(asrc, min(st + 2, last));
-    gemm_compute<FMT>(acc, w0, s0, abase0);
-    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 2, last), w0, s0);
-    __syncthreads();
-    av.store(adst0);  // stage st+2
-    av.load(asrc, min(st + 3, last));
-    gemm_compute<FMT>(acc, w1, s1, abase1);
-    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 3, last), w1, s1);
-  }
-  if (nst & 1) {  // the last stage (buffer 0, w0)
-    __syncthreads();
-    gemm_compute<FMT>(acc, w0, s0, abase0);
-  }
-
-  // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
-#pragma unroll
-  for (int m = 0; m < kMB; ++m) {
-    const int tok = m * 16 + r;  // position within the tile
-    if (tok >= ncols) continue;
-    const int pos = pos0 + tok;
-    if (MODE == kGemmW13) {  // block 0: gate rows, block 1: the matching up rows
-      const int hc = nt * (kBN / 2) + wn * 16 + 4 * g;
-      uint16_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float gv = acc[0][m][i], uv = acc[1][m][i];
-        if (FMT == kFmtI8) {
-          gv *= p.row_scale[hc + i];
-          uv *= p.row_scale[p.half + hc + i];
-        }
-        h[i] = f32_to_bf16(swiglu_clamped(gv, uv, p.limit));
-      }
-      uint2 pk;
-      pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-      pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-      *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
-    } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot]
-      const int slot = p.sorted_slots[pos];
-      const float wv = p.slot_w[slot];
-#pragma unroll
-      for (int b = 0; b < kRB; ++b) {
-        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
-        *reinterpret_cast<float4*>(p.yout + (size_t)slot * p.yout_ld + n) =
-            make_float4(acc[b][m][0] * wv, acc[b][m][1] * wv, acc[b][m][2] * wv, acc[b][m][3] * wv);
-      }
-    } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
-#pragma unroll
-      for (int b = 0; b < kRB; ++b) {
-        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < p.topk; ++j) {
-          const float4 y = *reinterpret_cast<const float4*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
-          o.x += y.x;
-          o.y += y.y;
-          o.z += y.z;
-          o.w += y.w;
-        }
-        o.x += p.row_scale[n] * acc[b][m][0];
-        o.y += p.row_scale[n + 1] * acc[b][m][1];
-        o.z += p.row_scale[n + 2] * acc[b][m][2];
-        o.w += p.row_scale[n + 3] * acc[b][m][3];
-        if (p.out_is_fp32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)pos * p.out_ld + n) = o;
-        } else {
-          uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16);
-          pk.y = (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (size_t)pos * p.out_ld + n) = pk;
-        }
-      }
-    }
-  }
+  // a tile of at most 64 positions runs half the MFMAs (uniform branch)
+  if (ncols <= kBM / 2)
+    gemm_main<FMT, MODE, kMB / 2>(p, qe, se, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
+                                  wn, g, r);
+  else
+    gemm_main<FMT, MODE, kMB>(p, qe, se, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
+                              g, r);
 }
 
 template <int FMT, int MODE>
