@@ -42,10 +42,10 @@ DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), b
 # The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
 # names it, and what it does there.
 DOMINANT = {
-    "decode_t1": ("moe::k_pair<0, 0, 0, 0, 4, 8, 8>",
+    "decode_t1": ("moe::k_single<0, 0, 4, 8, true>",
                   "routed w13: top-6 in-block + MXFP4 GEMV + clamped SwiGLU, one block per (slot, 16 rows)"),
-    "decode_t64": ("moe::k_pair<0, 0, 1, 1, 8, 4, 4>",
-                   "routed w13 (MXFP4 skinny GEMM + clamped SwiGLU) with the shared expert's int8 w2"),
+    "decode_t64": ("moe::k_stream<0, 8, 4>",
+                   "routed MXFP4 w13 + shared int8 w13 streaming passes with the clamped SwiGLU"),
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
     "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
 }
