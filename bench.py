@@ -40,14 +40,15 @@ DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), b
     "hash_t4096": (20, 3, 1, "routed_w13", "mfma"),
 }
 # The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
-# names it, and what it does there.
+# names it, what it does there, and which algorithmic work it is priced on.
 DOMINANT = {
-    "decode_t1": ("moe::k_single<0, 0, 4, 8, true>",
-                  "routed w13: top-6 in-block + MXFP4 GEMV + clamped SwiGLU, one block per (slot, 16 rows)"),
+    "decode_t1": ("moe::k_layer_small<4, 2, 1, 6>",
+                  "the whole layer in one launch of one block per CU: router, shared int8 w13, top-6, routed "
+                  "MXFP4 w13 + clamped SwiGLU, routed MXFP4 + shared int8 w2 and the weighted combine", "layer"),
     "decode_t64": ("moe::k_stream<0, 8, 4>",
-                   "routed MXFP4 w13 + shared int8 w13 streaming passes with the clamped SwiGLU"),
-    "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
-    "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU"),
+                   "routed MXFP4 w13 + shared int8 w13 streaming passes with the clamped SwiGLU", "w13"),
+    "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
+    "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
 }
 COPY_CAL_BYTES = 1 << 28  # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
@@ -196,7 +197,7 @@ def summarize(workload, outdir, commands):
     when the counter runs exist, profiles/<kernel>_<workload>_traffic.txt
     (HBM bytes per launch of the dominant kernel, calibrated by a plain copy
     of known size, stamped with the hash of the kernel sources)."""
-    kname, what = DOMINANT[workload]
+    kname, what, _ = DOMINANT[workload]
     short = kname.split("::")[1].split("<")[0]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     stats = _csv_rows(_find(outdir, "kernel_trace", "kernel_stats.csv"))
@@ -393,12 +394,13 @@ def main():
     ids_np = ids_all.cpu().numpy()
     alg = algorithmic(wl, ids_np)
     value = T * K / (total_ms / 1e3)
+    scope = DOMINANT[args.workload][2]
     if bound == "hbm":
-        achieved = alg["w13_bytes"] / (kern_avg_ms / 1e3) / 1e9
+        achieved = alg[scope + "_bytes"] / (kern_avg_ms / 1e3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     else:
-        achieved = alg["w13_flops"] / (kern_avg_ms / 1e3) / 1e12
+        achieved = alg[scope + "_flops"] / (kern_avg_ms / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4))
     traffic = traffic_from_profiles(args.workload)

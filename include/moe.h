@@ -45,9 +45,14 @@
  *   - Device-side values are trusted: expert ids must lie in [0, E), token
  *     ids in [0, V); E8M0 scale bytes should not be 0xFF (NaN).
  *   - `workspace` is device scratch of at least moe_workspace_size() bytes,
- *     256-byte aligned. Its contents on entry do not matter: every call
- *     writes each workspace value before reading it. Calls that share one
- *     workspace must be ordered on one stream.
+ *     256-byte aligned. Zero-fill it once before its first use
+ *     (moe_workspace_init, or any zero fill): bytes 256 .. 136447 hold the
+ *     hand-off state of the single-launch layer (MOE_SCHED_SINGLE), which
+ *     every call leaves ready for the next; every other workspace value is
+ *     written before it is read. Calls that share one workspace must be
+ *     ordered on one stream. If a single-launch call's bounded wait for
+ *     another block of its grid expires (about a second), its output is
+ *     NaN; the hand-off state stays consistent.
  *   - Supported shapes: H and I multiples of 128, 1 <= top_k <= 8,
  *     top_k <= E <= 256, 0 <= T <= 65536. Device pointers must be 16-byte
  *     aligned.
@@ -92,8 +97,8 @@ const char* moe_version(void);
 size_t moe_workspace_size(const moe_config* cfg, int32_t T);
 
 /* Zero-fill a workspace on `stream` (with a fill kernel, so it may be
- * captured in a HIP graph). Optional: no entry point needs it; it gives the
- * workspace defined contents, e.g. for inspection. */
+ * captured in a HIP graph). Needed once before a workspace's first use,
+ * unless it was allocated zeroed. */
 int moe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Learned router: scores, bias-assisted top-k, renormalised weights.
@@ -156,12 +161,28 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The launch sequence moe_forward takes. */
+enum {
+  MOE_SCHED_SINGLE = 1,  /* T <= 2, learned router, shapes with a single-launch kernel whose whole
+                          * grid the device holds at once: the layer in one launch */
+  MOE_SCHED_TINY = 2,    /* T * (top_k + 1) <= 16 otherwise: three launches */
+  MOE_SCHED_DECODE = 3,  /* T <= 64: router, top-k + permutation, streaming w13, streaming w2, combine */
+  MOE_SCHED_LARGE = 4    /* larger T or a hash layer: route, permutation, grouped GEMMs, combine */
+};
+
+/* Which of the MOE_SCHED_* sequences moe_forward takes for T tokens on the
+ * current device (hash != 0: a hash layer). Returns a negative MOE_E* code
+ * if cfg or T is invalid or unsupported. May query the device (occupancy),
+ * never launches anything. */
+int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash);
+
 /* Kernels that moe_set_kernel_events can bracket. */
 enum {
   MOE_KERNEL_NONE = 0,
   MOE_KERNEL_ROUTER = 1,       /* router logits (+ top-k, + small-T permutation) */
   MOE_KERNEL_PERMUTE = 2,      /* multi-block permutation (large T only) */
-  MOE_KERNEL_ROUTED_W13 = 3,   /* routed experts: MXFP4 w13 + clamped SwiGLU */
+  MOE_KERNEL_ROUTED_W13 = 3,   /* routed experts: MXFP4 w13 + clamped SwiGLU (MOE_SCHED_SINGLE: the
+                                * whole layer's one launch) */
   MOE_KERNEL_ROUTED_W2 = 4,    /* routed experts: MXFP4 w2 x routing weight */
   MOE_KERNEL_SHARED_W13 = 5,   /* shared expert: int8 w13 + clamped SwiGLU */
   MOE_KERNEL_SHARED_W2 = 6,    /* shared expert: int8 w2 */

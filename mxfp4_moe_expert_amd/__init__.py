@@ -64,6 +64,7 @@ _SIGNATURES = {
     "moe_expert_ffn": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                        ctypes.c_int),
     "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
+    "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                      _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -130,6 +131,19 @@ def set_kernel_events(kernel: str | None, start_event=None, stop_event=None):
     hipEvent_t handles (ints or c_void_p); None stops. Measurement only."""
     kid = 0 if kernel is None else KERNELS[kernel]
     _check(lib().moe_set_kernel_events(kid, start_event, stop_event), "moe_set_kernel_events")
+
+
+SCHEDULES = {1: "single", 2: "tiny", 3: "decode", 4: "large"}
+
+
+def forward_schedule(cfg: MoeConfig, T: int, hash_layer: bool = False) -> str:
+    """Which launch sequence ``forward`` takes for T tokens on the current
+    device: "single" (the whole layer in one launch), "tiny", "decode" or
+    "large"."""
+    rc = lib().moe_forward_schedule(ctypes.byref(cfg), T, 1 if hash_layer else 0)
+    if rc < 0:
+        raise MoEError(rc, "moe_forward_schedule")
+    return SCHEDULES[rc]
 
 
 def workspace_size(cfg: MoeConfig, T: int) -> int:

@@ -18,7 +18,7 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
+  size_t counters, xfer, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
   int tile_n, max_tiles;
 };
@@ -73,6 +73,7 @@ Layout layout(const moe_config& c, int T) {
     return at;
   };
   L.counters = take(256);
+  L.xfer = take(kXferBytes);
   L.scores = take((size_t)2 * T * E * 4);  // scores, then selection values
   L.ids = take(slots * 4);
   L.w = take(slots * 4);
@@ -359,6 +360,16 @@ RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const floa
   return a;
 }
 
+// The launch sequence of moe_forward (MOE_SCHED_*).
+int schedule(const moe_config& c, int T, bool hash) {
+  if (!hash && T * (c.top_k + 1) <= 16)
+    return layer_small_supported(c.hidden_size, c.moe_intermediate, c.n_routed_experts, T, c.top_k)
+               ? MOE_SCHED_SINGLE
+               : MOE_SCHED_TINY;
+  if (!hash && T <= kSmallT) return MOE_SCHED_DECODE;
+  return MOE_SCHED_LARGE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -518,6 +529,13 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 
+int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash) {
+  if (!cfg) return MOE_EINVAL;
+  if (!cfg_ok(cfg) || T > kMaxT) return MOE_EUNSUPPORTED;
+  if (T < 0) return MOE_EINVAL;
+  return schedule(*cfg, T, hash != 0);
+}
+
 int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w, const float* bias,
                 const float* logit_offset, const int32_t* token_ids, const int32_t* tid2eid, int32_t V,
                 const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
@@ -557,9 +575,39 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
   const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
   const int r13_blocks = p.max_tiles * r13.n_rowblocks, r2_blocks = p.max_tiles * r2.n_rowblocks;
-  const bool tiny = !hash && T * (cfg->top_k + 1) <= 16;
-  const bool decode = !hash && T <= kSmallT;
+  const int sched = schedule(*cfg, T, hash);
+  const bool tiny = sched == MOE_SCHED_TINY;
+  const bool decode = sched == MOE_SCHED_DECODE;
 
+  if (sched == MOE_SCHED_SINGLE) {
+    // the whole layer in one launch, one block per CU
+    LayerArgs la;
+    la.T = T;
+    la.H = cfg->hidden_size;
+    la.I = cfg->moe_intermediate;
+    la.E = cfg->n_routed_experts;
+    la.k = cfg->top_k;
+    la.scale = cfg->routed_scaling_factor;
+    la.limit = cfg->swiglu_limit;
+    la.x = x;
+    la.gate_w = gate_w;
+    la.bias = bias;
+    la.logit_offset = logit_offset;
+    la.w13c = w13_codes;
+    la.w13s = w13_scales;
+    la.w2c = w2_codes;
+    la.w2s = w2_scales;
+    la.sh13 = sh_w13;
+    la.sh13s = sh_w13_scale;
+    la.sh2 = sh_w2;
+    la.sh2s = sh_w2_scale;
+    la.out = out;
+    la.out_is_fp32 = out_is_fp32 ? 1 : 0;
+    la.ids_out = ids;
+    la.w_out = w;
+    la.xfer = at<uint32_t>(workspace, L.xfer);
+    return status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_layer_small(la, st); }));
+  }
   if (tiny) {
     // router logits + shared w13 | routed w13 (top-k in each block, one tile
     // per slot) | routed w2 + shared w2 + combine

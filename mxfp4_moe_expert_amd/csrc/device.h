@@ -129,14 +129,38 @@ struct TopkRow {
 };
 
 // The lane's four (score, selection value) pairs of one token.
+// Device-wide coherent (agent-scope) 32-bit load and store: they bypass the
+// per-XCD L2 copies, for data handed between blocks of one launch.
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes as two coherent 64-bit loads.
+__device__ __forceinline__ u32x4_t load_agent_u32x4(const void* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (u32x4_t){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+
+// COH: the scores were written by other blocks of the same launch.
+template <bool COH = false>
 __device__ __forceinline__ TopkRow topk_load(const float* s_row, const float* b_row, int E) {
   const int lane = threadIdx.x & 63;
   TopkRow t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = min(lane + 64 * q, E - 1);  // loads stay in bounds; surplus lanes get key 0 below
-    t.s[q] = s_row[e];
-    t.b[q] = b_row[e];
+    t.s[q] = COH ? load_agent(s_row + e) : s_row[e];
+    t.b[q] = COH ? load_agent(b_row + e) : b_row[e];
   }
   return t;
 }

@@ -177,6 +177,42 @@ hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st);
 hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks,
                          hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
+// Hand-off region of the single-launch layer, at a fixed offset at the start
+// of every workspace (zero on first use): per-block call counters, then two
+// buffers, used by alternate calls, of router scores and h columns.
+constexpr int kXferBlocks = 256;  // blocks tracked: the largest single-launch grid
+constexpr int kXferTokens = 2, kXferCols = 16, kXferMaxI = 2048;
+constexpr size_t kXferScoreWords = (size_t)kXferTokens * kXferBlocks;  // [2 tokens][256 experts]
+constexpr size_t kXferHWords = (size_t)kXferCols * (kXferMaxI / 2);     // [16 columns][1024 bf16 pairs]
+constexpr size_t kXferBytes = ((size_t)kXferBlocks + 2 * (kXferScoreWords + kXferHWords)) * 4;
+
+// The whole layer for T <= 2 tokens (T*(k+1) <= 16) in one launch of one
+// block per CU.
+struct LayerArgs {
+  int T, H, I, E, k;
+  float scale, limit;
+  const uint16_t* x;           // [T][H] bf16
+  const float* gate_w;         // [E][H] fp32 router
+  const float* bias;           // [E]
+  const float* logit_offset;   // [E] or null
+  const uint8_t* w13c;         // [E][2I][H/2]
+  const uint8_t* w13s;         // [E][2I][H/32]
+  const uint8_t* w2c;          // [E][H][I/2]
+  const uint8_t* w2s;          // [E][H][I/32]
+  const int8_t* sh13;          // [2I][H]
+  const float* sh13s;          // [2I]
+  const int8_t* sh2;           // [H][I]
+  const float* sh2s;           // [H]
+  void* out;                   // [T][H]
+  int out_is_fp32;
+  int32_t* ids_out;            // [T][k]
+  float* w_out;                // [T][k]
+  uint32_t* xfer;              // hand-off region (kXferBytes, workspace)
+};
+// Whether the single-launch layer has a kernel for this shape whose whole
+// grid the current device holds at once.
+bool layer_small_supported(int H, int I, int E, int T, int k);
+hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace moe

@@ -115,3 +115,20 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(2, 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mx.route(cfg, x, torch.zeros(16, 256), torch.zeros(16))
+
+
+def test_forward_schedule_host_logic():
+    """The schedule query's argument checks and the choices that need no
+    device (hash layers, batches past the single-launch sizes)."""
+    L = mx.lib()
+    cfg = _cfg()
+    assert L.moe_forward_schedule(None, 1, 0) == mx.MOE_EINVAL
+    assert L.moe_forward_schedule(ctypes.byref(cfg), -1, 0) == mx.MOE_EINVAL
+    assert L.moe_forward_schedule(ctypes.byref(cfg), 65537, 0) == mx.MOE_EUNSUPPORTED
+    assert L.moe_forward_schedule(ctypes.byref(_cfg(top_k=9)), 1, 0) == mx.MOE_EUNSUPPORTED
+    assert mx.forward_schedule(cfg, 1, hash_layer=True) == "large"
+    assert mx.forward_schedule(cfg, 3) == "decode"
+    assert mx.forward_schedule(cfg, 64) == "decode"
+    assert mx.forward_schedule(cfg, 65) == "large"
+    # hidden 1024 has no single-launch kernel: the three-launch schedule
+    assert mx.forward_schedule(_cfg(hidden_size=1024, moe_intermediate=512, n_routed_experts=32), 1) == "tiny"

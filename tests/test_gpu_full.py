@@ -71,8 +71,18 @@ def _run(wl, Lv, Dv, rep, rows=None, check_all_routing=True):
 def test_decode_t1_full(full_layer, rep):
     L, D = full_layer
     wl = synth.WORKLOADS["decode_t1"]
+    assert mx.forward_schedule(mx.config_of(wl), 1) == "single"
     Lv, Dv = _variant(L, D, wl)
     _run(wl, Lv, Dv, rep)
+
+
+def test_decode_t2_full(full_layer):
+    """Two tokens: twelve slots and two shared columns in the one launch."""
+    L, D = full_layer
+    wl = dataclasses.replace(synth.WORKLOADS["decode_t1"], name="decode_t2", T=2)
+    assert mx.forward_schedule(mx.config_of(wl), 2) == "single"
+    Lv, Dv = _variant(L, D, wl)
+    _run(wl, Lv, Dv, 5)
 
 
 def test_decode_t64_full(full_layer):
