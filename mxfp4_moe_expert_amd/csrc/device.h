@@ -72,7 +72,13 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
 
 __device__ __forceinline__ float softplus(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware base-2 exponential and
+// reciprocal (about 1 ulp each; h is rounded to bf16 right after). For very
+// negative z, e^-z overflows to +inf and the reciprocal gives 0: silu -> -0.
+__device__ __forceinline__ float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // h = silu(min(g, L)) * clamp(u, -L, L)
 __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {

@@ -17,10 +17,17 @@
 //     stage and row block, 16 bytes of its row (the quarter g of the stage's
 //     K-values) straight into registers, two stages ahead. For MXFP4 these 32
 //     values are exactly one group, so one E8M0 byte per row block and stage;
-//     MXFP4 is converted to bf16 with the exact scaled FP4 convert.
+//     MXFP4 is converted to bf16 with the exact scaled FP4 convert. The E8M0
+//     bytes of the block's 256 rows are copied to LDS once, at the start
+//     (rows padded to K/32 + 4 bytes: 16 consecutive rows hit 16 banks): a
+//     one-byte global load per lane and stage costs as much of the memory
+//     pipeline as a 16-byte one.
 //   - tokens: the 128 gathered activation rows of a stage go global ->
-//     registers -> LDS (rows padded by 16 bytes, conflict-free 16-byte
-//     reads), double-buffered, one stage ahead.
+//     registers -> LDS, double-buffered, one stage ahead. LDS holds them
+//     fragment-major: for each (16-token block m, k-step kk) the 64 lanes'
+//     16-byte B fragments lie contiguously in lane order, so every MFMA
+//     operand read, and every store of a wave, is one contiguous 1 KB
+//     (padded token rows leave 16-byte reads with bank conflicts on gfx950).
 //   - MFMA k-step kk of a stage takes the lane's K-values 8kk .. +8 of its
 //     quarter on both operands (a fixed permutation of K, so the dot products
 //     are unchanged).
@@ -42,14 +49,15 @@ constexpr int kRB = 2;              // 16-row weight blocks per wave
 
 // Per format: K per stage (each lane's 16 weight bytes per row block are 32
 // E2M1 values or 16 int8 values, a quarter of the stage), MFMA k-steps per
-// stage, padded LDS bytes per token row and 16-byte activation pieces per
-// thread.
+// stage, LDS bytes per stage and 16-byte activation pieces per thread (the
+// thread's quarter of one token row: pieces kk = 0 .. kKK-1 of quarter g).
 template <int FMT>
 struct GemmCfg {
   static constexpr int kBK = FMT == kFmtMx ? 128 : 64;
   static constexpr int kKK = kBK / 32;
-  static constexpr int kArow = kBK * 2 + 16;
+  static constexpr int kStage = kBM * kBK * 2;
   static constexpr int kAVec = kBK / 32;
+  static_assert(kAVec == kKK, "a thread's pieces are the k-steps of one quarter");
 };
 
 // A lane's 16 weight bytes for one row block and stage, converted to bf16
@@ -64,18 +72,21 @@ __device__ __forceinline__ bf16x8_t gemm_conv(const u32x4_t& q, int kk, uint32_t
   }
 }
 
-// Weights (and, for MXFP4, the E8M0 scale byte of the lane's 32 K-values,
-// byte 4 st + g of the row: those 32 values are exactly one group) of the 4
-// row blocks for stage st.
+// Weights of the wave's row blocks for stage st.
+__device__ __forceinline__ void gemm_load_w(const uint8_t* qe, const uint32_t (&qoff)[kRB], int st,
+                                            u32x4_t (&w)[kRB]) {
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) w[b] = *reinterpret_cast<const u32x4_t*>(qe + (qoff[b] + (uint32_t)st * 64));
+}
+
+// MXFP4: the E8M0 byte of the lane's 32 K-values of stage st in each row
+// block (byte 4 st + g of the row: those 32 values are exactly one group),
+// from the block's scales in LDS.
 template <int FMT>
-__device__ __forceinline__ void gemm_load_w(const uint8_t* qe, const uint8_t* se, const uint32_t (&qoff)[kRB],
-                                            const uint32_t (&soff)[kRB], int st, u32x4_t (&w)[kRB],
+__device__ __forceinline__ void gemm_scales(const unsigned char* lds_s, const uint32_t (&soff)[kRB], int st,
                                             uint32_t (&sc)[kRB]) {
 #pragma unroll
-  for (int b = 0; b < kRB; ++b) {
-    w[b] = *reinterpret_cast<const u32x4_t*>(qe + (qoff[b] + (uint32_t)st * 64));
-    if (FMT == kFmtMx) sc[b] = se[soff[b] + (uint32_t)st * 4];
-  }
+  for (int b = 0; b < kRB; ++b) sc[b] = FMT == kFmtMx ? lds_s[soff[b] + (uint32_t)st * 4] : 0u;
 }
 
 
@@ -93,35 +104,49 @@ struct GemmA {
     for (int j = 0; j < N; ++j) v[j] = s[j];
     asm volatile("" ::: "memory");
   }
+  // dst: the thread's piece for k-step 0; k-step j lies 64 pieces further.
   __device__ __forceinline__ void store(u32x4_t* dst) const {
 #pragma unroll
-    for (int j = 0; j < N; ++j) dst[j] = v[j];
+    for (int j = 0; j < N; ++j) dst[j * 64] = v[j];
   }
 };
 
-// For each MFMA k-step: the wave's weight fragments converted once, then
-// each activation fragment read from LDS and used for kRB MFMAs.
+// For each MFMA k-step: the wave's weight fragments converted once, each
+// activation fragment used for kRB MFMAs. The activation fragments of k-step
+// kk+1 are read from LDS before the MFMAs of k-step kk (a scheduling barrier
+// keeps the reads there: left alone, the compiler issues each read right
+// before its MFMAs and every MFMA pair waits for the LDS latency).
 template <int FMT, int MB>
 __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x4_t (&w)[kRB],
-                                             const uint32_t (&sc)[kRB], const unsigned char* abase) {
-  constexpr int kArow = GemmCfg<FMT>::kArow;
+                                             const unsigned char* lds_s, const uint32_t (&soff)[kRB], int st,
+                                             const unsigned char* abase) {
+  constexpr int kKK = GemmCfg<FMT>::kKK;
+  uint32_t sc[kRB];
+  gemm_scales<FMT>(lds_s, soff, st, sc);
+  bf16x8_t bt[2][MB];
 #pragma unroll
-  for (int kk = 0; kk < GemmCfg<FMT>::kKK; ++kk) {
+  for (int m = 0; m < MB; ++m) bt[0][m] = *reinterpret_cast<const bf16x8_t*>(abase + (m * kKK) * 1024);
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    if (kk + 1 < kKK) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        bt[(kk + 1) & 1][m] = *reinterpret_cast<const bf16x8_t*>(abase + (m * kKK + kk + 1) * 1024);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8_t wa[kRB];
 #pragma unroll
     for (int b = 0; b < kRB; ++b) wa[b] = gemm_conv<FMT>(w[b], kk, sc[b]);
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const bf16x8_t bt = *reinterpret_cast<const bf16x8_t*>(abase + m * 16 * kArow + kk * 16);
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int b = 0; b < kRB; ++b) acc[b][m] = mfma_16x16x32(wa[b], bt, acc[b][m]);
-    }
+      for (int b = 0; b < kRB; ++b) acc[b][m] = mfma_16x16x32(wa[b], bt[kk & 1][m], acc[b][m]);
   }
 }
 
 // The K loop and epilogue of one block over its first MB*16 positions.
 template <int FMT, int MODE, int MB>
-__device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, const uint8_t* se,
+__device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, const unsigned char* lds_s,
                                           const uint32_t (&qoff)[kRB], const uint32_t (&soff)[kRB],
                                           const uint16_t* asrc, u32x4_t* adst0, u32x4_t* adst1,
                                           const unsigned char* abase0, const unsigned char* abase1, int nst,
@@ -133,33 +158,34 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
     for (int m = 0; m < MB; ++m) acc[b][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   // Software pipeline, branch-free so that every wait counts exactly: stage
-  // st computes from LDS buffer st%2 and weight registers st%2 while the
-  // activations of st+1 wait in registers and the weights of st+2 are in
-  // flight. Loads past the last stage re-read it (clamped, never used).
+  // st computes from LDS buffer st%2 and weight registers st%2; the
+  // activations of stages st+1 and st+2 are in registers (set s%2 holds
+  // stage s) or in flight, and the weights of st+2 are in flight. Loads past
+  // the last stage re-read it (clamped, never used).
   u32x4_t w0[kRB], w1[kRB];
-  uint32_t s0[kRB] = {}, s1[kRB] = {};
-  GemmA<FMT> av;
+  GemmA<FMT> av0, av1;
   const int last = nst - 1;
-  gemm_load_w<FMT>(qe, se, qoff, soff, 0, w0, s0);
-  av.load(asrc, 0);
-  av.store(adst0);
-  av.load(asrc, min(1, last));
-  gemm_load_w<FMT>(qe, se, qoff, soff, min(1, last), w1, s1);
+  gemm_load_w(qe, qoff, 0, w0);
+  av0.load(asrc, 0);
+  av0.store(adst0);
+  av1.load(asrc, min(1, last));
+  av0.load(asrc, min(2, last));
+  gemm_load_w(qe, qoff, min(1, last), w1);
   for (int st = 0; st + 1 < nst; st += 2) {
     __syncthreads();
-    av.store(adst1);  // stage st+1
-    av.load(asrc, min(st + 2, last));
-    gemm_compute<FMT, MB>(acc, w0, s0, abase0);
-    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 2, last), w0, s0);
+    av1.store(adst1);  // stage st+1
+    av1.load(asrc, min(st + 3, last));
+    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, st, abase0);
+    gemm_load_w(qe, qoff, min(st + 2, last), w0);
     __syncthreads();
-    av.store(adst0);  // stage st+2
-    av.load(asrc, min(st + 3, last));
-    gemm_compute<FMT, MB>(acc, w1, s1, abase1);
-    gemm_load_w<FMT>(qe, se, qoff, soff, min(st + 3, last), w1, s1);
+    av0.store(adst0);  // stage st+2
+    av0.load(asrc, min(st + 4, last));
+    gemm_compute<FMT, MB>(acc, w1, lds_s, soff, st + 1, abase1);
+    gemm_load_w(qe, qoff, min(st + 3, last), w1);
   }
   if (nst & 1) {  // the last stage (buffer 0, w0)
     __syncthreads();
-    gemm_compute<FMT, MB>(acc, w0, s0, abase0);
+    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, last, abase0);
   }
 
   // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
@@ -224,8 +250,9 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
 
 template <int FMT, int MODE>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
-  constexpr int kBK = GemmCfg<FMT>::kBK, kArow = GemmCfg<FMT>::kArow;
-  __shared__ __align__(16) unsigned char lds_a[2][kBM * kArow];
+  constexpr int kBK = GemmCfg<FMT>::kBK, kKK = GemmCfg<FMT>::kKK;
+  __shared__ __align__(16) unsigned char lds_a[2][GemmCfg<FMT>::kStage];
+  extern __shared__ __align__(16) unsigned char lds_s[];  // MXFP4: [256 local rows][K/32 + 4] E8M0 bytes
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int wn = wave;  // the wave's 32 weight rows; every wave covers all 128 positions
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
   // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
   const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
-  const uint8_t* se = FMT == kFmtMx ? p.wsc + (long long)e * p.s_expert_stride : p.wq;
+  const int srow = K / 32 + 4;  // padded LDS row of scales
   uint32_t qoff[kRB], soff[kRB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b) {
@@ -265,27 +292,63 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     if (MODE == kGemmW13) wrow = (b == 0 ? 0 : p.half) + nt * (kBN / 2) + wn * 16 + r;
     else wrow = nt * kBN + wn * 32 + b * 16 + r;
     qoff[b] = (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
-    soff[b] = (uint32_t)wrow * (K / 32) + g;
+    // local row: gate rows (w13) or the first 128 rows (w2) at 0 .., the rest at 128 ..
+    const int lrow = MODE == kGemmW13 ? (b == 0 ? 0 : 128) + wn * 16 + r : wn * 32 + b * 16 + r;
+    soff[b] = (uint32_t)lrow * srow + g;
   }
-  // this thread's activation loads: token row tid/4, quarter tid%4 of the
-  // row's stage. Rows past the tile re-read its first row: their results are
-  // never stored.
-  const int arow = tid >> 2, apart = tid & 3;
+  if (FMT == kFmtMx) {
+    // the block's scales: two runs of 128 rows (w13: gate rows, up rows;
+    // w2: the tile's 256 rows), K/32 bytes per row, in 16-byte pieces
+    const uint8_t* se = p.wsc + (long long)e * p.s_expert_stride;
+    const int rowlen = K / 32, npieces = 2 * 128 * rowlen / 16;
+    for (int i = tid; i < npieces; i += kGemmThreads) {
+      const int run = i / (npieces / 2), o = (i - run * (npieces / 2)) * 16;
+      const int grow0 = MODE == kGemmW13 ? (run == 0 ? 0 : p.half) + nt * (kBN / 2) : nt * kBN + run * 128;
+      const uint4 v = *reinterpret_cast<const uint4*>(se + (size_t)grow0 * rowlen + o);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int oq = o + 4 * q, row = oq / rowlen, col = oq - row * rowlen;
+        *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[q];
+      }
+    }
+  }
+  // this thread's activation loads: token row 16*wave + lane%16, quarter
+  // lane/16 of the row's stage (so that a wave's LDS stores are contiguous).
+  // Rows past the tile re-read its first row: their results are never stored.
+  const int arow = wave * 16 + r, apart = g;
   const int apos = pos0 + (arow < ncols ? arow : 0);
   const size_t atrow = p.act_row ? (size_t)p.act_row[apos] : (size_t)apos;
   const uint16_t* asrc = p.act + atrow * p.act_ld + apart * (kBK / 4);
-  u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][arow * kArow + apart * (kBK / 2)]);
-  u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][arow * kArow + apart * (kBK / 2)]);
-  const unsigned char* abase0 = &lds_a[0][r * kArow + g * (kBK / 2)];
-  const unsigned char* abase1 = &lds_a[1][r * kArow + g * (kBK / 2)];
+  // fragment-major LDS: piece (token t, quarter q, k-step j) at 16 bytes x
+  // ((t/16 * kKK + j) * 64 + q * 16 + t%16), i.e. where lane (r = t%16, g =
+  // q) of the MFMAs of token block t/16 reads it
+  const int aslot = ((arow >> 4) * kKK) * 64 + apart * 16 + (arow & 15);
+  u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][aslot * 16]);
+  u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][aslot * 16]);
+  const unsigned char* abase0 = &lds_a[0][lane * 16];
+  const unsigned char* abase1 = &lds_a[1][lane * 16];
 
-  // a tile of at most 64 positions runs half the MFMAs (uniform branch)
-  if (ncols <= kBM / 2)
-    gemm_main<FMT, MODE, kMB / 2>(p, qe, se, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                  wn, g, r);
-  else
-    gemm_main<FMT, MODE, kMB>(p, qe, se, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
+  // a tile runs the MFMAs of its positions rounded up to 32 (uniform branch:
+  // partly filled last tiles of the experts would otherwise waste about a
+  // sixth of the work at prefill)
+  switch ((ncols + 31) >> 5) {
+    case 1:
+      gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
                               g, r);
+      break;
+    case 2:
+      gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
+                              g, r);
+      break;
+    case 3:
+      gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
+                              g, r);
+      break;
+    default:
+      gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
+                                wn, g, r);
+  }
 }
 
 template <int FMT, int MODE>
@@ -293,7 +356,16 @@ static hipError_t launch_gemm_t(const GemmArgs& p, int tiles, hipStream_t st) {
   const long long nblk = (long long)tiles * p.n_ntiles;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_gemm<FMT, MODE><<<(unsigned)nblk, kGemmThreads, 0, st>>>(p);
+  const size_t dyn = FMT == kFmtMx ? (size_t)2 * 128 * (p.K / 32 + 4) : 0;
+  if (dyn + 2 * GemmCfg<FMT>::kStage > 160 * 1024) return hipErrorInvalidValue;
+  static size_t raised = 0;  // dynamic LDS limit set so far for this kernel
+  if (dyn > raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT, MODE>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    raised = dyn;
+  }
+  k_gemm<FMT, MODE><<<(unsigned)nblk, kGemmThreads, dyn, st>>>(p);
   return hipGetLastError();
 }
 
