@@ -645,9 +645,12 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;
     g13.n_rowblocks = h13.n_rowblocks = I / 64;
     g2.n_rowblocks = h2.n_rowblocks = H / 128;
-    h13.tile_n = fit_tile(T < 4 ? T : 4, H);
+    // shared-expert tiles of 8 tokens: each tile streams the whole shared
+    // expert, so wider tiles read it fewer times (measured best: 16 would
+    // set the launch's LDS, and with it the routed blocks' occupancy)
+    h13.tile_n = fit_tile(T < 8 ? T : 8, H);
     h13.n_tiles_grid = (T + h13.tile_n - 1) / h13.tile_n;
-    h2.tile_n = fit_tile(T < 4 ? T : 4, I);
+    h2.tile_n = fit_tile(T < 8 ? T : 8, I);
     h2.n_tiles_grid = (T + h2.tile_n - 1) / h2.tile_n;
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
       return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks, st);

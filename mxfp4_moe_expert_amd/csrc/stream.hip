@@ -21,8 +21,9 @@
 //     fragments for the same K range come from the tile's columns in LDS.
 //     Any permutation of K shared by both operands leaves the sums unchanged.
 //   - Loads for stage st + D are issued right after stage st is consumed;
-//     past the last stage they re-read it (clamped), so the loop has no
-//     branches and the compiler's waits count exactly.
+//     the last D stages are a second copy of the loop body without loads, so
+//     neither loop has branches (the compiler's waits count exactly) and no
+//     load is spent on a stage past the end.
 //   - The first D stages of weights are requested as soon as the tile's
 //     expert is known; the activation columns' round trips (row ids, then
 //     rows) overlap them.
@@ -196,26 +197,30 @@ __device__ __forceinline__ void stream_block(const SkinnyArgs& p, int bid, unsig
   const int brB = MODE == kW13 ? 64 + wave * 16 + r : wave * 32 + 16 + r;
   const unsigned char* scA = lds_sc + (size_t)brA * srow + g;
   const unsigned char* scB = lds_sc + (size_t)brB * srow + g;
-  for (int st0 = 0; st0 < S; st0 += D) {
+  auto stage = [&](int i, int st) __attribute__((always_inline)) {
+    bf16x8_t b[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      b[kk] = live ? *reinterpret_cast<const bf16x8_t*>(bcol + st * 256 + kk * 16) : zero8;
+    const uint32_t scaleA = FMT == kFmtMx ? scA[st * 4] : 0u;
+    const uint32_t scaleB = FMT == kFmtMx ? scB[st * 4] : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      accA = mfma_16x16x32(stream_frag<FMT>(wA[i], kk, scaleA), b[kk], accA);
+      accB = mfma_16x16x32(stream_frag<FMT>(wB[i], kk, scaleB), b[kk], accB);
+    }
+  };
+  int st0 = 0;
+  for (; st0 + D < S; st0 += D) {  // S is a multiple of D
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      const int st = st0 + i;
-      bf16x8_t b[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        b[kk] = live ? *reinterpret_cast<const bf16x8_t*>(bcol + st * 256 + kk * 16) : zero8;
-      const uint32_t scaleA = FMT == kFmtMx ? scA[st * 4] : 0u;
-      const uint32_t scaleB = FMT == kFmtMx ? scB[st * 4] : 0u;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        accA = mfma_16x16x32(stream_frag<FMT>(wA[i], kk, scaleA), b[kk], accA);
-        accB = mfma_16x16x32(stream_frag<FMT>(wB[i], kk, scaleB), b[kk], accB);
-      }
-      const int nx = min(st + D, S - 1);
-      stream_load<FMT>(qA, nx, wA[i]);
-      stream_load<FMT>(qB, nx, wB[i]);
+      stage(i, st0 + i);
+      stream_load<FMT>(qA, st0 + i + D, wA[i]);
+      stream_load<FMT>(qB, st0 + i + D, wB[i]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < D; ++i) stage(i, st0 + i);  // the last D stages: nothing left to request
   if (!live) return;
 
   // 5. epilogue: lane (r, g) holds rows 4g .. 4g+3 of each row block, column r
