@@ -18,7 +18,7 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, xfer, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
+  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
   int tile_n, max_tiles;
 };
@@ -74,6 +74,10 @@ Layout layout(const moe_config& c, int T) {
   };
   L.counters = take(256);
   L.xfer = take(kXferBytes);
+  // large-T router: bf16 planes of the router rows, partial logits per K slice
+  const bool big = T > kSmallT;
+  L.wsplit = take(big ? (size_t)3 * E * H * 2 : 0);
+  L.plog = take(big ? (size_t)router_mfma_splits(T, (int)H) * T * E * 4 : 0);
   L.scores = take((size_t)2 * T * E * 4);  // scores, then selection values
   L.ids = take(slots * 4);
   L.w = take(slots * 4);
@@ -427,7 +431,7 @@ int moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* 
     if (rc) return rc;
     return status(launch_topk_permute_small(a, p, st));
   }
-  return status(launch_router_large(a, st));
+  return status(launch_router_mfma(a, at<uint16_t>(workspace, L.wsplit), at<float>(workspace, L.plog), st));
 }
 
 int moe_hash_route(const moe_config* cfg, int32_t T, const uint16_t* x, const int32_t* token_ids,
@@ -679,7 +683,9 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_hash_route(h, st); }));
     } else {
       RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
-      rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_large(a, st); }));
+      rc = status(timed(MOE_KERNEL_ROUTER, st, [&] {
+        return launch_router_mfma(a, at<uint16_t>(workspace, L.wsplit), at<float>(workspace, L.plog), st);
+      }));
     }
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] {

@@ -157,7 +157,17 @@ struct CombineArgs {
 hipError_t launch_router_small(const RouterArgs& r, const SkinnyArgs* shared_w13, int shared_blocks,
                                hipStream_t st);
 hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStream_t st);
-hipError_t launch_router_large(const RouterArgs& r, hipStream_t st);
+// Large-T learned router on bf16 MFMA (fp32 router rows split into three
+// bf16 planes, wsplit [3][E][H]; partial logits plog [KS][T][E] with KS =
+// router_mfma_splits(T, H)).
+struct RouterMfmaArgs {
+  int T, H, E, KS;
+  const uint16_t* x;
+  const uint16_t* wsplit;
+  float* plog;
+};
+int router_mfma_splits(int T, int H);
+hipError_t launch_router_mfma(const RouterArgs& r, uint16_t* wsplit, float* plog, hipStream_t st);
 hipError_t launch_hash_route(const HashArgs& a, hipStream_t st);
 // Permutation and tiles
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p, int32_t* blk_counts,

@@ -221,82 +221,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_permute_small(RouterArgs 
   }
 }
 
-// ---------------------------------------------------------------- large-T router
-
-// logits[T][E] = x[T][H] * Wg[E][H]^T (+ offset): 64x64 output tile per block,
-// 256 threads with 4x4 outputs each, K staged through LDS 32 at a time.
-__global__ __launch_bounds__(256) void k_router_tiled(RouterArgs a) {
-  constexpr int BT = 64, BE = 64, BK = 32;
-  __shared__ float xs[BK][BT + 4];
-  __shared__ float gs[BK][BE + 4];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4] = {};
-  const int lr = tid / 4, lk = (tid % 4) * 8;
-  for (int k0 = 0; k0 < a.H; k0 += BK) {
-    {
-      const int t = t0 + lr;
-      uint4 xv = make_uint4(0, 0, 0, 0);
-      if (t < a.T) xv = *reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + k0 + lk);
-      xs[lk + 0][lr] = bf16_to_f32(xv.x & 0xffff);
-      xs[lk + 1][lr] = bf16_to_f32(xv.x >> 16);
-      xs[lk + 2][lr] = bf16_to_f32(xv.y & 0xffff);
-      xs[lk + 3][lr] = bf16_to_f32(xv.y >> 16);
-      xs[lk + 4][lr] = bf16_to_f32(xv.z & 0xffff);
-      xs[lk + 5][lr] = bf16_to_f32(xv.z >> 16);
-      xs[lk + 6][lr] = bf16_to_f32(xv.w & 0xffff);
-      xs[lk + 7][lr] = bf16_to_f32(xv.w >> 16);
-      const int e = e0 + lr;
-      float4 g0 = make_float4(0, 0, 0, 0), g1 = make_float4(0, 0, 0, 0);
-      if (e < a.E) {
-        g0 = *reinterpret_cast<const float4*>(a.gate_w + (size_t)e * a.H + k0 + lk);
-        g1 = *reinterpret_cast<const float4*>(a.gate_w + (size_t)e * a.H + k0 + lk + 4);
-      }
-      gs[lk + 0][lr] = g0.x;
-      gs[lk + 1][lr] = g0.y;
-      gs[lk + 2][lr] = g0.z;
-      gs[lk + 3][lr] = g0.w;
-      gs[lk + 4][lr] = g1.x;
-      gs[lk + 5][lr] = g1.y;
-      gs[lk + 6][lr] = g1.z;
-      gs[lk + 7][lr] = g1.w;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < BK; ++kk) {
-      float xa[4], gb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[i] = xs[kk][ty * 4 + i];
-        gb[i] = gs[kk][tx * 4 + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += xa[i] * gb[j];
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= a.T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < a.E) store_score(a, t, e, acc[i][j] + (a.logit_offset ? a.logit_offset[e] : 0.0f));
-    }
-  }
-}
-
-// One wave per token: top-k of the scores written by k_router_tiled.
-__global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
-            a.w + (size_t)t * a.k, nullptr);
-}
+// The large-T learned router is in router_mfma.hip.
 
 // ---------------------------------------------------------------- hash router
 
@@ -375,16 +300,6 @@ hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStre
   if (r.T <= 0) return hipSuccess;
   if (r.T > kSmallT || r.k > kMaxTopK || r.E > kMaxExperts) return hipErrorInvalidValue;
   k_topk_permute_small<<<1, kTopkThreads, 0, st>>>(r, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_large(const RouterArgs& a, hipStream_t st) {
-  if (a.T <= 0) return hipSuccess;
-  dim3 g((a.T + 63) / 64, (a.E + 63) / 64);
-  k_router_tiled<<<g, 256, 0, st>>>(a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  k_topk<<<(a.T + 3) / 4, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
