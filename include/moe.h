@@ -46,10 +46,11 @@
  *     ids in [0, V); E8M0 scale bytes should not be 0xFF (NaN).
  *   - `workspace` is device scratch of at least moe_workspace_size() bytes,
  *     256-byte aligned. Zero-fill it once before its first use
- *     (moe_workspace_init, or any zero fill): bytes 256 .. 136447 hold the
- *     hand-off state of the single-launch layer (MOE_SCHED_SINGLE), which
- *     every call leaves ready for the next; every other workspace value is
- *     written before it is read. Calls that share one workspace must be
+ *     (moe_workspace_init, or any zero fill): bytes 64 .. 67 count the
+ *     blocks of the decode-size top-k, and bytes 256 .. 136447 hold the
+ *     hand-off state of the single-launch layer (MOE_SCHED_SINGLE); every
+ *     call leaves both ready for the next, and every other workspace value
+ *     is written before it is read. Calls that share one workspace must be
  *     ordered on one stream. If a single-launch call's bounded wait for
  *     another block of its grid expires (about a second), its output is
  *     NaN; the hand-off state stays consistent.

@@ -41,16 +41,19 @@ int fit_tile(int want, int K) {
   return tn;
 }
 
-// Columns per routed expert tile: about the expected tokens per expert, so
-// the LDS activation tile stays small at decode sizes.
+// Columns per routed expert tile at decode sizes: a few times the expected
+// tokens per expert (1.5 at 64 tokens, 6 of 256 experts), so that an expert
+// seldom needs a second tile, which would stream its weights again, while
+// the LDS activation tile stays no larger than the shared expert's.
 // Batches above kSmallT run the grouped GEMMs (256-row output tiles along H).
 bool use_gemm(const moe_config& c, int T) { return T > kSmallT && c.hidden_size % 256 == 0; }
 
 int routed_tile_n(const moe_config& c, int T) {
   if (use_gemm(c, T)) return kGemmTokens;
-  const int want = T <= 1 ? 1 : 4;
   const int K = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
-  return fit_tile(want, K);
+  int tn = T <= 1 ? 1 : 6;
+  while (tn > 1 && (size_t)tn * (2 * (size_t)K + 16) > kActLdsBudget) --tn;
+  return tn;
 }
 
 int routed_max_tiles(const moe_config& c, int T, int tile_n) {
@@ -427,9 +430,9 @@ int moe_route(const moe_config* cfg, int32_t T, const uint16_t* x, const float* 
   if (T <= kSmallT) {
     Perm p = perm_of(workspace, L, at<int32_t>(workspace, L.offsets), at<int32_t>(workspace, L.sorted),
                      at<int32_t>(workspace, L.slot_pos));
-    rc = status(launch_router_small(a, nullptr, 0, st));
+    rc = status(launch_router_dec(a, st));
     if (rc) return rc;
-    return status(launch_topk_permute_small(a, p, st));
+    return status(launch_topk_permute_small(a, p, at<int32_t>(workspace, L.counters) + kArrivalsInt, st));
   }
   return status(launch_router_mfma(a, at<uint16_t>(workspace, L.wsplit), at<float>(workspace, L.plog), st));
 }
@@ -641,9 +644,11 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     // router | top-k + permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine,
     // the expert passes as streaming blocks
     RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
-    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_small(a, nullptr, 0, st); }));
+    rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_dec(a, st); }));
     if (rc) return rc;
-    rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] { return launch_topk_permute_small(a, p, st); }));
+    rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] {
+      return launch_topk_permute_small(a, p, at<int32_t>(workspace, L.counters) + kArrivalsInt, st);
+    }));
     if (rc) return rc;
     const int H = cfg->hidden_size, I = cfg->moe_intermediate;
     SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;

@@ -156,7 +156,13 @@ struct CombineArgs {
 // Routers
 hipError_t launch_router_small(const RouterArgs& r, const SkinnyArgs* shared_w13, int shared_blocks,
                                hipStream_t st);
-hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStream_t st);
+// Decode router (H = 1024, 2048 or 4096; other sizes use launch_router_small).
+hipError_t launch_router_dec(const RouterArgs& r, hipStream_t st);
+// Top-k of every token and the permutation; arrivals: an int of the
+// workspace that is zero before the call and is zero again after it.
+hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, int* arrivals, hipStream_t st);
+// Workspace int (in the counters region) that counts the top-k blocks.
+constexpr int kArrivalsInt = 16;
 // Large-T learned router on bf16 MFMA (fp32 router rows split into three
 // bf16 planes, wsplit [3][E][H]; partial logits plog [KS][T][E] with KS =
 // router_mfma_splits(T, H)).

@@ -14,11 +14,13 @@
 // Logits are fp32 sums of bf16 x times fp32 Wg. The selection compares the
 // fp32 values s + bias; equal values go to the lower expert id.
 //
-// Decode sizes (T <= kSmallT) use two launches: k_router_small computes the
-// logits and from them the scores and selection values, one block per expert, and shares its launch with the shared
-// expert's w13 blocks (that work does not depend on the routing); then one
-// block (k_topk_permute_small) selects the experts of every token and builds
-// the permutation and the expert tile table.
+// Decode sizes (T <= kSmallT) use two launches. The logits, scores and
+// selection values come from k_router_dec (blocks of 4 experts x 8 tokens,
+// the tokens staged in LDS) or, for one or two tokens, from k_router_small
+// (one block per expert, sharing its launch with the shared expert's w13
+// blocks, which do not depend on the routing). Then k_topk_dec selects the
+// experts of every token, one wave per token over many blocks, and the last
+// block to finish builds the permutation and the expert tile table.
 #include "device.h"
 #include "internal.h"
 #include "skinny.h"
@@ -141,6 +143,69 @@ __global__ __launch_bounds__(kThreads) void k_router_small(RouterArgs a, SkinnyA
   }
 }
 
+// Logits of experts 8 bx .. 8 bx + 7 (one per wave) for tokens 8 by .. +7,
+// H = 512 NC (NC = 2, 4 or 8): the block stages the token rows in LDS in one
+// round of loads; each wave keeps its expert's router row in registers
+// (lane l: elements 512 c + 8 l .. +8), forms the lane partials of all 8
+// tokens at once (the products of a token in the order of
+// router_logits_waves), reduces them over the wave, and lane q then takes
+// the score of token q.
+constexpr int kDecExperts = 8, kDecTokens = 8;
+
+template <int NC>
+__global__ __launch_bounds__(kDecExperts * 64) void k_router_dec(RouterArgs a) {
+  constexpr int H = NC * 512;
+  __shared__ __align__(16) uint16_t xs[kDecTokens * H];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.x * kDecExperts + wave;  // surplus waves compute, never store
+  const int t0 = blockIdx.y * kDecTokens, nt = min(kDecTokens, a.T - t0);
+  const float* we = a.gate_w + (size_t)min(e, a.E - 1) * H;
+  float4 w[2 * NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    w[2 * c] = *reinterpret_cast<const float4*>(we + c * 512 + lane * 8);
+    w[2 * c + 1] = *reinterpret_cast<const float4*>(we + c * 512 + lane * 8 + 4);
+  }
+  constexpr int n16 = H / 8, npieces = kDecTokens * n16;  // 16-byte pieces of the 8 rows
+  constexpr int per = npieces / (kDecExperts * 64);
+  uint4 v[per];
+#pragma unroll
+  for (int j = 0; j < per; ++j) {  // rows past the batch repeat its last one (never used)
+    const int i = tid + kDecExperts * 64 * j;
+    v[j] = *reinterpret_cast<const uint4*>(a.x + (size_t)(t0 + min(i / n16, nt - 1)) * H + (i % n16) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < per; ++j) *reinterpret_cast<uint4*>(xs + (size_t)(tid + kDecExperts * 64 * j) * 8) = v[j];
+  __syncthreads();
+  float acc[kDecTokens];
+#pragma unroll
+  for (int t = 0; t < kDecTokens; ++t) {
+    acc[t] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * H + c * 512 + lane * 8);
+      const float4 w0 = w[2 * c], w1 = w[2 * c + 1];
+      float s = acc[t];
+      s += bf16_to_f32(xv.x & 0xffff) * w0.x;
+      s += bf16_to_f32(xv.x >> 16) * w0.y;
+      s += bf16_to_f32(xv.y & 0xffff) * w0.z;
+      s += bf16_to_f32(xv.y >> 16) * w0.w;
+      s += bf16_to_f32(xv.z & 0xffff) * w1.x;
+      s += bf16_to_f32(xv.z >> 16) * w1.y;
+      s += bf16_to_f32(xv.w & 0xffff) * w1.z;
+      s += bf16_to_f32(xv.w >> 16) * w1.w;
+      acc[t] = s;
+    }
+  }
+  float mine = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kDecTokens; ++t) {
+    const float v = wave_sum(acc[t]);
+    mine = lane == t ? v : mine;
+  }
+  if (e < a.E && lane < nt) store_score(a, t0 + lane, e, mine + (a.logit_offset ? a.logit_offset[e] : 0.0f));
+}
+
 // Writes the expert tile table from the per-expert counts (thread e < E of a
 // block holds count c and first position off of expert e): tiles of at most
 // tile_n consecutive sorted positions of one expert, in expert order.
@@ -158,45 +223,38 @@ __device__ void block_write_tiles(int c, int off, int E, const Perm& p, int* sca
   if (tid == 0) *p.n_tiles = total;
 }
 
-// One block of 1024 threads: top-k of every token (16 waves, one token at a
-// time each), then the stable counting sort of the T*k <= 512 slots and the
+// Top-k of every token, one wave per token (4 per block); then the last
+// block to finish (an arrival count in the workspace, which it sets back to
+// zero) makes the stable counting sort of the T*k <= 512 slots and the
 // expert tile table. Stable ranks come from per-expert slot bitmasks: the
 // rank of slot i among the slots of its expert is the number of set bits
 // below bit i of that expert's mask.
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = 256;
 constexpr int kMaskWords = kSmallT * kMaxTopK / 64;  // 64-bit words per expert mask
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk_permute_small(RouterArgs a, Perm p) {
-  __shared__ int32_t ids_lds[kSmallT * kMaxTopK];
+__global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p, int* arrivals) {
   __shared__ unsigned long long mask[kMaxExperts][kMaskWords];
   __shared__ int first[kMaxExperts];
   __shared__ int scan_tmp[kTopkThreads];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  {  // each wave's (at most 4) tokens: every score load first, then the selections
-    constexpr int kW = kTopkThreads / 64;
-    TopkRow rows[kSmallT / kW];
-#pragma unroll
-    for (int i = 0; i < kSmallT / kW; ++i) {
-      const int t = min(wave + kW * i, a.T - 1);
-      rows[i] = topk_load(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E);
-    }
-#pragma unroll
-    for (int i = 0; i < kSmallT / kW; ++i) {
-      const int t = wave + kW * i;
-      if (t < a.T)
-        wave_topk_row(rows[i], a.E, a.k, a.scale, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, ids_lds + t * a.k);
-    }
-  }
+  __shared__ int is_last;
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * (kTopkThreads / 64) + (tid >> 6);
+  if (t < a.T)
+    wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
+              a.w + (size_t)t * a.k, nullptr);
+  __threadfence();  // this block's ids are visible before it is counted
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();  // every other block's ids are visible from here on
+
   unsigned long long* mflat = &mask[0][0];
   for (int i = tid; i < kMaxExperts * kMaskWords; i += kTopkThreads) mflat[i] = 0ull;
   __syncthreads();
   const int n = a.T * a.k;
   const int words = (n + 63) >> 6;
-  int e_i = 0;
-  if (tid < n) {
-    e_i = ids_lds[tid];
-    atomicOr(&mask[e_i][tid >> 6], 1ull << (tid & 63));
-  }
+  for (int i = tid; i < n; i += kTopkThreads) atomicOr(&mask[a.ids[i]][i >> 6], 1ull << (i & 63));
   __syncthreads();
   int c = 0;
   if (tid < a.E)
@@ -210,15 +268,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_permute_small(RouterArgs 
   if (tid == 0) p.offsets[a.E] = total;
   block_write_tiles(c, off, a.E, p, scan_tmp);
   __syncthreads();
-  if (tid < n) {
-    const int wi = tid >> 6;
-    int rank = __popcll(mask[e_i][wi] & ((1ull << (tid & 63)) - 1ull));
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const int e_i = a.ids[i];
+    const int wi = i >> 6;
+    int rank = __popcll(mask[e_i][wi] & ((1ull << (i & 63)) - 1ull));
     for (int w = 0; w < wi; ++w) rank += __popcll(mask[e_i][w]);
     const int pos = first[e_i] + rank;
-    p.sorted_slots[pos] = tid;
-    p.slot_pos[tid] = pos;
-    p.sorted_tok[pos] = tid / a.k;
+    p.sorted_slots[pos] = i;
+    p.slot_pos[i] = pos;
+    p.sorted_tok[pos] = i / a.k;
   }
+  if (tid == 0) *arrivals = 0;  // ready for the next call
 }
 
 // The large-T learned router is in router_mfma.hip.
@@ -296,10 +356,22 @@ hipError_t launch_router_small(const RouterArgs& r, const SkinnyArgs* sh, int sh
   return hipGetLastError();
 }
 
-hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, hipStream_t st) {
+hipError_t launch_router_dec(const RouterArgs& r, hipStream_t st) {
+  if (r.T <= 0) return hipSuccess;
+  const dim3 grid((r.E + kDecExperts - 1) / kDecExperts, (r.T + kDecTokens - 1) / kDecTokens);
+  const dim3 block(kDecExperts * 64);
+  if (r.H == 1024) k_router_dec<2><<<grid, block, 0, st>>>(r);
+  else if (r.H == 2048) k_router_dec<4><<<grid, block, 0, st>>>(r);
+  else if (r.H == 4096) k_router_dec<8><<<grid, block, 0, st>>>(r);
+  else return launch_router_small(r, nullptr, 0, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, int* arrivals, hipStream_t st) {
   if (r.T <= 0) return hipSuccess;
   if (r.T > kSmallT || r.k > kMaxTopK || r.E > kMaxExperts) return hipErrorInvalidValue;
-  k_topk_permute_small<<<1, kTopkThreads, 0, st>>>(r, p);
+  const int per = kTopkThreads / 64;
+  k_topk_dec<<<(r.T + per - 1) / per, kTopkThreads, 0, st>>>(r, p, arrivals);
   return hipGetLastError();
 }
 
