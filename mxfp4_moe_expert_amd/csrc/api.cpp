@@ -18,7 +18,7 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, blk_counts, hbuf, hs, ybuf,
+  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, tile_rec, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
   int tile_n, max_tiles;
 };
@@ -89,6 +89,7 @@ Layout layout(const moe_config& c, int T) {
   L.slot_pos = take(slots * 4);
   L.sorted_tok = take(slots * 4);
   L.tile_info = take((size_t)L.max_tiles * 16);
+  L.tile_rec = take((size_t)L.max_tiles * kRecInts * 4);
   L.blk_counts = take(nblk * E * 4);
   L.hbuf = take(slots * I * 2);
   L.hs = take((size_t)T * I * 2);
@@ -133,6 +134,8 @@ Perm perm_of(void* ws, const Layout& L, int32_t* offsets, int32_t* sorted, int32
   p.sorted_tok = at<int32_t>(ws, L.sorted_tok);
   p.tile_info = at<int4>(ws, L.tile_info);
   p.n_tiles = at<int32_t>(ws, L.counters);
+  p.tile_rec = at<int32_t>(ws, L.tile_rec);
+  p.queues = at<int32_t>(ws, L.counters) + kQueueInts;
   p.tile_n = L.tile_n;
   p.max_tiles = L.max_tiles;
   return p;
@@ -162,12 +165,14 @@ SkinnyArgs routed_w13_args(const moe_config& c, int T, const uint16_t* x, const 
   a.s_expert_stride = (long long)2 * I * (H / 32);
   a.K = H;
   a.half = I;
+  a.rows = 2 * I;
   a.n_rowblocks = I / 16;
   a.act = x;
   a.act_ld = H;
   a.act_row = p.sorted_tok;
   a.hout = hbuf;
   a.hout_ld = I;
+  a.tile_rec = p.tile_rec;
   return a;
 }
 
@@ -187,6 +192,7 @@ SkinnyArgs routed_w2_args(const moe_config& c, int T, const Perm& p, const float
   a.s_expert_stride = (long long)H * (I / 32);
   a.K = I;
   a.half = 0;
+  a.rows = H;
   a.n_rowblocks = H / 16;
   a.act = hbuf;
   a.act_ld = I;
@@ -195,6 +201,7 @@ SkinnyArgs routed_w2_args(const moe_config& c, int T, const Perm& p, const float
   a.yout_ld = H;
   a.sorted_slots = p.sorted_slots;
   a.slot_w = slot_w;
+  a.tile_rec = p.tile_rec;
   return a;
 }
 
@@ -211,6 +218,7 @@ SkinnyArgs shared_w13_args(const moe_config& c, int T, const uint16_t* x, const 
   a.row_scale = s13;
   a.K = H;
   a.half = I;
+  a.rows = 2 * I;
   a.n_rowblocks = slim ? I / 8 : I / 16;
   a.act = x;
   a.act_ld = H;
@@ -232,6 +240,7 @@ SkinnyArgs shared_w2_args(const moe_config& c, int T, const int8_t* q2, const fl
   a.row_scale = s2;
   a.K = I;
   a.half = 0;
+  a.rows = H;
   a.n_rowblocks = H / 16;
   a.act = hs;
   a.act_ld = I;
@@ -512,14 +521,17 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   } else if (T <= kSmallT) {
     SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
     SkinnyArgs r2 = routed_w2_args(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
-    r13.n_rowblocks = cfg->moe_intermediate / 64;
-    r2.n_rowblocks = cfg->hidden_size / 128;
+    r13.n_rowblocks = cfg->moe_intermediate / 128;
+    r2.n_rowblocks = (cfg->hidden_size + 255) / 256;
+    rc = status(launch_tile_records(p, topk_w, st));
+    if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
-      return launch_stream(kW13, r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, st);
+      return launch_stream(kW13, r13, p.max_tiles * r13.n_rowblocks, nullptr, 0, p.queues, st);
     }));
     if (rc) return rc;
-    rc = status(timed(MOE_KERNEL_ROUTED_W2, st,
-                      [&] { return launch_stream(kW2, r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
+    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] {
+      return launch_stream(kW2, r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, p.queues + 1, st);
+    }));
     if (rc) return rc;
   } else {
     const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
@@ -652,8 +664,8 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     if (rc) return rc;
     const int H = cfg->hidden_size, I = cfg->moe_intermediate;
     SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;
-    g13.n_rowblocks = h13.n_rowblocks = I / 64;
-    g2.n_rowblocks = h2.n_rowblocks = H / 128;
+    g13.n_rowblocks = h13.n_rowblocks = I / 128;
+    g2.n_rowblocks = h2.n_rowblocks = (H + 255) / 256;
     // shared-expert tiles of 8 tokens: each tile streams the whole shared
     // expert, so wider tiles read it fewer times (measured best: 16 would
     // set the launch's LDS, and with it the routed blocks' occupancy)
@@ -662,11 +674,13 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     h2.tile_n = fit_tile(T < 8 ? T : 8, I);
     h2.n_tiles_grid = (T + h2.tile_n - 1) / h2.tile_n;
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
-      return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks, st);
+      return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks,
+                           p.queues, st);
     }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] {
-      return launch_stream(kW2, g2, p.max_tiles * g2.n_rowblocks, &h2, h2.n_tiles_grid * h2.n_rowblocks, st);
+      return launch_stream(kW2, g2, p.max_tiles * g2.n_rowblocks, &h2, h2.n_tiles_grid * h2.n_rowblocks,
+                           p.queues + 1, st);
     }));
     if (rc) return rc;
   } else {

@@ -24,9 +24,18 @@ struct Perm {
   int32_t* sorted_tok;    // [T*k] token of each sorted position
   int4* tile_info;        // [max_tiles] {expert, first position, columns, 0}
   int32_t* n_tiles;       // [1] tiles in use
+  int32_t* tile_rec;      // [max_tiles][kRecInts] tile records (decode sizes)
+  int32_t* queues;        // [2] unit counters of the streaming w13 and w2 passes
   int tile_n;
   int max_tiles;
 };
+
+// Tile record, one per routed tile, written with the tile table at decode
+// sizes (write_tile_records) and read by the streaming passes, kRecInts ints:
+// expert, first position, columns, 0, then for columns c < 16 (columns past
+// the tile repeat its last one) the token of the position, the slot, and the
+// slot's routing weight (float bits).
+constexpr int kRecInts = 52;
 
 enum { kFmtMx = 0, kFmtI8 = 1 };  // routed MXFP4 / shared int8 weights
 enum { kW13 = 0, kW2 = 1 };        // expert stage
@@ -66,6 +75,7 @@ struct SkinnyArgs {
   long long s_expert_stride;  // bytes between experts of wsc
   int K;                      // input features
   int half;                   // w13: I (up rows start there); w2: 0
+  int rows;                   // weight rows of the pass (w13: 2I, w2: H)
   int n_rowblocks;            // output rows / 16
   int routed;                 // 1: tiles from perm.tile_info; 0: tiles of consecutive tokens;
                               // 2: one tile per slot, expert from the top-k computed in the block
@@ -83,6 +93,7 @@ struct SkinnyArgs {
   int yout_ld;
   const int32_t* sorted_slots;
   const float* slot_w;        // w2 routed: combine weight of each slot
+  const int32_t* tile_rec;    // routed tile records (streaming passes)
   float limit;
   // routed == 2 only: router scores and selection values, and the routing
   // outputs this pass writes
@@ -161,8 +172,10 @@ hipError_t launch_router_dec(const RouterArgs& r, hipStream_t st);
 // Top-k of every token and the permutation; arrivals: an int of the
 // workspace that is zero before the call and is zero again after it.
 hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, int* arrivals, hipStream_t st);
-// Workspace int (in the counters region) that counts the top-k blocks.
+// Workspace ints (in the counters region): the top-k blocks' arrival count,
+// then the streaming passes' two unit counters.
 constexpr int kArrivalsInt = 16;
+constexpr int kQueueInts = 17;
 // Large-T learned router on bf16 MFMA (fp32 router rows split into three
 // bf16 planes, wsplit [3][E][H]; partial logits plog [KS][T][E] with KS =
 // router_mfma_splits(T, H)).
@@ -190,8 +203,12 @@ hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st);
 // Streaming expert pass (batched decode): routed MXFP4 pass a and int8 shared
 // pass b of stage `mode` (kW13 / kW2) in one grid; n_rowblocks of each holds
 // its row groups (w13: I/64, w2: H/128).
+// queue: the pass's unit counter, zero before the launch (the tile-record
+// writers reset it).
 hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks,
-                         hipStream_t st);
+                         int* queue, hipStream_t st);
+// Tile records and queue reset for tiles built by launch_tiles_from_offsets.
+hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
 // Hand-off region of the single-launch layer, at a fixed offset at the start
 // of every workspace (zero on first use): per-block call counters, then two

@@ -15,6 +15,7 @@
 //                  earlier slots of the same expert -> its sorted position
 #include "device.h"
 #include "internal.h"
+#include "tilerec.h"
 
 namespace moe {
 
@@ -128,6 +129,16 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   k_perm_scatter<<<nblk, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_tile_records(Perm p, const float* slot_w) {
+  write_tile_records(p, slot_w, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+}
+
+hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t st) {
+  const int blocks = (p.max_tiles * kRecInts + 255) / 256;
+  k_tile_records<<<blocks < 1 ? 1 : blocks, 256, 0, st>>>(p, slot_w);
   return hipGetLastError();
 }
 

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(kDecExperts * 64) void k_router_dec(RouterArgs a) {
 // Writes the expert tile table from the per-expert counts (thread e < E of a
 // block holds count c and first position off of expert e): tiles of at most
 // tile_n consecutive sorted positions of one expert, in expert order.
-__device__ void block_write_tiles(int c, int off, int E, const Perm& p, int* scan_tmp) {
+// Returns the index of the thread's expert's first tile.
+__device__ int block_write_tiles(int c, int off, int E, const Perm& p, int* scan_tmp) {
   const int tid = threadIdx.x;
   const int nt = tid < E ? (c + p.tile_n - 1) / p.tile_n : 0;
   int total;
@@ -221,12 +222,13 @@ __device__ void block_write_tiles(int c, int off, int E, const Perm& p, int* sca
     }
   }
   if (tid == 0) *p.n_tiles = total;
+  return toff;
 }
 
 // Top-k of every token, one wave per token (4 per block); then the last
 // block to finish (an arrival count in the workspace, which it sets back to
-// zero) makes the stable counting sort of the T*k <= 512 slots and the
-// expert tile table. Stable ranks come from per-expert slot bitmasks: the
+// zero) makes the stable counting sort of the T*k <= 512 slots, the expert
+// tile table and the tile records of the streaming passes. Stable ranks come from per-expert slot bitmasks: the
 // rank of slot i among the slots of its expert is the number of set bits
 // below bit i of that expert's mask.
 constexpr int kTopkThreads = 256;
@@ -234,7 +236,7 @@ constexpr int kMaskWords = kSmallT * kMaxTopK / 64;  // 64-bit words per expert 
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p, int* arrivals) {
   __shared__ unsigned long long mask[kMaxExperts][kMaskWords];
-  __shared__ int first[kMaxExperts];
+  __shared__ int first[kMaxExperts], count[kMaxExperts], tile0[kMaxExperts];
   __shared__ int scan_tmp[kTopkThreads];
   __shared__ int is_last;
   const int tid = threadIdx.x;
@@ -264,12 +266,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   if (tid < a.E) {
     p.offsets[tid] = off;
     first[tid] = off;
+    count[tid] = c;
   }
   if (tid == 0) p.offsets[a.E] = total;
-  block_write_tiles(c, off, a.E, p, scan_tmp);
+  const int t0 = block_write_tiles(c, off, a.E, p, scan_tmp);
+  if (tid < a.E) tile0[tid] = t0;
   __syncthreads();
+  // every slot: its sorted position, and its column of its tile's record
+  // (the tile's first column also writes the record's head, its last column
+  // the repeats up to column 16)
   for (int i = tid; i < n; i += kTopkThreads) {
     const int e_i = a.ids[i];
+    const float wv = a.w[i];
     const int wi = i >> 6;
     int rank = __popcll(mask[e_i][wi] & ((1ull << (i & 63)) - 1ull));
     for (int w = 0; w < wi; ++w) rank += __popcll(mask[e_i][w]);
@@ -277,8 +285,26 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
     p.sorted_slots[pos] = i;
     p.slot_pos[i] = pos;
     p.sorted_tok[pos] = i / a.k;
+    const int tl = rank / p.tile_n, col = rank - tl * p.tile_n;
+    const int ncols = min(p.tile_n, count[e_i] - tl * p.tile_n);
+    int* rec = p.tile_rec + (size_t)(tile0[e_i] + tl) * kRecInts;
+    if (col == 0) {
+      rec[0] = e_i;
+      rec[1] = pos;
+      rec[2] = ncols;
+      rec[3] = 0;
+    }
+    for (int cc = col; cc < (col == ncols - 1 ? 16 : col + 1); ++cc) {
+      rec[4 + cc] = i / a.k;
+      rec[20 + cc] = i;
+      rec[36 + cc] = __float_as_int(wv);
+    }
   }
-  if (tid == 0) *arrivals = 0;  // ready for the next call
+  if (tid == 0) {
+    *arrivals = 0;  // ready for the next call
+    p.queues[0] = 0;
+    p.queues[1] = 0;
+  }
 }
 
 // The large-T learned router is in router_mfma.hip.

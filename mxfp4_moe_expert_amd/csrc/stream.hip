@@ -9,10 +9,12 @@
 // scales each slot by its routing weight, the shared w2 pass by the output
 // channel's int8 scale.
 //
-// Unit (4 waves) = one tile of at most 16 activation columns (an expert's
-// sorted positions, or consecutive tokens for the shared expert) x one row
-// group: w13 = 64 h columns (wave w: gate rows and up rows of columns
-// 16w .. 16w+15), w2 = 128 output rows (wave w: rows 32w .. 32w+31).
+// Unit (8 waves, one block per CU) = one tile of at most 16 activation
+// columns (an expert's sorted positions, or consecutive tokens for the
+// shared expert) x one row group: w13 = 128 h columns (wave w: gate rows and
+// up rows of columns 16w .. 16w+15), w2 = 256 output rows (wave w: rows
+// 32w .. 32w+31; rows past H in the last group are clamped on load and not
+// stored).
 //   - K runs in stages of 128. Lane (r = l%16, g = l/16) reads, per stage and
 //     row block, 32 K-values of row r: MXFP4, the range 128 st + 32g .. +32
 //     (16 bytes of E2M1 pairs, exactly one E8M0 group, whose byte the block
@@ -24,36 +26,32 @@
 //     columns in LDS. Any permutation of K shared by both operands leaves
 //     the sums unchanged.
 //
-// Persistent grid: only as many blocks as the chip holds at once, so no
-// block waits for the dispatcher and no block is spent on a tile that
-// routing left empty (the live tile count is read on the device). The
-// shared units go to the first blocks, the routed units to the rest, in
-// proportion to their weight bytes; each block takes a contiguous run of
-// units, row group fastest, so consecutive units mostly share a tile. Per
-// run of at most kMetaTiles tiles the block stages their metadata in LDS
-// (expert, first position, columns, each column's activation row and, for
-// the routed w2 pass, slot and routing weight); every later look-up is an
-// LDS read. Per unit:
+// Persistent grid with a work queue: only as many blocks as the chip holds
+// at once; block b starts with unit b and then takes units from the pass's
+// counter (one atomic per unit), so blocks that run faster take more units. (Two blocks sharing a CU do not
+// stream at the same rate, so any fixed split leaves a tail.) Queue order:
+// the shared units first, then the routed units, row group fastest; the
+// live routed tile count is read on the device. A block grabs its units two
+// ahead and loads their tile records (expert, first position, columns, the
+// columns' activation rows, slots and routing weights: one 208-byte row
+// written with the tile table) one ahead, so every look-up is ready before
+// it is needed. Per unit:
 //   - loads for stage st + D are issued right after stage st is consumed;
-//   - in the last D stages the loads are the next unit's first D stages,
-//     after its scales and epilogue scales: the weight stream never drains
-//     between units (after the block's last unit the same loads re-read
-//     that unit's last stages, a cache hit, so that no load is conditional
-//     and the compiler's waits count exactly);
-//   - epilogue, barrier, the next unit's scales to LDS (and its activation
-//     columns, if its tile differs), barrier.
+//   - in the last D stages the loads are the next unit's scales, activation
+//     columns and epilogue scales, its tile record's successor and the next
+//     grab, then its first D stages: the weight stream never drains between
+//     units (after the block's last unit the same loads re-read that unit's
+//     last stages, a cache hit, so that no load is conditional and the
+//     compiler's waits count exactly);
+//   - epilogue, barrier, the next unit's scales and columns to LDS, barrier.
 #include "device.h"
 #include "internal.h"
 #include "skinny.h"
 
 namespace moe {
 
-constexpr int kStreamThreads = 256;
-constexpr int kMetaTiles = 16;  // tiles whose metadata is staged at once
-// per tile: expert, first position, columns, unused, then per column its
-// activation row, its slot and its routing weight (bits)
-constexpr int kMetaInts = 4 + 3 * 16;
-constexpr int kMetaBytes = kMetaTiles * kMetaInts * 4;
+constexpr int kStreamThreads = 512;
+constexpr int kUnitRows = 256;  // weight rows per unit
 
 template <int FMT>
 struct StreamStage {
@@ -82,101 +80,88 @@ __device__ __forceinline__ bf16x8_t stream_frag(const StreamStage<FMT>& d, int k
   }
 }
 
-// Metadata of tiles t0 .. t0+nt-1 -> LDS (two rounds: tile entries, then the
-// per-column values that depend on them). Starts with a barrier: the
-// previous run's units may still be reading the region.
-template <int FMT, int MODE>
-__device__ __forceinline__ void stage_meta(const SkinnyArgs& p, int t0, int nt, int* meta) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  if (tid < nt) {
-    const int t = t0 + tid;
-    int e = 0, pos0, ncols;
-    if (p.routed) {
-      const int4 ti = p.tile_info[t];
-      e = ti.x;
-      pos0 = ti.y;
-      ncols = ti.z;
-    } else {
-      pos0 = t * p.tile_n;
-      ncols = min(p.tile_n, p.T - pos0);
-    }
-    meta[tid * kMetaInts + 0] = e;
-    meta[tid * kMetaInts + 1] = pos0;
-    meta[tid * kMetaInts + 2] = ncols;
-  }
-  __syncthreads();
-  if (tid < nt * 16) {  // nt * 16 <= kStreamThreads
-    int* m = meta + (tid >> 4) * kMetaInts;
-    const int c = tid & 15;
-    const int pos = m[1] + min(c, m[2] - 1);  // columns past the tile repeat its last one
-    m[4 + c] = p.act_row ? p.act_row[pos] : pos;
-    if (FMT == kFmtMx && MODE == kW2) {
-      const int slot = p.sorted_slots[pos];
-      m[20 + c] = slot;
-      m[36 + c] = __float_as_int(p.slot_w[slot]);
-    }
-  }
-  __syncthreads();
-}
+// A unit of the queue: its index, this lane's int of its tile record, and
+// the record's uniform fields.
+struct SUnit {
+  int idx, rec, e, pos0, ncols, rg;
+};
 
-// Units [u0, u1) of one run (their tiles' metadata at meta, tile t0 first).
-// NS scale pieces per thread travel in registers from the previous unit's
-// last stages (any beyond are loaded at the unit boundary); the activation
-// columns are loaded at the boundary when the tile changes, which a run of
-// consecutive units seldom does.
-template <int FMT, int MODE, int D, int NS>
-__device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, int t0, unsigned char* lds,
-                                           const int* meta) {
+// Units of one format while the queue hands them out: queue indices
+// [lo, hi). idx holds the current unit and the two grabbed after it
+// (uniform; idx[0] in range on entry). Returns with idx[0] the first unit
+// handed out that is not of this format (or past the end), followed by the
+// two grabbed after it. NS scale pieces and NA activation pieces per thread
+// travel in registers; any beyond are loaded at the unit boundary.
+template <int FMT, int MODE, int D, int NS, int NA>
+__device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi, int* queue, int (&idx)[3],
+                                            unsigned char* lds, int* sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K, S = K >> 7, n16 = K >> 3, row_bytes = 2 * K + 16;
   const int nrb = p.n_rowblocks;
   const int srow = K / 32;  // scale bytes per row (a multiple of 4)
-  unsigned char* lds_sc = lds + (size_t)p.tile_n * row_bytes;  // [128 rows][srow]
+  unsigned char* lds_sc = lds + (size_t)p.tile_n * row_bytes;  // [256 rows][srow]
   const bool sc16 = srow % 16 == 0;                            // rows of whole 16-byte pieces
-  const int nsc = FMT == kFmtMx ? 128 * srow / (sc16 ? 16 : 4) : 0;
-  // this lane's two block rows (of the unit's 128)
+  const int nsc = FMT == kFmtMx ? kUnitRows * srow / (sc16 ? 16 : 4) : 0;
+  // this lane's two block rows (of the unit's 256)
   const int brA = MODE == kW13 ? wave * 16 + r : wave * 32 + r;
-  const int brB = MODE == kW13 ? 64 + wave * 16 + r : wave * 32 + 16 + r;
+  const int brB = MODE == kW13 ? 128 + wave * 16 + r : wave * 32 + 16 + r;
 
-  struct Unit {
-    int e, pos0, ncols, rg, tl;
+  auto in_range = [&](int i) { return i >= lo && i < hi; };
+  auto local = [&](int i) { return min(max(i, lo), hi - 1) - lo; };  // clamped into the range
+  // the lane's int of unit i's tile record: routed tiles from the table,
+  // shared tiles (consecutive tokens) computed
+  auto rec_of = [&](int i) -> int {
+    const int tile = local(i) / nrb;
+    if constexpr (FMT == kFmtMx) {
+      return p.tile_rec[(size_t)tile * kRecInts + min(lane, kRecInts - 1)];
+    } else {
+      const int pos0 = tile * p.tile_n, ncols = min(p.tile_n, p.T - pos0);
+      return lane == 1 ? pos0 : lane == 2 ? ncols : (lane >= 4 && lane < 20) ? pos0 + min(lane - 4, ncols - 1) : 0;
+    }
   };
-  auto unit_at = [&](int u) {
-    Unit x;
-    const int tg = u / nrb;
-    x.rg = u - tg * nrb;
-    x.tl = tg - t0;
-    const int* m = meta + x.tl * kMetaInts;
-    x.e = __builtin_amdgcn_readfirstlane(m[0]);
-    x.pos0 = __builtin_amdgcn_readfirstlane(m[1]);
-    x.ncols = __builtin_amdgcn_readfirstlane(m[2]);
+  auto unit_of = [&](int i, int rec) {
+    SUnit x;
+    x.idx = i;
+    x.rec = rec;
+    x.e = __builtin_amdgcn_readlane(rec, 0);
+    x.pos0 = __builtin_amdgcn_readlane(rec, 1);
+    x.ncols = __builtin_amdgcn_readlane(rec, 2);
+    x.rg = local(i) % nrb;
     return x;
   };
-  auto grow = [&](const Unit& x, int br) {  // weight row of block row br
-    return MODE == kW13 ? (br < 64 ? x.rg * 64 + br : p.half + x.rg * 64 + (br - 64)) : x.rg * 128 + br;
+  auto grow = [&](const SUnit& x, int br) {  // weight row of block row br (clamped to the last)
+    return MODE == kW13 ? (br < 128 ? x.rg * 128 + br : p.half + x.rg * 128 + (br - 128))
+                        : min(x.rg * kUnitRows + br, p.rows - 1);
   };
-  auto wptr = [&](const Unit& x, int br) -> const uint8_t* {
+  auto wptr = [&](const SUnit& x, int br) -> const uint8_t* {
     if (FMT == kFmtMx) return p.wq + (long long)x.e * p.q_expert_stride + (size_t)grow(x, br) * (K / 2) + g * 16;
     return p.wq + (size_t)grow(x, br) * K + g * 16;
   };
-  auto sc_src = [&](const Unit& x, int i, int piece) {  // piece i of the unit's scales
+  auto sc_src = [&](const SUnit& x, int i, int piece) {  // piece i of the unit's scales
     const int row = (i * piece) / srow;
     return p.wsc + (long long)x.e * p.s_expert_stride + (size_t)grow(x, row) * srow + (i * piece - row * srow);
   };
-  auto act_src = [&](const Unit& x, int i) {  // piece i (16 bytes) of the unit's columns
+  // piece i (16 bytes) of the unit's columns; the row of its column from the
+  // tile record (a shuffle: every lane must take part) or, in divergent
+  // code, from memory
+  auto act_src = [&](const SUnit& x, int i) {
     const int c = min(i / n16, x.ncols - 1), o = i - (i / n16) * n16;
-    const int row = meta[x.tl * kMetaInts + 4 + c];
+    const int row = p.act_row ? __shfl(x.rec, 4 + c) : x.pos0 + c;
+    return reinterpret_cast<const u32x4_t*>(p.act + (size_t)row * p.act_ld) + o;
+  };
+  auto act_src_mem = [&](const SUnit& x, int i) {
+    const int c = i / n16, o = i - c * n16;
+    const int row = p.act_row ? p.act_row[x.pos0 + c] : x.pos0 + c;
     return reinterpret_cast<const u32x4_t*>(p.act + (size_t)row * p.act_ld) + o;
   };
   auto act_dst = [&](int i) { return reinterpret_cast<u32x4_t*>(lds + (i / n16) * row_bytes + (i % n16) * 16); };
 
-  // register-staged operands of a unit: scales and the int8 epilogue's row
-  // scales (every load unconditional: clamped indices)
-  u32x4_t sv[NS];
+  // register-staged operands of a unit: scales, activation pieces and the
+  // int8 epilogue's row scales (every load unconditional: clamped indices)
+  u32x4_t sv[NS], av[NA];
   float es[8] = {};
-  auto load_ops = [&](const Unit& x) __attribute__((always_inline)) {
+  auto load_ops = [&](const SUnit& x) __attribute__((always_inline)) {
     if constexpr (FMT == kFmtMx) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -187,18 +172,21 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
         sv[j] = *reinterpret_cast<const u32x4_t*>(src);
       }
     }
+    const int nact = x.ncols * n16;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) av[j] = *act_src(x, min(tid + j * kStreamThreads, nact - 1));
     if constexpr (FMT == kFmtI8) {
-      const int base = MODE == kW13 ? x.rg * 64 + wave * 16 + 4 * g : x.rg * 128 + wave * 32 + 4 * g;
+      const int base = MODE == kW13 ? x.rg * 128 + wave * 16 + 4 * g : x.rg * kUnitRows + wave * 32 + 4 * g;
       const int off = MODE == kW13 ? p.half : 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        es[i] = p.row_scale[base + i];
-        es[4 + i] = p.row_scale[base + off + i];
+        es[i] = p.row_scale[min(base + i, p.rows - 1)];
+        es[4 + i] = p.row_scale[min(base + off + i, p.rows - 1)];
       }
     }
     asm volatile("" ::: "memory");
   };
-  auto store_ops = [&](const Unit& x, bool new_tile) __attribute__((always_inline)) {
+  auto store_ops = [&](const SUnit& x) __attribute__((always_inline)) {
     if constexpr (FMT == kFmtMx) {
       if (sc16) {
 #pragma unroll
@@ -213,19 +201,13 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
           *reinterpret_cast<uint32_t*>(lds_sc + i * 4) = *reinterpret_cast<const uint32_t*>(sc_src(x, i, 4));
       }
     }
-    if (new_tile) {
-      const int nact = x.ncols * n16;
-      for (int i0 = 0; i0 < nact; i0 += 4 * kStreamThreads) {  // 4 pieces per thread in flight
-        u32x4_t v[4];
+    const int nact = x.ncols * n16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = *act_src(x, min(i0 + tid + j * kStreamThreads, nact - 1));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i0 + tid + j * kStreamThreads;
-          if (i < nact) *act_dst(i) = v[j];
-        }
-      }
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + j * kStreamThreads;
+      if (i < nact) *act_dst(i) = av[j];
     }
+    for (int i = tid + NA * kStreamThreads; i < nact; i += kStreamThreads) *act_dst(i) = *act_src_mem(x, i);
   };
 
   // MXFP4 stages come in pairs whose loads are issued back to back: the two
@@ -233,8 +215,10 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
   // whole line in two adjacent loads already)
   constexpr int P = (FMT == kFmtMx && D % 2 == 0) ? 2 : 1;
 
-  // first unit: its first D stages, then its operands
-  Unit cur = unit_at(u0);
+  // first unit: its record, its first D stages, its operands; the next
+  // unit's record
+  SUnit cur = unit_of(idx[0], rec_of(idx[0]));
+  int rec_nxt = rec_of(idx[1]);
   const uint8_t* qA = wptr(cur, brA);
   const uint8_t* qB = wptr(cur, brB);
   StreamStage<FMT> wA[D], wB[D];
@@ -244,11 +228,11 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
     stream_load<FMT>(qB, i, wB[i]);
   }
   load_ops(cur);
-  store_ops(cur, true);
+  store_ops(cur);
   __syncthreads();
 
   const bf16x8_t zero8 = {};
-  for (int u = u0;; ++u) {
+  for (;;) {
     f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     const bool live = r < cur.ncols;
     const unsigned char* bcol = lds + (live ? r : 0) * row_bytes + g * (FMT == kFmtMx ? 64 : 32);
@@ -281,9 +265,10 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
         for (int j = 0; j < P; ++j) stream_load<FMT>(qB, st0 + i + j + D, wB[i + j]);
       }
     }
-    // the last D stages request the next unit: operands, then first stages
-    const bool more = u + 1 < u1;
-    const Unit nxt = unit_at(more ? u + 1 : u);
+    // the last D stages request the next unit: operands, the record after
+    // it, the next grab, then its first stages
+    const bool more = in_range(idx[1]);
+    const SUnit nxt = unit_of(more ? idx[1] : idx[0], more ? rec_nxt : cur.rec);
     const uint8_t* nA = more ? wptr(nxt, brA) : qA;
     const uint8_t* nB = more ? wptr(nxt, brB) : qB;
     const int nst = more ? 0 : S - D;
@@ -291,6 +276,9 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) ec[i] = es[i];
     load_ops(nxt);
+    const int rec_after = rec_of(idx[2]);
+    int grabbed = 0;
+    if (tid == 0) grabbed = (int)gridDim.x + atomicAdd(queue, 1);
 #pragma unroll
     for (int i = 0; i < D; i += P) {
 #pragma unroll
@@ -302,9 +290,15 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
     }
 
     // epilogue: lane (r, g) holds rows 4g .. 4g+3 of each row block, column r
+    int slot = 0;
+    float wv = 0.0f;
+    if (FMT == kFmtMx && MODE == kW2) {  // every lane takes part in the shuffles
+      slot = __shfl(cur.rec, 20 + r);
+      wv = __int_as_float(__shfl(cur.rec, 36 + r));
+    }
     if (live) {
       if (MODE == kW13) {
-        const int hc = cur.rg * 64 + wave * 16 + 4 * g;
+        const int hc = cur.rg * 128 + wave * 16 + 4 * g;
         uint16_t h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -320,76 +314,61 @@ __device__ __forceinline__ void stream_run(const SkinnyArgs& p, int u0, int u1, 
         packed.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
         *reinterpret_cast<uint2*>(p.hout + (size_t)(cur.pos0 + r) * p.hout_ld + hc) = packed;
       } else {
-        const int n0 = cur.rg * 128 + wave * 32 + 4 * g;
+        const int n0 = cur.rg * kUnitRows + wave * 32 + 4 * g;
         float* dst;
         float4 ya, yb;
         if (FMT == kFmtMx) {
-          const int* m = meta + cur.tl * kMetaInts;
-          const float wv = __int_as_float(m[36 + r]);
           ya = make_float4(accA[0] * wv, accA[1] * wv, accA[2] * wv, accA[3] * wv);
           yb = make_float4(accB[0] * wv, accB[1] * wv, accB[2] * wv, accB[3] * wv);
-          dst = p.yout + (size_t)m[20 + r] * p.yout_ld;
+          dst = p.yout + (size_t)slot * p.yout_ld;
         } else {
           ya = make_float4(accA[0] * ec[0], accA[1] * ec[1], accA[2] * ec[2], accA[3] * ec[3]);
           yb = make_float4(accB[0] * ec[4], accB[1] * ec[5], accB[2] * ec[6], accB[3] * ec[7]);
           dst = p.yout + (size_t)(cur.pos0 + r) * p.yout_ld;
         }
-        *reinterpret_cast<float4*>(dst + n0) = ya;
-        *reinterpret_cast<float4*>(dst + n0 + 16) = yb;
+        if (n0 < p.rows) *reinterpret_cast<float4*>(dst + n0) = ya;  // rows come in whole blocks of 16
+        if (n0 + 16 < p.rows) *reinterpret_cast<float4*>(dst + n0 + 16) = yb;
       }
     }
-    if (!more) break;
-    __syncthreads();  // every wave is done with this unit's LDS
-    store_ops(nxt, nxt.tl != cur.tl);
+    // every wave is done with this unit's LDS; hand the grab to every thread
     __syncthreads();
+    if (tid == 0) sh[0] = grabbed;
+    if (more) store_ops(nxt);
+    __syncthreads();
+    idx[0] = idx[1];
+    idx[1] = idx[2];
+    idx[2] = __builtin_amdgcn_readfirstlane(sh[0]);
+    if (!more) break;
     cur = nxt;
+    rec_nxt = rec_after;
     qA = nA;
     qB = nB;
   }
   __builtin_amdgcn_s_waitcnt(0);  // the last unit's re-reads have landed before the registers are reused
 }
 
-// Units [u0, u1) of one pass, in runs of at most kMetaTiles tiles.
-template <int FMT, int MODE, int D, int NS>
-__device__ __forceinline__ void stream_units(const SkinnyArgs& p, long long u0, long long u1, unsigned char* lds) {
-  const int nrb = p.n_rowblocks;
-  int* meta = reinterpret_cast<int*>(lds + (size_t)p.tile_n * (2 * (size_t)p.K + 16) +
-                                     (FMT == kFmtMx ? 128 * (size_t)(p.K / 32) : 0));
-  for (long long s0 = u0; s0 < u1;) {
-    const int t0 = (int)(s0 / nrb);
-    const long long s1 = min(u1, (long long)(t0 + kMetaTiles) * nrb);
-    const int nt = (int)((s1 - 1) / nrb) - t0 + 1;
-    stage_meta<FMT, MODE>(p, t0, nt, meta);
-    stream_run<FMT, MODE, D, NS>(p, (int)s0, (int)s1, t0, lds, meta);
-    s0 = s1;
-  }
-}
-
 // Pass b (int8 shared) and pass a (MXFP4 routed) of the same stage in one
-// persistent grid: blocks [0, gb) take the shared units, the rest the routed
-// ones; gb splits the grid in proportion to the weight bytes of the two
-// (per row: K int8 bytes; K/2 code bytes + K/32 scale bytes).
+// persistent grid fed by one queue: indices [0, nb) are the shared units,
+// [nb, nb + na) the routed ones (row group fastest in both).
 template <int MODE, int DA, int DB>
-__global__ __launch_bounds__(kStreamThreads) void k_stream(SkinnyArgs a, int has_a, SkinnyArgs b, int has_b) {
+__global__ __launch_bounds__(kStreamThreads) void k_stream(SkinnyArgs a, int has_a, SkinnyArgs b, int has_b,
+                                                           int* queue) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const long long a_tiles = has_a ? (a.routed ? min(*a.n_tiles, a.n_tiles_grid) : a.n_tiles_grid) : 0;
-  const long long na = a_tiles * a.n_rowblocks;
-  const long long nb = has_b ? (long long)b.n_tiles_grid * b.n_rowblocks : 0;
-  const long long G = gridDim.x, x = blockIdx.x;
-  long long gb = 0;
-  if (nb > 0 && na == 0) {
-    gb = G;
-  } else if (nb > 0) {
-    const long long cb = nb * 32, tot = cb + na * 17;
-    gb = max(1LL, min(G - 1, (G * cb + tot / 2) / tot));
-  }
+  __shared__ int sh[4];
+  const int na = has_a ? (a.routed ? min(*a.n_tiles, a.n_tiles_grid) : a.n_tiles_grid) * a.n_rowblocks : 0;
+  const int nb = has_b ? b.n_tiles_grid * b.n_rowblocks : 0;
+  // the block's first unit is its own index; the queue hands out the rest,
+  // from gridDim.x on
+  const int G = gridDim.x;
+  if (threadIdx.x == 0) sh[0] = G + atomicAdd(queue, 2);
+  __syncthreads();
+  const int next = __builtin_amdgcn_readfirstlane(sh[0]);
+  int idx[3] = {(int)blockIdx.x, next, next + 1};
   constexpr int NSA = MODE == kW13 ? 4 : 2;  // all scale pieces of K = 4096 / 2048
-  if (x < gb) {
-    stream_units<kFmtI8, MODE, DB, 1>(b, nb * x / gb, nb * (x + 1) / gb, lds);
-  } else {
-    const long long m = G - gb, i = x - gb;
-    stream_units<kFmtMx, MODE, DA, NSA>(a, na * i / m, na * (i + 1) / m, lds);
-  }
+  constexpr int NAA = MODE == kW13 ? 6 : 3;  // 6 columns of K = 4096 / 2048
+  constexpr int NAB = MODE == kW13 ? 8 : 4;  // 8 columns
+  if (idx[0] < nb) stream_loop<kFmtI8, MODE, DB, 1, NAB>(b, 0, nb, queue, idx, lds, sh);
+  if (idx[0] >= nb && idx[0] < nb + na) stream_loop<kFmtMx, MODE, DA, NSA, NAA>(a, nb, nb + na, queue, idx, lds, sh);
 }
 
 // Blocks of kernel k with lds bytes that the current device holds at once
@@ -419,20 +398,20 @@ static int stream_resident(const void* k, size_t lds) {
 }
 
 template <int MODE, int DA, int DB>
-static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks,
+static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks, int* queue,
                                   hipStream_t st) {
   const long long nblk = (long long)a_blocks + b_blocks;
   if (nblk <= 0) return hipSuccess;
-  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  if ((a_blocks > 0 && (a.tile_n > 16 || a.tile_n < 1)) || (b_blocks > 0 && (b.tile_n > 16 || b.tile_n < 1)))
+  if (nblk > 0x3fffffffLL || !queue) return hipErrorInvalidValue;
+  if ((a_blocks > 0 && (a.tile_n > 16 || a.tile_n < 1 || !a.tile_rec)) ||
+      (b_blocks > 0 && (b.tile_n > 16 || b.tile_n < 1)))
     return hipErrorInvalidValue;
   size_t lds = 0;
-  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + 128 * (size_t)(a.K / 32);
+  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / 32);
   if (b_blocks > 0) {
     const size_t lb = (size_t)b.tile_n * (2 * (size_t)b.K + 16);
     lds = lb > lds ? lb : lds;
   }
-  lds += kMetaBytes;
   auto kern = &k_stream<MODE, DA, DB>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -443,16 +422,17 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
   const int res = stream_resident(reinterpret_cast<const void*>(kern), lds);
   if (res <= 0) return hipErrorInvalidValue;
   const long long grid = nblk < res ? nblk : res;
-  kern<<<(unsigned)grid, kStreamThreads, lds, st>>>(a, a_blocks > 0 ? 1 : 0, b, b_blocks > 0 ? 1 : 0);
+  kern<<<(unsigned)grid, kStreamThreads, lds, st>>>(a, a_blocks > 0 ? 1 : 0, b, b_blocks > 0 ? 1 : 0, queue);
   return hipGetLastError();
 }
 
-// Row groups: w13 I/64 (64 h columns each), w2 H/128 (128 rows each); the
-// caller sets n_rowblocks to that count, and a_blocks / b_blocks to the
-// most units each pass can have (tiles x row groups). Stage depth D: 8
+// Row groups: w13 I/128 (128 h columns each), w2 ceil(H/256) (256 rows
+// each); the caller sets n_rowblocks to that count, rows to the pass's
+// weight rows, and a_blocks / b_blocks to the most units each pass can have
+// (tiles x row groups). Stage depth D: 8
 // (MXFP4) and 4 (int8) when the stage count is a multiple of 8, else the
 // largest that divides it of 4 and 1.
-hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks,
+hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks, int* queue,
                          hipStream_t st) {
   SkinnyArgs bb{};
   if (b) bb = *b; else b_blocks = 0;
@@ -460,13 +440,13 @@ hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const Skin
   if (K % 128 || (a_blocks > 0 && b_blocks > 0 && a.K != bb.K)) return hipErrorInvalidValue;
   const int S = K / 128;
   if (mode == kW13) {
-    if (S % 8 == 0) return launch_stream_t<kW13, 8, 4>(a, a_blocks, bb, b_blocks, st);
-    if (S % 4 == 0) return launch_stream_t<kW13, 4, 4>(a, a_blocks, bb, b_blocks, st);
-    return launch_stream_t<kW13, 1, 1>(a, a_blocks, bb, b_blocks, st);
+    if (S % 8 == 0) return launch_stream_t<kW13, 8, 4>(a, a_blocks, bb, b_blocks, queue, st);
+    if (S % 4 == 0) return launch_stream_t<kW13, 4, 4>(a, a_blocks, bb, b_blocks, queue, st);
+    return launch_stream_t<kW13, 1, 1>(a, a_blocks, bb, b_blocks, queue, st);
   }
-  if (S % 8 == 0) return launch_stream_t<kW2, 8, 4>(a, a_blocks, bb, b_blocks, st);
-  if (S % 4 == 0) return launch_stream_t<kW2, 4, 4>(a, a_blocks, bb, b_blocks, st);
-  return launch_stream_t<kW2, 1, 1>(a, a_blocks, bb, b_blocks, st);
+  if (S % 8 == 0) return launch_stream_t<kW2, 8, 4>(a, a_blocks, bb, b_blocks, queue, st);
+  if (S % 4 == 0) return launch_stream_t<kW2, 4, 4>(a, a_blocks, bb, b_blocks, queue, st);
+  return launch_stream_t<kW2, 1, 1>(a, a_blocks, bb, b_blocks, queue, st);
 }
 
 }  // namespace moe
