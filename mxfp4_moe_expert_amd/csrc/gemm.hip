@@ -145,12 +145,13 @@ __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x
 }
 
 // The K loop and epilogue of one block over its first MB*16 positions.
-template <int FMT, int MODE, int MB>
+template <int FMT, int MODE, int MB, class StoreScales>
 __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, const unsigned char* lds_s,
                                           const uint32_t (&qoff)[kRB], const uint32_t (&soff)[kRB],
                                           const uint16_t* asrc, u32x4_t* adst0, u32x4_t* adst1,
                                           const unsigned char* abase0, const unsigned char* abase1, int nst,
-                                          int ncols, int pos0, int nt, int wn, int g, int r) {
+                                          int ncols, int pos0, int nt, int wn, int g, int r,
+                                          const StoreScales& store_scales) {
   f32x4_t acc[kRB][MB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b)
@@ -167,6 +168,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
   const int last = nst - 1;
   gemm_load_w(qe, qoff, 0, w0);
   av0.load(asrc, 0);
+  store_scales();  // the block's scales, requested before these first loads
   av0.store(adst0);
   av1.load(asrc, min(1, last));
   av0.load(asrc, min(2, last));
@@ -296,23 +298,44 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     const int lrow = MODE == kGemmW13 ? (b == 0 ? 0 : 128) + wn * 16 + r : wn * 32 + b * 16 + r;
     soff[b] = (uint32_t)lrow * srow + g;
   }
-  if (FMT == kFmtMx) {
-    // the block's scales: two runs of 128 rows (w13: gate rows, up rows;
-    // w2: the tile's 256 rows), K/32 bytes per row, in 16-byte pieces
-    const uint8_t* se = p.wsc + (long long)e * p.s_expert_stride;
-    const int rowlen = K / 32, npieces = 2 * 128 * rowlen / 16;
-    for (int i = tid; i < npieces; i += kGemmThreads) {
-      const int run = i / (npieces / 2), o = (i - run * (npieces / 2)) * 16;
-      const int grow0 = MODE == kGemmW13 ? (run == 0 ? 0 : p.half) + nt * (kBN / 2) : nt * kBN + run * 128;
-      const uint4 v = *reinterpret_cast<const uint4*>(se + (size_t)grow0 * rowlen + o);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // the block's scales: two runs of 128 rows (w13: gate rows, up rows; w2:
+  // the tile's 256 rows), K/32 bytes per row, in 16-byte pieces. Up to
+  // kScalePieces per thread are requested now, ahead of the pipeline's
+  // first loads, and written to LDS after those are issued (any more are
+  // copied then, for K above 4096).
+  constexpr int kScalePieces = 4;
+  const uint8_t* se = p.wsc + (long long)e * p.s_expert_stride;
+  const int rowlen = K / 32, npieces = FMT == kFmtMx ? 2 * 128 * rowlen / 16 : 0;
+  const int hpieces = npieces > 1 ? npieces / 2 : 1;  // pieces per run of 128 rows
+  auto piece_src = [&](int i) {
+    const int run = i / hpieces, o = (i - run * hpieces) * 16;
+    const int grow0 = MODE == kGemmW13 ? (run == 0 ? 0 : p.half) + nt * (kBN / 2) : nt * kBN + run * 128;
+    return reinterpret_cast<const uint4*>(se + (size_t)grow0 * rowlen + o);
+  };
+  auto piece_store = [&](int i, const uint4& v) {
+    const int run = i / hpieces, o = (i - run * hpieces) * 16;
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int oq = o + 4 * q, row = oq / rowlen, col = oq - row * rowlen;
-        *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[q];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int oq = o + 4 * q, row = oq / rowlen, col = oq - row * rowlen;
+      *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[q];
     }
+  };
+  uint4 scv[kScalePieces];
+  if (FMT == kFmtMx) {
+#pragma unroll
+    for (int j = 0; j < kScalePieces; ++j) scv[j] = *piece_src(min(tid + j * kGemmThreads, npieces - 1));
   }
+  auto store_scales = [&]() __attribute__((always_inline)) {
+    if (FMT == kFmtMx) {
+#pragma unroll
+      for (int j = 0; j < kScalePieces; ++j) {
+        const int i = tid + j * kGemmThreads;
+        if (i < npieces) piece_store(i, scv[j]);
+      }
+      for (int i = tid + kScalePieces * kGemmThreads; i < npieces; i += kGemmThreads) piece_store(i, *piece_src(i));
+    }
+  };
   // this thread's activation loads: token row 16*wave + lane%16, quarter
   // lane/16 of the row's stage (so that a wave's LDS stores are contiguous).
   // Rows past the tile re-read its first row: their results are never stored.
@@ -335,19 +358,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   switch ((ncols + 31) >> 5) {
     case 1:
       gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r);
+                              g, r, store_scales);
       break;
     case 2:
       gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r);
+                              g, r, store_scales);
       break;
     case 3:
       gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r);
+                              g, r, store_scales);
       break;
     default:
       gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                wn, g, r);
+                                wn, g, r, store_scales);
   }
 }
 
