@@ -12,7 +12,8 @@
 //   k_perm_scan    one block: per-expert prefix over blocks, expert offsets,
 //                  the tile table
 //   k_perm_scatter per block, the stable rank of each slot among the block's
-//                  earlier slots of the same expert -> its sorted position
+//                  earlier slots of the same expert (wave ballots) -> its
+//                  sorted position
 #include "device.h"
 #include "internal.h"
 #include "tilerec.h"
@@ -52,50 +53,76 @@ __global__ __launch_bounds__(256) void k_perm_count(PermArgs a) {
   if (tid < a.E) a.blk_counts[(size_t)b * a.E + tid] = hist[tid];
 }
 
+// Thread e: the exclusive prefix of expert e's counts over the blocks (its
+// count in blocks before b), loaded in batches of independent loads; the
+// expert offsets and the tile table. The scatter adds the offsets.
 __global__ __launch_bounds__(256) void k_perm_scan(PermArgs a, int nblk) {
   __shared__ int tmp[256];
   const int tid = threadIdx.x;
+  constexpr int kBatch = 16;
   int running = 0;
   if (tid < a.E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = a.blk_counts[(size_t)b * a.E + tid];
-      a.blk_counts[(size_t)b * a.E + tid] = running;
-      running += c;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) c[j] = a.blk_counts[(size_t)min(b0 + j, nblk - 1) * a.E + tid];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (b0 + j < nblk) {
+          a.blk_counts[(size_t)(b0 + j) * a.E + tid] = running;
+          running += c[j];
+        }
+      }
     }
   }
   int total;
   const int off = block_exclusive_scan(tid < a.E ? running : 0, tmp, &total);
-  if (tid < a.E) {
-    a.p.offsets[tid] = off;
-    for (int b = 0; b < nblk; ++b) a.blk_counts[(size_t)b * a.E + tid] += off;
-  }
+  if (tid < a.E) a.p.offsets[tid] = off;
   if (tid == 0) a.p.offsets[a.E] = total;
   write_tiles(running, off, a.E, a.p, tmp);
 }
 
+// Per block of kPermBlock slots, in chunks of 256 (4 waves): each slot's
+// rank among the earlier slots of its expert. Within a wave, the lanes with
+// the same expert come from 8 ballots (one per bit of the id) and the rank
+// is the number of such lanes below; the waves then take their turns, in
+// order, adding their group sizes to the block's running count per expert.
+// Sorted position = expert offset + the expert's count in earlier blocks +
+// the running count + the rank.
 __global__ __launch_bounds__(256) void k_perm_scatter(PermArgs a) {
-  __shared__ int chunk[256];
   __shared__ int seen[kMaxExperts];
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tid = threadIdx.x, b = blockIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.T * a.k;
-  seen[tid] = 0;
+  seen[tid] = 0;  // 256 threads, kMaxExperts = 256
   const int beg = b * kPermBlock, end = min(n, beg + kPermBlock);
+  const unsigned long long below = (1ull << lane) - 1ull;
   for (int c0 = beg; c0 < end; c0 += 256) {
     const int i = c0 + tid;
     const int e = i < end ? a.ids[i] : -1;
-    chunk[tid] = e;
+    unsigned long long m = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = ((e >> bit) & 1) != 0;
+      const unsigned long long bs = __ballot(set);
+      m &= set ? bs : ~bs;
+    }
+    const int rank = __popcll(m & below);
+    const int group = __popcll(m);
+    int base = 0;
+    for (int w = 0; w < 4; ++w) {
+      __syncthreads();
+      if (wave == w && e >= 0) {
+        base = seen[e];  // every lane of the group reads before its first lane adds
+        if (rank == 0) seen[e] = base + group;
+      }
+    }
     __syncthreads();
     if (e >= 0) {
-      int rank = 0;
-      for (int j = 0; j < tid; ++j) rank += (chunk[j] == e);
-      const int pos = a.blk_counts[(size_t)b * a.E + e] + seen[e] + rank;
+      const int pos = a.p.offsets[e] + a.blk_counts[(size_t)b * a.E + e] + base + rank;
       a.p.sorted_slots[pos] = i;
       a.p.slot_pos[i] = pos;
       a.p.sorted_tok[pos] = i / a.k;
     }
-    __syncthreads();
-    if (e >= 0) atomicAdd(&seen[e], 1);
-    __syncthreads();
   }
 }
 
