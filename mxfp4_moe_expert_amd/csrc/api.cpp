@@ -41,6 +41,16 @@ int fit_tile(int want, int K) {
   return tn;
 }
 
+// Tokens per shared-expert tile of the streaming passes: each tile streams
+// the whole shared expert, so wide tiles read it fewer times; up to 16 (one
+// MFMA's columns), with the tile's bf16 rows at most 140 KB of LDS (the
+// streaming blocks run one per CU).
+int shared_stream_tile(int T, int K) {
+  int tn = T < 16 ? T : 16;
+  while (tn > 1 && (size_t)tn * (2 * (size_t)K + 16) > 140 * 1024) --tn;
+  return tn;
+}
+
 // Columns per routed expert tile at decode sizes: a few times the expected
 // tokens per expert (1.5 at 64 tokens, 6 of 256 experts), so that an expert
 // seldom needs a second tile, which would stream its weights again, while
@@ -666,12 +676,9 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;
     g13.n_rowblocks = h13.n_rowblocks = I / 128;
     g2.n_rowblocks = h2.n_rowblocks = (H + 255) / 256;
-    // shared-expert tiles of 8 tokens: each tile streams the whole shared
-    // expert, so wider tiles read it fewer times (measured best: 16 would
-    // set the launch's LDS, and with it the routed blocks' occupancy)
-    h13.tile_n = fit_tile(T < 8 ? T : 8, H);
+    h13.tile_n = shared_stream_tile(T, H);
     h13.n_tiles_grid = (T + h13.tile_n - 1) / h13.tile_n;
-    h2.tile_n = fit_tile(T < 8 ? T : 8, I);
+    h2.tile_n = shared_stream_tile(T, I);
     h2.n_tiles_grid = (T + h2.tile_n - 1) / h2.tile_n;
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
       return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks,
