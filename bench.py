@@ -45,8 +45,9 @@ DOMINANT = {
     "decode_t1": ("moe::k_layer_small<4, 2, 1, 6>",
                   "the whole layer in one launch of one block per CU: router, shared int8 w13, top-6, routed "
                   "MXFP4 w13 + clamped SwiGLU, routed MXFP4 + shared int8 w2 and the weighted combine", "layer"),
-    "decode_t64": ("moe::k_stream<0, 8, 4>",
-                   "routed MXFP4 w13 + shared int8 w13 streaming passes with the clamped SwiGLU", "w13"),
+    "decode_t64": ("moe::k_stream_fused<8, 4>",
+                   "both expert stages in one launch: routed MXFP4 + shared int8 w13 with the clamped SwiGLU, "
+                   "then routed MXFP4 (x routing weight) + shared int8 w2", "experts"),
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
     "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
 }
@@ -121,9 +122,13 @@ def algorithmic(wl, ids_np):
     slots = T * k
     layer_bytes = Dm * (w13_exp + w2_exp) + shared + router + T * H * 2 + T * H * 2
     w13_bytes = Dm * w13_exp + slots * H * 2 + slots * I * 2  # weights + gathered x + h out
+    # both expert stages: weights + gathered x + h out and back in + weighted y out (fp32)
+    experts_bytes = (Dm * (w13_exp + w2_exp) + shared + (slots + T) * H * 2 + 2 * (slots + T) * I * 2
+                     + (slots + T) * H * 4)
     flops_w13 = 2.0 * slots * H * 2 * I
     flops = 2.0 * slots * (H * 2 * I + I * H) + 2.0 * T * (H * 2 * I + I * H)
     return dict(distinct_experts=Dm, layer_bytes=layer_bytes, w13_bytes=w13_bytes, w13_flops=flops_w13,
+                experts_bytes=experts_bytes,
                 layer_flops=flops, router_flops=2.0 * T * E * H)
 
 

@@ -18,7 +18,7 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, tile_rec, blk_counts, hbuf, hs, ybuf,
+  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, tile_rec, done, blk_counts, hbuf, hs, ybuf,
       zbuf, total;
   int tile_n, max_tiles;
 };
@@ -100,6 +100,7 @@ Layout layout(const moe_config& c, int T) {
   L.sorted_tok = take(slots * 4);
   L.tile_info = take((size_t)L.max_tiles * 16);
   L.tile_rec = take((size_t)L.max_tiles * kRecInts * 4);
+  L.done = take((size_t)(L.max_tiles + kSmallT) * 4);
   L.blk_counts = take(nblk * E * 4);
   L.hbuf = take(slots * I * 2);
   L.hs = take((size_t)T * I * 2);
@@ -146,6 +147,7 @@ Perm perm_of(void* ws, const Layout& L, int32_t* offsets, int32_t* sorted, int32
   p.n_tiles = at<int32_t>(ws, L.counters);
   p.tile_rec = at<int32_t>(ws, L.tile_rec);
   p.queues = at<int32_t>(ws, L.counters) + kQueueInts;
+  p.done = at<int32_t>(ws, L.done);
   p.tile_n = L.tile_n;
   p.max_tiles = L.max_tiles;
   return p;
@@ -676,20 +678,28 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     SkinnyArgs g13 = r13, g2 = r2, h13 = s13w, h2 = s2;
     g13.n_rowblocks = h13.n_rowblocks = I / 128;
     g2.n_rowblocks = h2.n_rowblocks = (H + 255) / 256;
-    h13.tile_n = shared_stream_tile(T, H);
-    h13.n_tiles_grid = (T + h13.tile_n - 1) / h13.tile_n;
-    h2.tile_n = shared_stream_tile(T, I);
-    h2.n_tiles_grid = (T + h2.tile_n - 1) / h2.tile_n;
-    rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
-      return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks,
-                           p.queues, st);
-    }));
-    if (rc) return rc;
-    rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] {
-      return launch_stream(kW2, g2, p.max_tiles * g2.n_rowblocks, &h2, h2.n_tiles_grid * h2.n_rowblocks,
-                           p.queues + 1, st);
-    }));
-    if (rc) return rc;
+    // the same shared tiles for both stages (one launch needs them alike)
+    h13.tile_n = h2.tile_n = std::min(shared_stream_tile(T, H), shared_stream_tile(T, I));
+    h13.n_tiles_grid = h2.n_tiles_grid = (T + h13.tile_n - 1) / h13.tile_n;
+    if (H % 1024 == 0 && I % 1024 == 0) {  // both stages in one launch
+      rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+        return launch_stream_fused(g13, h13, g2, h2, p.max_tiles * g13.n_rowblocks,
+                                   h13.n_tiles_grid * h13.n_rowblocks, p.max_tiles * g2.n_rowblocks,
+                                   h2.n_tiles_grid * h2.n_rowblocks, p.queues, p.done, p.done + p.max_tiles, st);
+      }));
+      if (rc) return rc;
+    } else {
+      rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] {
+        return launch_stream(kW13, g13, p.max_tiles * g13.n_rowblocks, &h13, h13.n_tiles_grid * h13.n_rowblocks,
+                             p.queues, st);
+      }));
+      if (rc) return rc;
+      rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] {
+        return launch_stream(kW2, g2, p.max_tiles * g2.n_rowblocks, &h2, h2.n_tiles_grid * h2.n_rowblocks,
+                             p.queues + 1, st);
+      }));
+      if (rc) return rc;
+    }
   } else {
     // route | permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine
     if (hash) {

@@ -26,6 +26,7 @@ struct Perm {
   int32_t* n_tiles;       // [1] tiles in use
   int32_t* tile_rec;      // [max_tiles][kRecInts] tile records (decode sizes)
   int32_t* queues;        // [2] unit counters of the streaming w13 and w2 passes
+  int32_t* done;          // [max_tiles + kSmallT] finished w13 units per routed, then shared, tile
   int tile_n;
   int max_tiles;
 };
@@ -207,6 +208,12 @@ hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st);
 // writers reset it).
 hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks,
                          int* queue, hipStream_t st);
+// Both decode stages in one launch (H and I multiples of 1024, the shared
+// tiles of w13 and w2 alike): done_r / done_s count the finished w13 units of
+// each routed / shared tile and must be zero before the launch.
+hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, const SkinnyArgs& a2,
+                               const SkinnyArgs& b2, int a_blocks13, int b_blocks13, int a_blocks2, int b_blocks2,
+                               int* queue, int* done_r, int* done_s, hipStream_t st);
 // Tile records and queue reset for tiles built by launch_tiles_from_offsets.
 hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);

@@ -228,7 +228,8 @@ __device__ int block_write_tiles(int c, int off, int E, const Perm& p, int* scan
 // Top-k of every token, one wave per token (4 per block); then the last
 // block to finish (an arrival count in the workspace, which it sets back to
 // zero) makes the stable counting sort of the T*k <= 512 slots, the expert
-// tile table and the tile records of the streaming passes. Stable ranks come from per-expert slot bitmasks: the
+// tile table and the tile records of the streaming passes, and zeroes their
+// counters. Stable ranks come from per-expert slot bitmasks: the
 // rank of slot i among the slots of its expert is the number of set bits
 // below bit i of that expert's mask.
 constexpr int kTopkThreads = 256;
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
       rec[36 + cc] = __float_as_int(wv);
     }
   }
+  for (int i = tid; i < p.max_tiles + kSmallT; i += kTopkThreads) p.done[i] = 0;
   if (tid == 0) {
     *arrivals = 0;  // ready for the next call
     p.queues[0] = 0;

@@ -92,9 +92,17 @@ struct SUnit {
 // handed out that is not of this format (or past the end), followed by the
 // two grabbed after it. NS scale pieces and NA activation pieces per thread
 // travel in registers; any beyond are loaded at the unit boundary.
-template <int FMT, int MODE, int D, int NS, int NA>
+//
+// FUSED (w13 and w2 in one launch): a w13 unit writes its h with coherent
+// (write-through) stores and counts itself in done[its tile] once they are
+// complete (the count is issued at the block's next unit boundary, after
+// every wave has waited for its stores); a w2 unit reads its h with
+// coherent loads, after done[its tile] has reached done_target (the tile's
+// w13 units). The count of the unit after next is polled one unit ahead.
+template <int FMT, int MODE, int D, int NS, int NA, bool FUSED = false>
 __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi, int* queue, int (&idx)[3],
-                                            unsigned char* lds, int* sh) {
+                                            unsigned char* lds, int* sh, int* done = nullptr,
+                                            int done_target = 0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K, S = K >> 7, n16 = K >> 3, row_bytes = 2 * K + 16;
@@ -156,6 +164,28 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     return reinterpret_cast<const u32x4_t*>(p.act + (size_t)row * p.act_ld) + o;
   };
   auto act_dst = [&](int i) { return reinterpret_cast<u32x4_t*>(lds + (i / n16) * row_bytes + (i % n16) * 16); };
+  auto act_load = [&](const u32x4_t* src) -> u32x4_t {
+    if constexpr (FUSED && MODE == kW2) return load_agent_u32x4(src);
+    else return *src;
+  };
+  // FUSED: tiles of units, their published counts, and the wait for a w2
+  // unit's tile (bounded; every w13 unit is grabbed before any w2 unit and
+  // its block finishes it without waiting, so the count always arrives)
+  auto tile_of = [&](int i) { return local(i) / nrb; };
+  auto poll = [&](int i) -> int {
+    if constexpr (FUSED && MODE == kW2) return (int)load_agent(reinterpret_cast<const uint32_t*>(done + tile_of(i)));
+    else return 0;
+  };
+  auto wait_tile = [&](int i, int seen) __attribute__((always_inline)) {
+    if constexpr (FUSED && MODE == kW2) {
+      int v = __builtin_amdgcn_readfirstlane(seen);
+      for (int it = 0; v < done_target && it < (1 << 22); ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        v = __builtin_amdgcn_readfirstlane(poll(i));
+      }
+    }
+  };
+  int pub = -1;  // FUSED w13: tile of the unit whose completion is counted at the next boundary
 
   // register-staged operands of a unit: scales, activation pieces and the
   // int8 epilogue's row scales (every load unconditional: clamped indices)
@@ -174,7 +204,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     }
     const int nact = x.ncols * n16;
 #pragma unroll
-    for (int j = 0; j < NA; ++j) av[j] = *act_src(x, min(tid + j * kStreamThreads, nact - 1));
+    for (int j = 0; j < NA; ++j) av[j] = act_load(act_src(x, min(tid + j * kStreamThreads, nact - 1)));
     if constexpr (FMT == kFmtI8) {
       const int base = MODE == kW13 ? x.rg * 128 + wave * 16 + 4 * g : x.rg * kUnitRows + wave * 32 + 4 * g;
       const int off = MODE == kW13 ? p.half : 16;
@@ -207,7 +237,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
       const int i = tid + j * kStreamThreads;
       if (i < nact) *act_dst(i) = av[j];
     }
-    for (int i = tid + NA * kStreamThreads; i < nact; i += kStreamThreads) *act_dst(i) = *act_src_mem(x, i);
+    for (int i = tid + NA * kStreamThreads; i < nact; i += kStreamThreads) *act_dst(i) = act_load(act_src_mem(x, i));
   };
 
   // MXFP4 stages come in pairs whose loads are issued back to back: the two
@@ -227,9 +257,17 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     stream_load<FMT>(qA, i, wA[i]);
     stream_load<FMT>(qB, i, wB[i]);
   }
+  wait_tile(idx[0], poll(idx[0]));
+  int poll_nxt = poll(idx[1]);
   load_ops(cur);
   store_ops(cur);
   __syncthreads();
+  // FUSED w13: at a unit's last stages a wave's h stores of the unit before
+  // are complete once at most the last main-loop iteration's loads are
+  // outstanding (vmcnt(16): 8 MXFP4 stages x 2 loads, or 4 int8 stages x 4),
+  // if the main loop ran at all; else once nothing is outstanding
+  static_assert(!FUSED || MODE != kW13 || (FMT == kFmtMx ? 2 * D : 4 * D) == 16, "vmcnt of the h-store wait");
+  const bool deep = S >= 2 * D;
 
   const bf16x8_t zero8 = {};
   for (;;) {
@@ -275,8 +313,15 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     float ec[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) ec[i] = es[i];
+    if constexpr (FUSED && MODE == kW13) {
+      // vmcnt(16) / vmcnt(0), expcnt and lgkmcnt not waited for
+      if (deep) __builtin_amdgcn_s_waitcnt((1 << 14) | (15 << 8) | (7 << 4));
+      else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
+    }
+    if (more) wait_tile(idx[1], poll_nxt);
     load_ops(nxt);
     const int rec_after = rec_of(idx[2]);
+    const int poll_after = poll(idx[2]);
     int grabbed = 0;
     if (tid == 0) grabbed = (int)gridDim.x + atomicAdd(queue, 1);
 #pragma unroll
@@ -312,7 +357,13 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
         uint2 packed;
         packed.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
         packed.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        *reinterpret_cast<uint2*>(p.hout + (size_t)(cur.pos0 + r) * p.hout_ld + hc) = packed;
+        uint16_t* hdst = p.hout + (size_t)(cur.pos0 + r) * p.hout_ld + hc;
+        if constexpr (FUSED) {
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(hdst), (uint64_t)packed.x | ((uint64_t)packed.y << 32),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          *reinterpret_cast<uint2*>(hdst) = packed;
+        }
       } else {
         const int n0 = cur.rg * kUnitRows + wave * 32 + 4 * g;
         float* dst;
@@ -332,6 +383,10 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     }
     // every wave is done with this unit's LDS; hand the grab to every thread
     __syncthreads();
+    if constexpr (FUSED && MODE == kW13) {  // every wave has waited for the unit before's h stores
+      if (tid == 0 && pub >= 0) atomicAdd(done + pub, 1);
+      pub = tile_of(cur.idx);
+    }
     if (tid == 0) sh[0] = grabbed;
     if (more) store_ops(nxt);
     __syncthreads();
@@ -341,10 +396,15 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     if (!more) break;
     cur = nxt;
     rec_nxt = rec_after;
+    poll_nxt = poll_after;
     qA = nA;
     qB = nB;
   }
   __builtin_amdgcn_s_waitcnt(0);  // the last unit's re-reads have landed before the registers are reused
+  if constexpr (FUSED && MODE == kW13) {  // and its h stores are complete in every wave
+    __syncthreads();
+    if (tid == 0) atomicAdd(done + pub, 1);
+  }
 }
 
 // Pass b (int8 shared) and pass a (MXFP4 routed) of the same stage in one
@@ -369,6 +429,38 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(SkinnyArgs a, int has
   constexpr int NAB = MODE == kW13 ? 8 : 4;  // 8 columns
   if (idx[0] < nb) stream_loop<kFmtI8, MODE, DB, 1, NAB>(b, 0, nb, queue, idx, lds, sh);
   if (idx[0] >= nb && idx[0] < nb + na) stream_loop<kFmtMx, MODE, DA, NSA, NAA>(a, nb, nb + na, queue, idx, lds, sh);
+}
+
+// Both stages of the decode layer in one persistent grid fed by one queue:
+// [0, e0) shared w13 units, [e0, e1) routed w13, [e1, e2) shared w2,
+// [e2, e3) routed w2 (row group fastest in each). Every w13 unit is handed
+// out before any w2 unit, so a block's w2 phase overlaps the other blocks'
+// last w13 units and the w2 units start without a launch in between; a w2
+// unit waits (rarely) for its tile's w13 units through done_r (routed tiles)
+// and done_s (shared tiles), which the tile builders zero.
+template <int DA, int DB>
+__global__ __launch_bounds__(kStreamThreads) void k_stream_fused(SkinnyArgs a13, SkinnyArgs b13, SkinnyArgs a2,
+                                                                 SkinnyArgs b2, int* queue, int* done_r,
+                                                                 int* done_s) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int sh[4];
+  const int tiles = min(*a13.n_tiles, a13.n_tiles_grid);
+  const int e0 = b13.n_tiles_grid * b13.n_rowblocks;
+  const int e1 = e0 + tiles * a13.n_rowblocks;
+  const int e2 = e1 + b2.n_tiles_grid * b2.n_rowblocks;
+  const int e3 = e2 + tiles * a2.n_rowblocks;
+  const int G = gridDim.x;
+  if (threadIdx.x == 0) sh[0] = G + atomicAdd(queue, 2);
+  __syncthreads();
+  const int next = __builtin_amdgcn_readfirstlane(sh[0]);
+  int idx[3] = {(int)blockIdx.x, next, next + 1};
+  if (idx[0] < e0) stream_loop<kFmtI8, kW13, DB, 1, 8, true>(b13, 0, e0, queue, idx, lds, sh, done_s, 0);
+  if (idx[0] >= e0 && idx[0] < e1)
+    stream_loop<kFmtMx, kW13, DA, 4, 6, true>(a13, e0, e1, queue, idx, lds, sh, done_r, 0);
+  if (idx[0] >= e1 && idx[0] < e2)
+    stream_loop<kFmtI8, kW2, DB, 1, 4, true>(b2, e1, e2, queue, idx, lds, sh, done_s, b13.n_rowblocks);
+  if (idx[0] >= e2 && idx[0] < e3)
+    stream_loop<kFmtMx, kW2, DA, 2, 3, true>(a2, e2, e3, queue, idx, lds, sh, done_r, a13.n_rowblocks);
 }
 
 // Blocks of kernel k with lds bytes that the current device holds at once
@@ -423,6 +515,41 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
   if (res <= 0) return hipErrorInvalidValue;
   const long long grid = nblk < res ? nblk : res;
   kern<<<(unsigned)grid, kStreamThreads, lds, st>>>(a, a_blocks > 0 ? 1 : 0, b, b_blocks > 0 ? 1 : 0, queue);
+  return hipGetLastError();
+}
+
+static size_t stream_lds(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks) {
+  size_t lds = 0;
+  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / 32);
+  if (b_blocks > 0) {
+    const size_t lb = (size_t)b.tile_n * (2 * (size_t)b.K + 16);
+    lds = lb > lds ? lb : lds;
+  }
+  return lds;
+}
+
+hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, const SkinnyArgs& a2,
+                               const SkinnyArgs& b2, int a_blocks13, int b_blocks13, int a_blocks2, int b_blocks2,
+                               int* queue, int* done_r, int* done_s, hipStream_t st) {
+  if (a13.K % 1024 || a2.K % 1024 || !queue || !done_r || !done_s || !a13.tile_rec || !a2.tile_rec ||
+      b13.tile_n != b2.tile_n || b13.n_tiles_grid != b2.n_tiles_grid || a13.tile_n > 16 || b13.tile_n > 16 ||
+      a13.tile_n < 1 || b13.tile_n < 1 || a_blocks13 <= 0 || b_blocks13 <= 0)
+    return hipErrorInvalidValue;
+  const long long nblk = (long long)a_blocks13 + b_blocks13 + a_blocks2 + b_blocks2;
+  if (nblk > 0x3fffffffLL) return hipErrorInvalidValue;
+  size_t lds = stream_lds(a13, a_blocks13, b13, b_blocks13);
+  const size_t l2 = stream_lds(a2, a_blocks2, b2, b_blocks2);
+  lds = l2 > lds ? l2 : lds;
+  auto kern = &k_stream_fused<8, 4>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int res = stream_resident(reinterpret_cast<const void*>(kern), lds);
+  if (res <= 0) return hipErrorInvalidValue;
+  const long long grid = nblk < res ? nblk : res;
+  kern<<<(unsigned)grid, kStreamThreads, lds, st>>>(a13, b13, a2, b2, queue, done_r, done_s);
   return hipGetLastError();
 }
 
