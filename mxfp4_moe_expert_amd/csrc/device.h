@@ -221,22 +221,29 @@ __device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row
   wave_topk_row(topk_load(s_row, b_row, E), E, k, scale, ids_out, w_out, ids_lds);
 }
 
-// Exclusive scan over the block of one int per thread (tmp: blockDim.x ints
-// of LDS). Returns this thread's exclusive prefix; *total gets the sum.
+// Exclusive scan over the block of one int per thread (blockDim a multiple
+// of 64, at most 1024; tmp: at least blockDim/64 ints of LDS). Each wave
+// scans its lanes with shuffles, the waves' totals meet in LDS. Returns this
+// thread's exclusive prefix; *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int tid = threadIdx.x, n = blockDim.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < n; o <<= 1) {
-    const int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  const int incl = tmp[tid];
-  *total = tmp[n - 1];
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = tmp[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();  // tmp is free again
+  return base + x - v;
 }
 
 }  // namespace moe

@@ -245,19 +245,33 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   if (t < a.T)
     wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
               a.w + (size_t)t * a.k, nullptr);
-  __threadfence();  // this block's ids are visible before it is counted
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this block's ids are visible before it is counted
   __syncthreads();
   if (tid == 0) is_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
-  __threadfence();  // every other block's ids are visible from here on
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other blocks' ids are visible
 
+  // the thread's slots (tid, tid + 256; T*k <= 512): expert and weight, read once
+  constexpr int kPer = kSmallT * kMaxTopK / kTopkThreads;
+  const int n = a.T * a.k;
+  int es[kPer];
+  float ws[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = min(tid + j * kTopkThreads, n - 1);
+    es[j] = a.ids[i];
+    ws[j] = a.w[i];
+  }
   unsigned long long* mflat = &mask[0][0];
   for (int i = tid; i < kMaxExperts * kMaskWords; i += kTopkThreads) mflat[i] = 0ull;
   __syncthreads();
-  const int n = a.T * a.k;
   const int words = (n + 63) >> 6;
-  for (int i = tid; i < n; i += kTopkThreads) atomicOr(&mask[a.ids[i]][i >> 6], 1ull << (i & 63));
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + j * kTopkThreads;
+    if (i < n) atomicOr(&mask[es[j]][i >> 6], 1ull << (i & 63));
+  }
   __syncthreads();
   int c = 0;
   if (tid < a.E)
@@ -276,9 +290,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   // every slot: its sorted position, and its column of its tile's record
   // (the tile's first column also writes the record's head, its last column
   // the repeats up to column 16)
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const int e_i = a.ids[i];
-    const float wv = a.w[i];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + j * kTopkThreads;
+    if (i >= n) continue;
+    const int e_i = es[j];
+    const float wv = ws[j];
     const int wi = i >> 6;
     int rank = __popcll(mask[e_i][wi] & ((1ull << (i & 63)) - 1ull));
     for (int w = 0; w < wi; ++w) rank += __popcll(mask[e_i][w]);
