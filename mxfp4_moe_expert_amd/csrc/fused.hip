@@ -21,13 +21,17 @@
 //
 // The weight stream of a block is one in-order sequence: shared w13 (with
 // the router row), shared w2 once the block's score is published, the
-// routed w13 jobs with three in flight, then, once the block's h slices are
-// published, the routed w2 jobs, which stream while the other blocks' h
-// slices arrive. A CU queues its loads in order, so a load requested early
+// routed w13 jobs with three in flight, the first three routed w2 jobs
+// (they arrive while the block reduces and publishes its h slices, when the
+// CU's loads would otherwise pause), then, once the block's h slices are
+// published, the other routed w2 jobs, which stream while the other blocks'
+// h slices arrive. A CU queues its loads in order, so a load requested early
 // delays whatever the CU requests after it: each hand-off store goes out
 // before the bulk loads that follow it. (Requesting the w2 jobs before the
 // w13 jobs moves the end of the w13 stream, and with it every h slice, to
-// the end of the whole routed stream; measured slower.)
+// the end of the whole routed stream; measured slower. Requesting 2 to 4 w2
+// jobs before the h publish took the layer at one token from 30.0 to
+// 28.5 us; 5 or 6 delay the publish and lose it again.)
 //
 // Hand-offs: a producer stores each 32-bit word (a score, or a pair of bf16
 // h values) XORed with a tag that no computed word equals, so that no
@@ -53,6 +57,7 @@ constexpr uint32_t kScoreTag = 0x7F800001u;  // an fp32 signalling NaN: no compu
 constexpr uint32_t kHTag = 0x7F817F81u;      // two bf16 signalling NaNs: no rounded h pair
 constexpr uint32_t kNaNPair = 0x7FC07FC0u;   // h of a block whose routing timed out
 constexpr int kPollLimit = 1 << 20;          // polls (each followed by a short sleep)
+constexpr int kEarlyW2 = 3;                  // routed w2 jobs requested before the h publish
 
 template <int NH, int NI, int TT, int KK>
 struct LayerShape {
@@ -354,6 +359,13 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     if (j + P < NS) issue13(j + P);
     asm volatile("" ::: "memory");
   }
+  // the first routed w2 jobs, requested behind every w13 load: they arrive
+  // while the block reduces and publishes its h slices, when the CU's loads
+  // would otherwise pause
+  constexpr int kEarly = NS < kEarlyW2 ? NS : kEarlyW2;
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) issue2(u);
+  asm volatile("" ::: "memory");
 
   // 6. h slices: wave partials (the TT useful columns) -> LDS; wave 0 sums
   //    them in wave order, applies the clamped SwiGLU and publishes; then
@@ -391,9 +403,9 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
       if (b < I / 8) store_agent(X.h + col * (kXferMaxI / 2) + 4 * gb + p4, packed ^ kHTag);
     }
   }
-  __syncthreads();  // the h stores are requested before any routed w2 load of this CU
+  __syncthreads();  // the h stores are requested before the other routed w2 loads of this CU
 #pragma unroll
-  for (int u = 0; u < NS; ++u) issue2(u);
+  for (int u = kEarly; u < NS; ++u) issue2(u);
   asm volatile("" ::: "memory");
 
   // 7. every block's h slices: poll the columns into LDS
