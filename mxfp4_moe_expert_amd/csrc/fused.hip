@@ -203,6 +203,12 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
 #pragma unroll
   for (int i = 0; i < XPT / 4; ++i)
     rw[i] = *reinterpret_cast<const float4*>(a.gate_w + (size_t)er * H + tid * XPT + 4 * i);
+  // every wave's x and router slices are requested before any wave's shared
+  // expert weights (the logit needs all eight slices: with each wave
+  // requesting its three kinds back to back, the last slices queued behind
+  // up to 56 KB of other waves' shared weights; 0.7 us at one token)
+  asm volatile("" ::: "memory");
+  __syncthreads();
   uint4 qsh[N13I];
   {
     const int8_t* base = a.sh13 + (size_t)L.row13 * H + w * (H / 8) + g * 16;
@@ -408,6 +414,35 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   for (int u = kEarly; u < NS; ++u) issue2(u);
   asm volatile("" ::: "memory");
 
+  // the early routed w2 jobs' weights, converted to bf16 while the other
+  // blocks' h slices are awaited (they arrived before the h publish; the
+  // w2 MFMAs after the wait are bound by these converts, four per MFMA)
+  constexpr int kPre = NS <= 6 ? kEarly : 0;  // registers allow it for one token
+  bf16x8_t c2[kPre > 0 ? kPre : 1][N2][4];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      const float sc = e8m0_scale_operand((s2[u][i] >> (8 * g)) & 0xff);
+      const uint32_t d[4] = {q2[u][i].x, q2[u][i].y, q2[u][i].z, q2[u][i].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        c2[u][i][m] = fp4x8_to_bf16x8(d[m], sc);
+        asm volatile("" : "+v"(c2[u][i][m]));
+      }
+    }
+
+  // the shared w2 weights too (int8, in registers since the start)
+  bf16x8_t cs2[kPre > 0 ? N2I : 1][2];
+  if constexpr (kPre > 0) {
+#pragma unroll
+    for (int i = 0; i < N2I; ++i) {
+      cs2[i][0] = i8x8_to_bf16x8(qs2[i].x, qs2[i].y);
+      cs2[i][1] = i8x8_to_bf16x8(qs2[i].z, qs2[i].w);
+      asm volatile("" : "+v"(cs2[i][0]), "+v"(cs2[i][1]));
+    }
+  }
+
   // 7. every block's h slices: poll the columns into LDS
   {
     constexpr int n16 = I / 8;
@@ -452,14 +487,29 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   for (int u = 0; u < NS; ++u) {
     const unsigned char* bsrc = (r == u ? L.hl + (size_t)u * HROW : L.zero) + (size_t)(w * (I / 8) + g * 32) * 2;
 #pragma unroll
-    for (int i = 0; i < N2; ++i)
-      mx16_mfma(q2[u][i], (s2[u][i] >> (8 * g)) & 0xff, bsrc + i * 256, acc2[(u * N2 + i) & 3]);
+    for (int i = 0; i < N2; ++i) {
+      if (u < kPre) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc2[(u * N2 + i) & 3] = mfma_16x16x32(c2[u][i][m], *reinterpret_cast<const bf16x8_t*>(bsrc + i * 256 + m * 16),
+                                                 acc2[(u * N2 + i) & 3]);
+      } else {
+        mx16_mfma(q2[u][i], (s2[u][i] >> (8 * g)) & 0xff, bsrc + i * 256, acc2[(u * N2 + i) & 3]);
+      }
+    }
   }
   {
     const unsigned char* bsrc = (r >= NS && r < NCOL ? L.hl + (size_t)r * HROW : L.zero) +
                                 (size_t)(w * (I / 8) + g * 16) * 2;
 #pragma unroll
-    for (int i = 0; i < N2I; ++i) i816_mfma(qs2[i], bsrc + i * 128, acc2[i & 3]);
+    for (int i = 0; i < N2I; ++i) {
+      if constexpr (kPre > 0) {
+        acc2[i & 3] = mfma_16x16x32(cs2[i][0], *reinterpret_cast<const bf16x8_t*>(bsrc + i * 128), acc2[i & 3]);
+        acc2[i & 3] = mfma_16x16x32(cs2[i][1], *reinterpret_cast<const bf16x8_t*>(bsrc + i * 128 + 16), acc2[i & 3]);
+      } else {
+        i816_mfma(qs2[i], bsrc + i * 128, acc2[i & 3]);
+      }
+    }
   }
   L.red2[w * 64 + lane] = (acc2[0] + acc2[1]) + (acc2[2] + acc2[3]);
   __syncthreads();
