@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -132,10 +133,34 @@ def algorithmic(wl, ids_np):
                 layer_flops=flops, router_flops=2.0 * T * E * H)
 
 
-def source_hash() -> str:
+# Source file of each dominant kernel; its traffic record is keyed on this
+# file, the library headers it includes and the launcher (api.cpp, which sets
+# its launch configuration), so that a change elsewhere keeps the record.
+KERNEL_SOURCE = {"k_layer_small": "fused.hip", "k_stream_fused": "stream.hip", "k_gemm": "gemm.hip"}
+
+
+def kernel_files(workload: str):
+    csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
+    short = DOMINANT[workload][0].split("::")[1].split("<")[0]
+    todo, seen = [KERNEL_SOURCE[short], "api.cpp"], set()
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        with open(os.path.join(csrc, f)) as fh:
+            for line in fh:
+                m = re.match(r'\s*#include\s+"([^"]+)"', line)
+                if m and os.path.exists(os.path.join(csrc, m.group(1))):
+                    todo.append(m.group(1))
+    return sorted(seen)
+
+
+def source_hash(workload: str) -> str:
+    """Hash of the dominant kernel's sources (kernel_files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in kernel_files(workload):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -150,7 +175,7 @@ def traffic_from_profiles(workload: str):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -207,7 +232,8 @@ def summarize(workload, outdir, commands):
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     stats = _csv_rows(_find(outdir, "kernel_trace", "kernel_stats.csv"))
     lines = [f"# Kernel durations, moe_forward, workload {workload}", "",
-             f"Source hash of the kernels: `{source_hash()}`", "",
+             f"Source hash of the dominant kernel ({', '.join(kernel_files(workload))}): "
+             f"`{source_hash(workload)}`", "",
              "Command:", "", "```", commands.get("kernel_trace", "?"), "```", "",
              f"Dominant kernel: `{kname}` ({what}).", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
@@ -232,7 +258,8 @@ def summarize(workload, outdir, commands):
     f_fac = COPY_CAL_BYTES / (cf * 1024.0)
     w_fac = COPY_CAL_BYTES / (cw * 1024.0)
     rec = {
-        "workload": workload, "kernel": kname, "source_hash": source_hash(),
+        "workload": workload, "kernel": kname, "source_hash": source_hash(workload),
+        "source_files": kernel_files(workload),
         "fetch_kib_per_dispatch": round(fk, 2), "write_kib_per_dispatch": round(wk, 2),
         "dispatches": [nf, nw],
         "copy_bytes": COPY_CAL_BYTES, "copy_fetch_kib": round(cf, 2), "copy_write_kib": round(cw, 2),
