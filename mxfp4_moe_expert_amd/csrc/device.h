@@ -171,6 +171,9 @@ __device__ __forceinline__ TopkRow topk_load(const float* s_row, const float* b_
   return t;
 }
 
+// COH: ids and weights are written through to memory (agent-scope stores),
+// for other blocks of the same launch.
+template <bool COH = false>
 __device__ __forceinline__ void wave_topk_row(const TopkRow& row, int E, int k, float scale, int32_t* ids_out,
                                               float* w_out, int32_t* ids_lds) {
   const int lane = threadIdx.x & 63;
@@ -209,16 +212,23 @@ __device__ __forceinline__ void wave_topk_row(const TopkRow& row, int E, int k, 
 #pragma unroll
     for (int j = 0; j < kTopKMax; ++j) {
       if (j >= k) continue;
-      ids_out[j] = sel_id[j];
-      w_out[j] = scale * sel_s[j] / sum;
+      const float wj = scale * sel_s[j] / sum;
+      if constexpr (COH) {
+        store_agent(reinterpret_cast<uint32_t*>(ids_out) + j, (uint32_t)sel_id[j]);
+        store_agent(reinterpret_cast<uint32_t*>(w_out) + j, __float_as_uint(wj));
+      } else {
+        ids_out[j] = sel_id[j];
+        w_out[j] = wj;
+      }
       if (ids_lds) ids_lds[j] = sel_id[j];
     }
   }
 }
 
+template <bool COH = false>
 __device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row, int E, int k, float scale,
                                           int32_t* ids_out, float* w_out, int32_t* ids_lds) {
-  wave_topk_row(topk_load(s_row, b_row, E), E, k, scale, ids_out, w_out, ids_lds);
+  wave_topk_row<COH>(topk_load(s_row, b_row, E), E, k, scale, ids_out, w_out, ids_lds);
 }
 
 // Exclusive scan over the block of one int per thread (blockDim a multiple

@@ -32,10 +32,11 @@ struct Perm {
 };
 
 // Tile record, one per routed tile, written with the tile table at decode
-// sizes (write_tile_records) and read by the streaming passes, kRecInts ints:
-// expert, first position, columns, 0, then for columns c < 16 (columns past
-// the tile repeat its last one) the token of the position, the slot, and the
-// slot's routing weight (float bits).
+// sizes (write_tile_records, or the decode top-k) and read by the streaming
+// passes, kRecInts ints: expert, first position, columns, 0, then for
+// columns c < 16 the token of the position, the slot, and the slot's routing
+// weight (float bits). Only columns below the tile's count are defined (the
+// passes clamp or mask the others).
 constexpr int kRecInts = 52;
 
 enum { kFmtMx = 0, kFmtI8 = 1 };  // routed MXFP4 / shared int8 weights

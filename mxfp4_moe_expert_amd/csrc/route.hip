@@ -206,25 +206,6 @@ __global__ __launch_bounds__(kDecExperts * 64) void k_router_dec(RouterArgs a) {
   if (e < a.E && lane < nt) store_score(a, t0 + lane, e, mine + (a.logit_offset ? a.logit_offset[e] : 0.0f));
 }
 
-// Writes the expert tile table from the per-expert counts (thread e < E of a
-// block holds count c and first position off of expert e): tiles of at most
-// tile_n consecutive sorted positions of one expert, in expert order.
-// Returns the index of the thread's expert's first tile.
-__device__ int block_write_tiles(int c, int off, int E, const Perm& p, int* scan_tmp) {
-  const int tid = threadIdx.x;
-  const int nt = tid < E ? (c + p.tile_n - 1) / p.tile_n : 0;
-  int total;
-  const int toff = block_exclusive_scan(nt, scan_tmp, &total);
-  if (tid < E) {
-    for (int i = 0; i < nt; ++i) {
-      const int first = i * p.tile_n;
-      p.tile_info[toff + i] = make_int4(tid, off + first, min(p.tile_n, c - first), 0);
-    }
-  }
-  if (tid == 0) *p.n_tiles = total;
-  return toff;
-}
-
 // Top-k of every token, one wave per token (4 per block); then the last
 // block to finish (an arrival count in the workspace, which it sets back to
 // zero) makes the stable counting sort of the T*k <= 512 slots, the expert
@@ -242,15 +223,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   __shared__ int is_last;
   const int tid = threadIdx.x;
   const int t = blockIdx.x * (kTopkThreads / 64) + (tid >> 6);
+  // ids and weights are written through to memory; each wave waits for its
+  // stores before the block is counted, and the last block reads them with
+  // coherent loads (no cache write-back or invalidation: the fences that
+  // did this cost about 1.5 us)
   if (t < a.T)
-    wave_topk(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale, a.ids + (size_t)t * a.k,
-              a.w + (size_t)t * a.k, nullptr);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this block's ids are visible before it is counted
+    wave_topk<true>(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale,
+                    a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, nullptr);
+  __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));  // vmcnt(0): this wave's stores are done
   __syncthreads();
   if (tid == 0) is_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other blocks' ids are visible
 
   // the thread's slots (tid, tid + 256; T*k <= 512): expert and weight, read once
   constexpr int kPer = kSmallT * kMaxTopK / kTopkThreads;
@@ -260,8 +244,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = min(tid + j * kTopkThreads, n - 1);
-    es[j] = a.ids[i];
-    ws[j] = a.w[i];
+    es[j] = (int)load_agent(reinterpret_cast<const uint32_t*>(a.ids) + i);
+    ws[j] = __uint_as_float(load_agent(reinterpret_cast<const uint32_t*>(a.w) + i));
   }
   unsigned long long* mflat = &mask[0][0];
   for (int i = tid; i < kMaxExperts * kMaskWords; i += kTopkThreads) mflat[i] = 0ull;
@@ -276,20 +260,30 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   int c = 0;
   if (tid < a.E)
     for (int w = 0; w < words; ++w) c += __popcll(mask[tid][w]);
+  // one scan for both prefixes: slots in the low 16 bits, tiles in the high
+  // (at most 512 of either); expert e's tiles are at most tile_n consecutive
+  // sorted positions each, in expert order
+  const int nt = (c + p.tile_n - 1) / p.tile_n;
   int total;
-  const int off = block_exclusive_scan(c, scan_tmp, &total);
+  const int both = block_exclusive_scan(c | (nt << 16), scan_tmp, &total);
+  const int off = both & 0xffff, toff = both >> 16;
   if (tid < a.E) {
     p.offsets[tid] = off;
     first[tid] = off;
     count[tid] = c;
+    tile0[tid] = toff;
+    for (int i = 0; i < nt; ++i) {
+      const int f = i * p.tile_n;
+      p.tile_info[toff + i] = make_int4(tid, off + f, min(p.tile_n, c - f), 0);
+    }
   }
-  if (tid == 0) p.offsets[a.E] = total;
-  const int t0 = block_write_tiles(c, off, a.E, p, scan_tmp);
-  if (tid < a.E) tile0[tid] = t0;
+  if (tid == 0) {
+    p.offsets[a.E] = total & 0xffff;
+    *p.n_tiles = total >> 16;
+  }
   __syncthreads();
   // every slot: its sorted position, and its column of its tile's record
-  // (the tile's first column also writes the record's head, its last column
-  // the repeats up to column 16)
+  // (the tile's first column also writes the record's head)
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = tid + j * kTopkThreads;
@@ -312,11 +306,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
       rec[2] = ncols;
       rec[3] = 0;
     }
-    for (int cc = col; cc < (col == ncols - 1 ? 16 : col + 1); ++cc) {
-      rec[4 + cc] = i / a.k;
-      rec[20 + cc] = i;
-      rec[36 + cc] = __float_as_int(wv);
-    }
+    rec[4 + col] = i / a.k;
+    rec[20 + col] = i;
+    rec[36 + col] = __float_as_int(wv);
   }
   for (int i = tid; i < p.max_tiles + kSmallT; i += kTopkThreads) p.done[i] = 0;
   if (tid == 0) {
