@@ -296,9 +296,10 @@ GemmArgs gemm_routed_w13(const moe_config& c, int T, const uint16_t* x, const Pe
   return g;
 }
 
-// Routed w2 x routing weight: ybuf [slot][H].
+// Routed w2 x routing weight: ybuf [slot][H], bf16 (the combine sums the k
+// rounded slot outputs of a token in fp32).
 GemmArgs gemm_routed_w2(const moe_config& c, int T, const Perm& p, const float* slot_w, const uint8_t* w2c,
-                        const uint8_t* w2s, const uint16_t* hbuf, float* ybuf) {
+                        const uint8_t* w2s, const uint16_t* hbuf, uint16_t* ybuf) {
   const int H = c.hidden_size, I = c.moe_intermediate;
   GemmArgs g = gemm_common(c, T);
   g.fmt = 0;
@@ -343,7 +344,7 @@ GemmArgs gemm_shared_w13(const moe_config& c, int T, const uint16_t* x, const in
 
 // Shared w2 + the final combine: out[t] = sum_j ybuf[t*k+j] + s2 * (Q2 hs_t).
 GemmArgs gemm_shared_w2_combine(const moe_config& c, int T, const int8_t* q2, const float* s2, const uint16_t* hs,
-                                const float* ybuf, void* out, int out_is_fp32) {
+                                const uint16_t* ybuf, void* out, int out_is_fp32) {
   const int H = c.hidden_size, I = c.moe_intermediate;
   GemmArgs g = gemm_common(c, T);
   g.fmt = 1;
@@ -525,7 +526,8 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   float* ybuf = at<float>(workspace, L.ybuf);
   if (use_gemm(*cfg, T)) {
     const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
-    const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, ybuf);
+    const GemmArgs g2 =
+        gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, reinterpret_cast<uint16_t*>(ybuf));
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm(g2, p.max_tiles, st); }));
@@ -556,7 +558,7 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
                       [&] { return launch_w2(r2, p.max_tiles * r2.n_rowblocks, nullptr, 0, st); }));
     if (rc) return rc;
   }
-  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, nullptr, routed_out, 1};
+  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, nullptr, routed_out, 1, use_gemm(*cfg, T) ? 1 : 0};
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 
@@ -733,8 +735,9 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       // grouped GEMMs; the shared expert's w2 finishes with the combine
       const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
       const GemmArgs h13 = gemm_shared_w13(*cfg, T, x, sh_w13, sh_w13_scale, hs);
-      const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
-      const GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybuf, out, out_is_fp32 ? 1 : 0);
+      uint16_t* ybf = reinterpret_cast<uint16_t*>(ybuf);  // the slot outputs in bf16 here
+      const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybf);
+      const GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybf, out, out_is_fp32 ? 1 : 0);
       const int sh_tiles = (T + kGemmTokens - 1) / kGemmTokens;
       rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
       if (rc) return rc;
@@ -750,7 +753,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2(r2, r2_blocks, &s2, sh2_blocks, st); }));
     if (rc) return rc;
   }
-  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, zbuf, out, out_is_fp32 ? 1 : 0};
+  CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, zbuf, out, out_is_fp32 ? 1 : 0, 0};
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 

@@ -103,7 +103,8 @@ hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st) {
 
 // ---------------------------------------------------------------- combine
 
-// out[t][n] = sum_{j<k} ybuf[t*k+j][n] (+ zbuf[t][n]), slots in order.
+// out[t][n] = sum_{j<k} ybuf[t*k+j][n] (+ zbuf[t][n]), slots in order; ybuf
+// fp32, or bf16 (y_bf16) as the large-batch GEMMs write it.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
   const size_t n4 = (size_t)a.T * a.H / 4;
@@ -111,7 +112,14 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const size_t t = i4 * 4 / a.H, n = i4 * 4 - t * a.H;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < a.k; ++j) {
-    const float4 y = *reinterpret_cast<const float4*>(a.ybuf + (t * a.k + j) * a.H + n);
+    float4 y;
+    if (a.y_bf16) {
+      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ybuf) + (t * a.k + j) * a.H + n);
+      y = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffffu),
+                      bf16_to_f32(v.y >> 16));
+    } else {
+      y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.ybuf) + (t * a.k + j) * a.H + n);
+    }
     acc.x += y.x;
     acc.y += y.y;
     acc.z += y.z;

@@ -161,7 +161,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
                                           const uint16_t* asrc, u32x4_t* adst0, u32x4_t* adst1,
                                           const unsigned char* abase0, const unsigned char* abase1, int nst,
                                           int ncols, int pos0, int nt, int wn, int g, int r,
-                                          const StoreScales& store_scales) {
+                                          const StoreScales& store_scales, const int (&slot_r)[kMB]) {
   f32x4_t acc[kRB][MB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b)
@@ -179,6 +179,12 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
   gemm_load_w(qe, qoff, 0, w0);
   av0.load(asrc, 0);
   store_scales();  // the block's scales, requested before these first loads
+  // routed w2: the routing weights of the lane's columns (their slots came
+  // before the scales, so they are in), in flight during the K loop
+  float wv_r[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) wv_r[m] = MODE == kGemmW2 ? p.slot_w[slot_r[m]] : 0.0f;
+  asm volatile("" ::: "memory");
   av0.store(adst0);
   av1.load(asrc, min(1, last));
   av0.load(asrc, min(2, last));
@@ -222,14 +228,16 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
       pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
       pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
       *reinterpret_cast<uint2*>(p.hout + (size_t)pos * p.hout_ld + hc) = pk;
-    } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot]
-      const int slot = p.sorted_slots[pos];
-      const float wv = p.slot_w[slot];
+    } else if (MODE == kGemmW2) {  // routed: y * w -> yout[slot], bf16
+      const int slot = slot_r[m];
+      const float wv = wv_r[m];
 #pragma unroll
       for (int b = 0; b < kRB; ++b) {
         const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
-        *reinterpret_cast<float4*>(p.yout + (size_t)slot * p.yout_ld + n) =
-            make_float4(acc[b][m][0] * wv, acc[b][m][1] * wv, acc[b][m][2] * wv, acc[b][m][3] * wv);
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc[b][m][0] * wv) | ((uint32_t)f32_to_bf16(acc[b][m][1] * wv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc[b][m][2] * wv) | ((uint32_t)f32_to_bf16(acc[b][m][3] * wv) << 16);
+        *reinterpret_cast<uint2*>(p.yout + (size_t)slot * p.yout_ld + n) = pk;
       }
     } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
 #pragma unroll
@@ -237,11 +245,11 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
         const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int j = 0; j < p.topk; ++j) {
-          const float4 y = *reinterpret_cast<const float4*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
-          o.x += y.x;
-          o.y += y.y;
-          o.z += y.z;
-          o.w += y.w;
+          const uint2 y = *reinterpret_cast<const uint2*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
+          o.x += bf16_to_f32(y.x & 0xffffu);
+          o.y += bf16_to_f32(y.x >> 16);
+          o.z += bf16_to_f32(y.y & 0xffffu);
+          o.w += bf16_to_f32(y.y >> 16);
         }
         o.x += p.row_scale[n] * acc[b][m][0];
         o.y += p.row_scale[n + 1] * acc[b][m][1];
@@ -331,6 +339,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[q];
     }
   };
+  // routed w2: the slots of the lane's columns, requested first (the
+  // epilogue scatters by slot and scales by its routing weight: loaded there,
+  // slot then weight, two memory round trips ended every tile)
+  int slot_r[kMB];
+#pragma unroll
+  for (int m = 0; m < kMB; ++m) {
+    const int tok = m * 16 + r;
+    slot_r[m] = MODE == kGemmW2 ? p.sorted_slots[pos0 + (tok < ncols ? tok : 0)] : 0;
+  }
   uint4 scv[kScalePieces];
   if (FMT == kFmtMx) {
 #pragma unroll
@@ -368,19 +385,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   switch ((ncols + 31) >> 5) {
     case 1:
       gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales);
+                              g, r, store_scales, slot_r);
       break;
     case 2:
       gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales);
+                              g, r, store_scales, slot_r);
       break;
     case 3:
       gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales);
+                              g, r, store_scales, slot_r);
       break;
     default:
       gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                wn, g, r, store_scales);
+                                wn, g, r, store_scales, slot_r);
   }
 }
 

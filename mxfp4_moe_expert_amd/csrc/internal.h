@@ -146,11 +146,11 @@ struct GemmArgs {
   const int32_t* act_row;     // row of act for each position (null: the position)
   uint16_t* hout;
   int hout_ld;
-  float* yout;
+  uint16_t* yout;             // w2 routed: bf16 rows (x routing weight), by slot
   int yout_ld;
   const int32_t* sorted_slots;
   const float* slot_w;
-  const float* ybuf;          // combine: [T*k][H]
+  const uint16_t* ybuf;       // combine: [T*k][H] bf16
   int topk;
   void* out;
   int out_ld, out_is_fp32;
@@ -160,10 +160,11 @@ constexpr int kGemmTokens = 128;  // token positions per GEMM tile
 
 struct CombineArgs {
   int T, H, k;
-  const float* ybuf;  // [T*k][H] weighted expert outputs in slot order
+  const void* ybuf;   // [T*k][H] weighted expert outputs in slot order: fp32, or bf16 if y_bf16
   const float* zbuf;  // [T][H] shared expert or null
   void* out;          // [T][H]
   int out_is_fp32;
+  int y_bf16;
 };
 
 // Routers
