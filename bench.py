@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure a 1 GiB device copy and a bf16 matmul (denominators beside the published peaks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of %d bytes 5 times (the counters' calibration)"
                     % COPY_CAL_BYTES)
@@ -195,6 +197,43 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "dispatches": 5, "ok": ok}), flush=True)
 
 
+def measured_peaks():
+    """What plain library work reaches on this GPU, as denominators beside
+    the published peaks: a 1 GiB device copy (HBM GB/s, read + write bytes)
+    and a bf16 8192^3 matmul (TFLOP/s), each the median of 20 runs timed
+    with events."""
+    import torch
+
+    def timed(fn, n=20):
+        ts = []
+        for _ in range(3):
+            fn()
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    nb = 1 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    ms_mm = timed(lambda: torch.matmul(x, y))
+    rec = {"copy_bytes_moved": 2 * nb, "copy_ms": round(ms_copy, 4),
+           "copy_GBps": round(2 * nb / (ms_copy / 1e3) / 1e9, 1),
+           "matmul_bf16_n": n, "matmul_ms": round(ms_mm, 4),
+           "matmul_TFLOPs": round(2.0 * n ** 3 / (ms_mm / 1e3) / 1e12, 1),
+           "published": {"hbm_GBps": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS}}
+    print(json.dumps(rec), flush=True)
+
+
 def _csv_rows(path):
     import csv
 
@@ -313,6 +352,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "the layer runs on a single GPU: --gpus must be 1 (there is no multi-GPU path)"}))
         sys.exit(2)
+    if args.peaks:
+        measured_peaks()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
