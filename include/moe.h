@@ -47,10 +47,11 @@
  *   - `workspace` is device scratch of at least moe_workspace_size() bytes,
  *     256-byte aligned. Zero-fill it once before its first use
  *     (moe_workspace_init, or any zero fill): bytes 64 .. 67 count the
- *     blocks of the decode-size top-k, and bytes 256 .. 136447 hold the
- *     hand-off state of the single-launch layer (MOE_SCHED_SINGLE); every
- *     call leaves both ready for the next, and every other workspace value
- *     is written before it is read. Calls that share one workspace must be
+ *     blocks of the decode-size top-k, bytes 96 .. 239 hold the tile
+ *     queues of the grouped GEMMs (MOE_SCHED_LARGE), and bytes 256 ..
+ *     136447 hold the hand-off state of the single-launch layer
+ *     (MOE_SCHED_SINGLE); every call leaves all three ready for the next,
+ *     and every other workspace value is written before it is read. Calls that share one workspace must be
  *     ordered on one stream. If a single-launch call's bounded wait for
  *     another block of its grid expires (about a second), its output is
  *     NaN; the hand-off state stays consistent.

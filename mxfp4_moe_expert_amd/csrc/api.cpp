@@ -117,6 +117,12 @@ inline P* at(void* ws, size_t off) {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Tile queue of one grouped-GEMM launch (9 ints in the counters region,
+// zero on first use and left zero by every launch).
+inline int* gemm_queue(void* ws, const Layout& L, int which) {
+  return at<int32_t>(ws, L.counters) + kGemmQueueInts + 9 * which;
+}
+
 int status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 // Measurement hook (moe_set_kernel_events): events recorded around one kernel.
@@ -525,9 +531,10 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
   float* ybuf = at<float>(workspace, L.ybuf);
   if (use_gemm(*cfg, T)) {
-    const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
-    const GemmArgs g2 =
-        gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, reinterpret_cast<uint16_t*>(ybuf));
+    GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+    GemmArgs g2 = gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, reinterpret_cast<uint16_t*>(ybuf));
+    g13.queue = gemm_queue(workspace, L, kQRoutedW13);
+    g2.queue = gemm_queue(workspace, L, kQRoutedW2);
     rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm(g2, p.max_tiles, st); }));
@@ -733,11 +740,15 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     if (rc) return rc;
     if (use_gemm(*cfg, T)) {
       // grouped GEMMs; the shared expert's w2 finishes with the combine
-      const GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
-      const GemmArgs h13 = gemm_shared_w13(*cfg, T, x, sh_w13, sh_w13_scale, hs);
+      GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
+      GemmArgs h13 = gemm_shared_w13(*cfg, T, x, sh_w13, sh_w13_scale, hs);
       uint16_t* ybf = reinterpret_cast<uint16_t*>(ybuf);  // the slot outputs in bf16 here
-      const GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybf);
-      const GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybf, out, out_is_fp32 ? 1 : 0);
+      GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybf);
+      GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybf, out, out_is_fp32 ? 1 : 0);
+      g13.queue = gemm_queue(workspace, L, kQRoutedW13);
+      h13.queue = gemm_queue(workspace, L, kQSharedW13);
+      g2.queue = gemm_queue(workspace, L, kQRoutedW2);
+      h2.queue = gemm_queue(workspace, L, kQSharedW2);
       const int sh_tiles = (T + kGemmTokens - 1) / kGemmTokens;
       rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
       if (rc) return rc;

@@ -273,131 +273,170 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr int kBK = GemmCfg<FMT>::kBK, kKK = GemmCfg<FMT>::kKK;
   __shared__ __align__(16) unsigned char lds_a[2][GemmCfg<FMT>::kStage];
   extern __shared__ __align__(16) unsigned char lds_s[];  // MXFP4: [256 local rows][K/32 + 4] E8M0 bytes
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const int wn = wave;  // the wave's 32 weight rows; every wave covers all 128 positions
+  __shared__ int grabbed;
 
-  // XCD-aware order over the blocks in use: logical tile = (xcd, run
-  // position); N tiles fastest
-  const int nblk = p.routed ? *p.n_tiles * p.n_ntiles : (int)gridDim.x;
-  if ((int)blockIdx.x >= nblk) return;
+  // Persistent: at most the blocks that fit at once, each walking tiles.
+  // XCD-aware order: XCD x (blocks b with b % 8 == x) owns a contiguous run
+  // of the logical tiles (N tiles fastest), handed out in order: a block's
+  // first two tiles are fixed, then it grabs from its XCD's counter, two
+  // tiles ahead, so that while a tile computes the block already knows the
+  // next one and requests its record and gathered row ids.
+  const int nblk = p.routed ? *p.n_tiles * p.n_ntiles : ((p.T + kBM - 1) / kBM) * p.n_ntiles;
+  const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, inx = blockIdx.x >> 3;
+  const int nx = (G - xcd + 7) >> 3;  // blocks on this XCD
   const int per = nblk >> 3, extra = nblk & 7;
-  const int logical = xcd * per + min(xcd, extra) + inx;
-  const int nt = logical % p.n_ntiles;
-  const int tg = logical / p.n_ntiles;
-
-  int e = 0, pos0, ncols;
-  if (p.routed) {
-    const int4 ti = p.tile_info[tg];
-    e = ti.x;
-    pos0 = ti.y;
-    ncols = ti.z;
-  } else {
-    pos0 = tg * kBM;
-    if (pos0 >= p.T) return;
-    ncols = min(kBM, p.T - pos0);
-  }
+  const int lo = xcd * per + min(xcd, extra), hi = lo + per + (xcd < extra ? 1 : 0);
+  int* const q = p.queue;  // [8] tiles handed out per XCD, [8] blocks done
 
   const int K = p.K;
   const int nst = K / kBK;
-  // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
-  // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
-  const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
   const int srow = K / 32 + 4;  // padded LDS row of scales
-  uint32_t qoff[kRB], soff[kRB];
-#pragma unroll
-  for (int b = 0; b < kRB; ++b) {
-    int wrow;
-    if (MODE == kGemmW13) wrow = (b == 0 ? 0 : p.half) + nt * (kBN / 2) + wn * 16 + r;
-    else wrow = nt * kBN + wn * 32 + b * 16 + r;
-    qoff[b] = (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
-    // local row: gate rows (w13) or the first 128 rows (w2) at 0 .., the rest at 128 ..
-    const int lrow = MODE == kGemmW13 ? (b == 0 ? 0 : 128) + wn * 16 + r : wn * 32 + b * 16 + r;
-    soff[b] = (uint32_t)lrow * srow + g;
-  }
-  // the block's scales: two runs of 128 rows (w13: gate rows, up rows; w2:
-  // the tile's 256 rows), K/32 bytes per row, in 16-byte pieces. Up to
-  // kScalePieces per thread are requested now, ahead of the pipeline's
-  // first loads, and written to LDS after those are issued (any more are
-  // copied then, for K above 4096).
-  constexpr int kScalePieces = 4;
-  const uint8_t* se = p.wsc + (long long)e * p.s_expert_stride;
   const int rowlen = K / 32, npieces = FMT == kFmtMx ? 2 * 128 * rowlen / 16 : 0;
   const int hpieces = npieces > 1 ? npieces / 2 : 1;  // pieces per run of 128 rows
-  auto piece_src = [&](int i) {
-    const int run = i / hpieces, o = (i - run * hpieces) * 16;
-    const int grow0 = MODE == kGemmW13 ? (run == 0 ? 0 : p.half) + nt * (kBN / 2) : nt * kBN + run * 128;
-    return reinterpret_cast<const uint4*>(se + (size_t)grow0 * rowlen + o);
+  constexpr int kScalePieces = 4;
+
+  // a tile's record (uniform): expert, first sorted position, positions
+  auto record = [&](int lg) -> int4 {
+    const int tg = min(lg, nblk - 1) / p.n_ntiles;
+    int4 t = p.routed ? p.tile_info[tg] : make_int4(0, tg * kBM, min(kBM, p.T - tg * kBM), 0);
+    t.x = __builtin_amdgcn_readfirstlane(t.x);
+    t.y = __builtin_amdgcn_readfirstlane(t.y);
+    t.z = __builtin_amdgcn_readfirstlane(t.z);
+    t.w = 0;
+    return t;
   };
-  auto piece_store = [&](int i, const uint4& v) {
-    const int run = i / hpieces, o = (i - run * hpieces) * 16;
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // the gathered activation row of this lane's token (16*wave + lane%16 of
+  // the tile; rows past the tile re-read its first row, never stored)
+  auto act_row_of = [&](const int4& rec, int arow) -> int {
+    const int apos = rec.y + (arow < rec.z ? arow : 0);
+    return p.act_row ? p.act_row[apos] : apos;
+  };
+
+  int cur = lo + inx, nxt = lo + nx + inx;
+  int4 rec = record(cur);
+  int atrow = act_row_of(rec, (threadIdx.x >> 6) * 16 + (threadIdx.x & 15));
+  while (cur < hi) {
+    // Per-lane values come from an opaque copy of the thread index, so that
+    // they are recomputed per tile: hoisted out of the loop they stayed live
+    // across it and spilled.
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int wn = wave;  // the wave's 32 weight rows; every wave covers all 128 positions
+    // the tile after next: its index is only needed at the end of this tile
+    int grab = 0;
+    if (tid == 0) grab = atomicAdd(q + xcd, 1);
+    const int4 rec_n = record(nxt);  // the next tile's record; its row ids once the scales are in
+    int atrow_n = atrow;
+
+    const int nt = cur % p.n_ntiles;
+    const int e = rec.x, pos0 = rec.y, ncols = rec.z;
+    // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
+    // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
+    const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
+    uint32_t qoff[kRB], soff[kRB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int oq = o + 4 * q, row = oq / rowlen, col = oq - row * rowlen;
-      *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[q];
+    for (int b = 0; b < kRB; ++b) {
+      int wrow;
+      if (MODE == kGemmW13) wrow = (b == 0 ? 0 : p.half) + nt * (kBN / 2) + wn * 16 + r;
+      else wrow = nt * kBN + wn * 32 + b * 16 + r;
+      qoff[b] = (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
+      // local row: gate rows (w13) or the first 128 rows (w2) at 0 .., the rest at 128 ..
+      const int lrow = MODE == kGemmW13 ? (b == 0 ? 0 : 128) + wn * 16 + r : wn * 32 + b * 16 + r;
+      soff[b] = (uint32_t)lrow * srow + g;
     }
-  };
-  // routed w2: the slots of the lane's columns, requested first (the
-  // epilogue scatters by slot and scales by its routing weight: loaded there,
-  // slot then weight, two memory round trips ended every tile)
-  int slot_r[kMB];
+    // the tile's scales: two runs of 128 rows (w13: gate rows, up rows; w2:
+    // the tile's 256 rows), K/32 bytes per row, in 16-byte pieces. Up to
+    // kScalePieces per thread are requested now, ahead of the pipeline's
+    // first loads, and written to LDS after those are issued (any more are
+    // copied then, for K above 4096).
+    const uint8_t* se = p.wsc + (long long)e * p.s_expert_stride;
+    auto piece_src = [&](int i) {
+      const int run = i / hpieces, o = (i - run * hpieces) * 16;
+      const int grow0 = MODE == kGemmW13 ? (run == 0 ? 0 : p.half) + nt * (kBN / 2) : nt * kBN + run * 128;
+      return reinterpret_cast<const uint4*>(se + (size_t)grow0 * rowlen + o);
+    };
+    auto piece_store = [&](int i, const uint4& v) {
+      const int run = i / hpieces, o = (i - run * hpieces) * 16;
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int m = 0; m < kMB; ++m) {
-    const int tok = m * 16 + r;
-    slot_r[m] = MODE == kGemmW2 ? p.sorted_slots[pos0 + (tok < ncols ? tok : 0)] : 0;
-  }
-  uint4 scv[kScalePieces];
-  if (FMT == kFmtMx) {
+      for (int qq = 0; qq < 4; ++qq) {
+        const int oq = o + 4 * qq, row = oq / rowlen, col = oq - row * rowlen;
+        *reinterpret_cast<uint32_t*>(lds_s + (size_t)(run * 128 + row) * srow + col) = d[qq];
+      }
+    };
+    // routed w2: the slots of the lane's columns, requested first (the
+    // epilogue scatters by slot and scales by its routing weight: loaded
+    // there, slot then weight, two memory round trips ended every tile)
+    int slot_r[kMB];
 #pragma unroll
-    for (int j = 0; j < kScalePieces; ++j) scv[j] = *piece_src(min(tid + j * kGemmThreads, npieces - 1));
-  }
-  auto store_scales = [&]() __attribute__((always_inline)) {
+    for (int m = 0; m < kMB; ++m) {
+      const int tok = m * 16 + r;
+      slot_r[m] = MODE == kGemmW2 ? p.sorted_slots[pos0 + (tok < ncols ? tok : 0)] : 0;
+    }
+    uint4 scv[kScalePieces];
     if (FMT == kFmtMx) {
 #pragma unroll
-      for (int j = 0; j < kScalePieces; ++j) {
-        const int i = tid + j * kGemmThreads;
-        if (i < npieces) piece_store(i, scv[j]);
-      }
-      for (int i = tid + kScalePieces * kGemmThreads; i < npieces; i += kGemmThreads) piece_store(i, *piece_src(i));
+      for (int j = 0; j < kScalePieces; ++j) scv[j] = *piece_src(min(tid + j * kGemmThreads, npieces - 1));
     }
-  };
-  // this thread's activation loads: token row 16*wave + lane%16, quarter
-  // lane/16 of the row's stage (so that a wave's LDS stores are contiguous).
-  // Rows past the tile re-read its first row: their results are never stored.
-  const int arow = wave * 16 + r, apart = g;
-  const int apos = pos0 + (arow < ncols ? arow : 0);
-  const size_t atrow = p.act_row ? (size_t)p.act_row[apos] : (size_t)apos;
-  const uint16_t* asrc = p.act + atrow * p.act_ld + apart * (kBK / 4);
-  // fragment-major LDS: piece (token t, quarter q, k-step j) at 16 bytes x
-  // ((t/16 * kKK + j) * 64 + q * 16 + t%16), i.e. where lane (r = t%16, g =
-  // q) of the MFMAs of token block t/16 reads it
-  const int aslot = ((arow >> 4) * kKK) * 64 + apart * 16 + (arow & 15);
-  u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][aslot * 16]);
-  u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][aslot * 16]);
-  const unsigned char* abase0 = &lds_a[0][lane * 16];
-  const unsigned char* abase1 = &lds_a[1][lane * 16];
+    const int arow = wave * 16 + r;
+    auto store_scales = [&]() __attribute__((always_inline)) {
+      if (FMT == kFmtMx) {
+#pragma unroll
+        for (int j = 0; j < kScalePieces; ++j) {
+          const int i = tid + j * kGemmThreads;
+          if (i < npieces) piece_store(i, scv[j]);
+        }
+        for (int i = tid + kScalePieces * kGemmThreads; i < npieces; i += kGemmThreads)
+          piece_store(i, *piece_src(i));
+      }
+      atrow_n = act_row_of(rec_n, arow);  // the next tile's record came before these scales
+    };
+    // this thread's activation loads: token row arow, quarter lane/16 of
+    // the row's stage (so that a wave's LDS stores are contiguous)
+    const uint16_t* asrc = p.act + (size_t)atrow * p.act_ld + g * (kBK / 4);
+    // fragment-major LDS: piece (token t, quarter q, k-step j) at 16 bytes x
+    // ((t/16 * kKK + j) * 64 + q * 16 + t%16), i.e. where lane (r = t%16, g =
+    // q) of the MFMAs of token block t/16 reads it
+    const int aslot = ((arow >> 4) * kKK) * 64 + g * 16 + (arow & 15);
+    u32x4_t* adst0 = reinterpret_cast<u32x4_t*>(&lds_a[0][aslot * 16]);
+    u32x4_t* adst1 = reinterpret_cast<u32x4_t*>(&lds_a[1][aslot * 16]);
+    const unsigned char* abase0 = &lds_a[0][lane * 16];
+    const unsigned char* abase1 = &lds_a[1][lane * 16];
 
-  // a tile runs the MFMAs of its positions rounded up to 32 (uniform branch:
-  // partly filled last tiles of the experts would otherwise waste about a
-  // sixth of the work at prefill)
-  switch ((ncols + 31) >> 5) {
-    case 1:
-      gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales, slot_r);
-      break;
-    case 2:
-      gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales, slot_r);
-      break;
-    case 3:
-      gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt, wn,
-                              g, r, store_scales, slot_r);
-      break;
-    default:
-      gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
+    // a tile runs the MFMAs of its positions rounded up to 32 (uniform
+    // branch: partly filled last tiles of the experts would otherwise waste
+    // about a sixth of the work at prefill)
+    switch ((ncols + 31) >> 5) {
+      case 1:
+        gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
                                 wn, g, r, store_scales, slot_r);
+        break;
+      case 2:
+        gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
+                                wn, g, r, store_scales, slot_r);
+        break;
+      case 3:
+        gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
+                                wn, g, r, store_scales, slot_r);
+        break;
+      default:
+        gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0,
+                                  nt, wn, g, r, store_scales, slot_r);
+    }
+    if (tid == 0) grabbed = lo + 2 * nx + grab;
+    __syncthreads();  // every wave is done with this tile's LDS; the grab is visible
+    cur = nxt;
+    nxt = __builtin_amdgcn_readfirstlane(grabbed);
+    rec = rec_n;
+    atrow = atrow_n;
+  }
+  // the last block out sets the counters back to zero for the next launch
+  if (threadIdx.x == 0 && atomicAdd(q + 8, 1) == G - 1) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) q[i] = 0;
   }
 }
 
@@ -415,12 +454,23 @@ static hipError_t launch_gemm_t(const GemmArgs& p, int tiles, hipStream_t st) {
     if (e != hipSuccess) return e;
     raised = dyn;
   }
-  k_gemm<FMT, MODE><<<(unsigned)nblk, kGemmThreads, dyn, st>>>(p);
+  // persistent: at most the blocks that fit on the chip at once
+  static int resident = 0;  // per kernel: blocks per CU x CUs
+  if (resident == 0) {
+    int per_cu = 0, dev = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm<FMT, MODE>, kGemmThreads, dyn);
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    resident = per_cu * cus > 0 ? per_cu * cus : 1;
+  }
+  const long long grid = nblk < resident ? nblk : resident;
+  k_gemm<FMT, MODE><<<(unsigned)grid, kGemmThreads, dyn, st>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st) {
-  if (p.K % 128 || p.K <= 0) return hipErrorInvalidValue;
+  if (p.K % 128 || p.K <= 0 || !p.queue) return hipErrorInvalidValue;
   if (p.fmt == kFmtMx) {
     if (p.mode == kGemmW13) return launch_gemm_t<kFmtMx, kGemmW13>(p, tiles, st);
     return launch_gemm_t<kFmtMx, kGemmW2>(p, tiles, st);

@@ -151,6 +151,7 @@ struct GemmArgs {
   const int32_t* sorted_slots;
   const float* slot_w;
   const uint16_t* ybuf;       // combine: [T*k][H] bf16
+  int* queue;                 // [9] tile counters per XCD and blocks done: zero before the launch, left zero
   int topk;
   void* out;
   int out_ld, out_is_fp32;
@@ -179,6 +180,10 @@ hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, int* ar
 // then the streaming passes' two unit counters.
 constexpr int kArrivalsInt = 16;
 constexpr int kQueueInts = 17;
+// the grouped GEMMs' tile queues, 9 ints per launch: routed w13, shared w13,
+// routed w2, shared w2 + combine
+constexpr int kGemmQueueInts = 24;
+enum { kQRoutedW13 = 0, kQSharedW13 = 1, kQRoutedW2 = 2, kQSharedW2 = 3 };
 // Large-T learned router on bf16 MFMA (fp32 router rows split into three
 // bf16 planes, wsplit [3][E][H]; partial logits plog [KS][T][E] with KS =
 // router_mfma_splits(T, H)).
