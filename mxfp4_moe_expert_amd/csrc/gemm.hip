@@ -6,7 +6,7 @@
 // the k weighted routed outputs of the token in slot order (row "Shared
 // expert": routed + shared).
 //
-// Block: 8 waves, output tile of 256 weight rows x 128 token positions.
+// Tile: 256 weight rows x 128 token positions, one block of 8 waves.
 // Wave w owns 32 weight rows (2 blocks of 16) x all 128 positions (8 blocks
 // of 16): 16 MFMA 16x16x32 accumulators, so each weight fragment converted
 // to bf16 feeds 8 MFMAs (on gfx950 VALU work and MFMAs share a SIMD's issue
@@ -31,8 +31,13 @@
 //   - MFMA k-step kk of a stage takes the lane's K-values 8kk .. +8 of its
 //     quarter on both operands (a fixed permutation of K, so the dot products
 //     are unchanged).
-//   - blocks are ordered so that each XCD (block % 8) walks a contiguous run of
-//     tiles with the N tiles of one token tile adjacent (L2 reuse of tokens).
+//   - persistent: one block per CU walks tiles. Each XCD (block % 8) owns a
+//     contiguous run of the tiles with the N tiles of one token tile
+//     adjacent (L2 reuse of tokens), handed out by a counter per XCD; a
+//     block knows its next tile while the current one computes and requests
+//     that tile's record and gathered row ids meanwhile (with one block per
+//     tile, that chain of two dependent loads ran before every tile's first
+//     MFMA).
 #include <type_traits>
 
 #include "device.h"
