@@ -481,6 +481,9 @@ def main():
     roof["traffic"] = traffic
     roof["kernel"] = DOMINANT[args.workload][0]
     roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
+    ks = sorted(kern_ms)
+    roof["kernel_p50_us"] = round(ks[len(ks) // 2] * 1e3, 2)
+    roof["kernel_p99_us"] = round(ks[min(len(ks) - 1, (len(ks) * 99) // 100)] * 1e3, 2)
     layer_bw = alg["layer_bytes"] / (ms_step / 1e3) / 1e9
     layer_tf = alg["layer_flops"] / (ms_step / 1e3) / 1e12
 
