@@ -21,7 +21,7 @@
 //
 // The weight stream of a block is one in-order sequence: shared w13 (with
 // the router row), shared w2 once the block's score is published, the
-// routed w13 jobs with three in flight, the first three routed w2 jobs
+// routed w13 jobs with two in flight per wave, the first three routed w2 jobs
 // (they arrive while the block reduces and publishes its h slices, when the
 // CU's loads would otherwise pause), then, once the block's h slices are
 // published, the other routed w2 jobs, which stream while the other blocks'
@@ -64,7 +64,7 @@ struct LayerShape {
   static constexpr int H = 1024 * NH, I = 1024 * NI;
   static constexpr int NS = TT * KK, NCOL = NS + TT;
   static constexpr int XPT = H / kLayerThreads;  // x / router elements per thread
-  static constexpr int P = 3;                    // routed w13 jobs in flight
+  static constexpr int P = 2;                    // routed w13 jobs in flight per wave (1: 27.1 us, 3: 27.6)
   static constexpr int HROW = I * 2 + 16;        // LDS row of an h column
   static constexpr int ZROW = (H > I ? H : I) * 2;  // LDS zero row: the B operand of inactive lanes
   static constexpr size_t off_zero = (size_t)TT * H * 2;
