@@ -495,9 +495,71 @@ def check_forward_tiny():
     assert np.array_equal(sub["ids"], r["ids"][[3, 7, 0]])
 
 
+def _np_layer_rows(L, xd, ids, w):
+    """numpy composition of the layer for given expert ids and weights per row:
+    sum_j w_j * expert_{ids_j}(x) + shared(x), h not rounded."""
+    I = L.wl.I
+    S13 = L.sh_w13.astype(np.float64) * L.sh_w13_scale.astype(np.float64)[:, None]
+    S2 = L.sh_w2.astype(np.float64) * L.sh_w2_scale.astype(np.float64)[:, None]
+    out = np.zeros((len(ids), L.wl.H))
+    for r in range(len(ids)):
+        for j, e in enumerate(ids[r]):
+            y, _, _ = np_expert(xd[r], L.w13_codes[e], L.w13_scales[e], L.w2_codes[e], L.w2_scales[e], False)
+            out[r] += w[r, j] * y
+        out[r] += np_swiglu(S13[:I] @ xd[r], S13[I:] @ xd[r]) @ S2.T
+    return out
+
+
+def check_forward_forced_ids():
+    """Forced expert ids (used to grade near-tie tokens): the oracle must take
+    exactly the given experts, weight them by their own renormalised scores
+    (x 1.5), and compose those experts with the shared expert; on a subset of
+    rows the forced row r belongs to requested token rows[r]."""
+    L = synth.make_layer(synth.WORKLOADS["tiny"])
+    wl = L.wl
+    x = synth.make_tokens(wl, rep=3)
+    rows = np.array([9, 2, 14, 0], np.int32)
+    rng = _rng(12)
+    full = oracle.forward(L, x, rows=rows, round_h=False)
+    forced = np.stack([rng.choice(wl.E, size=wl.k, replace=False) for _ in rows]).astype(np.int32)
+    # at least one forced set must differ from the top-k, or the check is empty
+    assert any(set(forced[r]) != set(full["ids"][r]) for r in range(len(rows)))
+    r = oracle.forward(L, x, rows=rows, force_ids=forced, round_h=False)
+    assert np.array_equal(r["ids"], forced)
+    xd = bf16_to_f64(x[rows])
+    s = np_score(xd @ L.gate_w.astype(np.float64).T)
+    w = np.stack([1.5 * s[i, forced[i]] / s[i, forced[i]].sum() for i in range(len(rows))])
+    assert np.allclose(r["w"], w, rtol=1e-13, atol=0)
+    want = _np_layer_rows(L, xd, forced, w)
+    assert np.allclose(r["out"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def check_forward_hash():
+    """The whole hash-routed layer: experts are the table row of each token's
+    id (table order), weights their renormalised scores x 1.5 with no bias,
+    composed with the shared expert; checked on a subset of rows so the row
+    of each output is that of the requested token."""
+    wl = synth.Workload("tinyhash", T=16, H=256, E=16, k=6, I=128, V=40, hash_layer=True, seed=2)
+    L = synth.make_layer(wl)
+    x = synth.make_tokens(wl, rep=1)
+    tids = synth.make_token_ids(wl, rep=1)
+    rows = np.array([11, 3, 7, 15, 0], np.int32)
+    assert len(set(tids[rows].tolist())) > 1
+    r = oracle.forward(L, x, token_ids=tids, rows=rows, round_h=False)
+    assert np.array_equal(r["ids"], L.tid2eid[tids[rows]])
+    xd = bf16_to_f64(x[rows])
+    s = np_score(xd @ L.gate_w.astype(np.float64).T)
+    ids = L.tid2eid[tids[rows]]
+    w = np.stack([1.5 * s[i, ids[i]] / s[i, ids[i]].sum() for i in range(len(rows))])
+    assert np.allclose(r["w"], w, rtol=1e-13, atol=0)
+    want = _np_layer_rows(L, xd, ids, w)
+    assert np.allclose(r["out"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
 ALL_CHECKS = [
     check_e2m1_codes, check_e8m0_bytes, check_mxfp4_layout, check_block_bytes, check_bf16_values,
     check_softplus_score, check_swiglu, check_topk_exhaustive, check_topk_random, check_fp32_decision,
     check_noaux_bias, check_weights_sum, check_hash_route, check_permute, check_expert_ffn,
     check_shared_ffn, check_linearity, check_special_case_dense, check_forward_tiny,
+    check_forward_forced_ids, check_forward_hash,
 ]

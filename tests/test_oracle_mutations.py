@@ -65,6 +65,21 @@ MUTATIONS = [
      " if (i % 2) { int32_t q = offsets[ids[i] + 1] - 1 - (p - offsets[ids[i]]); p = q; }"),
     ("block_bytes_no_scale", "return ((int64_t)bits * group + scale_bits) / 8;",
      "return ((int64_t)bits * group) / 8;"),
+    ("force_ids_ignored", "for (int j = 0; j < k; ++j) ids[j] = force_ids[j];",
+     "nxt = topk_desc(b, E, k, ids);"),
+    ("force_weights_from_topk", "for (int j = 0; j < k; ++j) ids[j] = force_ids[j];",
+     "int32_t tk[64]; topk_desc(b, E, k, tk); double st[64];"
+     " for (int j = 0; j < k; ++j) st[j] = s[tk[j]];"
+     " for (int j = 0; j < k; ++j) { ids[j] = force_ids[j]; s[ids[j]] = st[j]; }"),
+    ("force_row_of_token", "force_ids ? force_ids + (int64_t)r * k : NULL",
+     "force_ids ? force_ids + (int64_t)(t % n_rows) * k : NULL"),
+    ("forward_hash_wrong_row", "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);",
+     "tid2eid + (int64_t)((tids[t] + 1) % V) * k, scale, idr, wr);"),
+    ("forward_hash_row_of_output", "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);",
+     "tid2eid + (int64_t)tids[r] * k, scale, idr, wr);"),
+    ("forward_hash_uses_bias", "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);",
+     "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);"
+     " for (int j = 0; j < k; ++j) wr[j] *= 1.0 + 0.5 * (double)bias[idr[j]];"),
 ]
 
 
