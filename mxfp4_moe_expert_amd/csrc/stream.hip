@@ -291,8 +291,12 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
         accB = mfma_16x16x32(stream_frag<FMT>(wB[i], kk, scaleB), b[kk], accB);
       }
     };
+    // Main loop: consume stages st0 .. st0+D-1, request st0+D .. st0+2D-1.
+    // Every requested stage is below S by the loop condition; the launchers
+    // require S to be a multiple of D (and S >= D), so the loop ends with
+    // st0 = S - D and the last D stages below cover the rest exactly.
     int st0 = 0;
-    for (; st0 + D < S; st0 += D) {  // S is a multiple of D
+    for (; st0 + 2 * D <= S; st0 += D) {
 #pragma unroll
       for (int i = 0; i < D; i += P) {
 #pragma unroll
@@ -489,12 +493,23 @@ static int stream_resident(const void* k, size_t lds) {
   return per_cu * cus;
 }
 
+// The stage loop of stream_loop needs the stage count S = K / 128 to be a
+// multiple of the stage depth D and at least D: the main loop steps D stages
+// at a time and the last D stages (and the next unit's first D, or the
+// re-read of the last D) are handled after it.
+inline bool stream_depth_ok(int K, int D) {
+  const int S = K >> 7;
+  return K % 128 == 0 && S >= D && S % D == 0;
+}
+
 template <int MODE, int DA, int DB>
 static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks, int* queue,
                                   hipStream_t st) {
   const long long nblk = (long long)a_blocks + b_blocks;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x3fffffffLL || !queue) return hipErrorInvalidValue;
+  if ((a_blocks > 0 && !stream_depth_ok(a.K, DA)) || (b_blocks > 0 && !stream_depth_ok(b.K, DB)))
+    return hipErrorInvalidValue;
   if ((a_blocks > 0 && (a.tile_n > 16 || a.tile_n < 1 || !a.tile_rec)) ||
       (b_blocks > 0 && (b.tile_n > 16 || b.tile_n < 1)))
     return hipErrorInvalidValue;
@@ -535,12 +550,16 @@ hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, con
       b13.tile_n != b2.tile_n || b13.n_tiles_grid != b2.n_tiles_grid || a13.tile_n > 16 || b13.tile_n > 16 ||
       a13.tile_n < 1 || b13.tile_n < 1 || a_blocks13 <= 0 || b_blocks13 <= 0)
     return hipErrorInvalidValue;
+  constexpr int kDA = 8, kDB = 4;  // stage depths of k_stream_fused<kDA, kDB>
+  if (!stream_depth_ok(a13.K, kDA) || !stream_depth_ok(a2.K, kDA) || !stream_depth_ok(b13.K, kDB) ||
+      !stream_depth_ok(b2.K, kDB))
+    return hipErrorInvalidValue;
   const long long nblk = (long long)a_blocks13 + b_blocks13 + a_blocks2 + b_blocks2;
   if (nblk > 0x3fffffffLL) return hipErrorInvalidValue;
   size_t lds = stream_lds(a13, a_blocks13, b13, b_blocks13);
   const size_t l2 = stream_lds(a2, a_blocks2, b2, b_blocks2);
   lds = l2 > lds ? l2 : lds;
-  auto kern = &k_stream_fused<8, 4>;
+  auto kern = &k_stream_fused<kDA, kDB>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

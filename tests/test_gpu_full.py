@@ -93,11 +93,45 @@ def test_decode_t64_full(full_layer):
     assert len(set(ids.ravel().tolist())) > 100
 
 
+def _stratified_rows(ids, k, n, seed, tile=128, top=4, per=8):
+    """Rows to compare at a large T: the first and last tokens, tokens whose
+    slots sit in the last (partial) 128-position tile of the `top` most-loaded
+    experts and in their first tile, then uniform random tokens up to n."""
+    T = ids.shape[0]
+    flat = ids.ravel()
+    counts = np.bincount(flat, minlength=int(flat.max()) + 1)
+    picks = [0, 1, T - 2, T - 1]
+    rng = np.random.default_rng(seed)
+    for e in np.argsort(-counts, kind="stable")[:top]:
+        slots = np.nonzero(flat == e)[0]  # ascending slot order = sorted positions of expert e
+        last0 = ((len(slots) - 1) // tile) * tile
+        tail = slots[last0:] // k
+        head = slots[:tile] // k
+        picks += rng.choice(tail, size=min(per, len(tail)), replace=False).tolist()
+        picks += rng.choice(head, size=min(per // 2, len(head)), replace=False).tolist()
+    picks = np.unique(np.array(picks, np.int64))
+    rest = np.setdiff1d(np.arange(T), picks)
+    fill = rng.choice(rest, size=max(0, n - len(picks)), replace=False)
+    return np.sort(np.concatenate([picks, fill])).astype(np.int32)
+
+
+def _gpu_ids(wl, Dv, rep):
+    cfg = mx.config_of(wl)
+    x = mx.bf16_from_numpy(synth.make_tokens(wl, rep=rep), DEV)
+    tids = torch.from_numpy(synth.make_token_ids(wl, rep=rep)).to(DEV) if wl.hash_layer else None
+    _, (ids, _) = mx.forward(cfg, x, Dv, token_ids=tids, return_routing=True)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy()
+
+
 def test_prefill_t8192_full_sampled(full_layer):
+    """256 stratified rows, including the ragged last tiles of the most-loaded
+    experts (the persistent GEMM's tile queue runs at this size)."""
     L, D = full_layer
     wl = synth.WORKLOADS["prefill_t8192"]
     Lv, Dv = _variant(L, D, wl)
-    rows = np.unique(np.concatenate([[0, 1, 4095, 8190, 8191], np.random.default_rng(0).integers(0, 8192, 11)]))
+    rows = _stratified_rows(_gpu_ids(wl, Dv, 0), wl.k, 256, seed=0)
+    assert len(rows) >= 256
     ids = _run(wl, Lv, Dv, 0, rows=rows)
     counts = np.bincount(ids.ravel(), minlength=256)
     assert counts.max() > 2 * counts.mean()  # the offsets skew the loads
@@ -107,5 +141,6 @@ def test_hash_t4096_full_sampled(full_layer):
     L, D = full_layer
     wl = synth.WORKLOADS["hash_t4096"]
     Lv, Dv = _variant(L, D, wl)
-    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(1).integers(0, 4096, 10)]))
+    rows = _stratified_rows(_gpu_ids(wl, Dv, 0), wl.k, 128, seed=1)
+    assert len(rows) >= 128
     _run(wl, Lv, Dv, 0, rows=rows)

@@ -86,6 +86,33 @@ def test_forward_hash_gemm_matches_oracle(mid):
     assert_outputs_close(out.cpu().numpy(), r["out"], "forward mid hash")
 
 
+def test_forward_gemm_tile_queue_every_row(mid):
+    """4096 tokens: the live 128-position tiles (about 6 * 4096 / 128 + 32 per
+    N tile, times 3 or 2 N tiles) are several times the persistent grid, so
+    blocks take tiles from the per-XCD queues past their first fixed ones;
+    every output row is compared, and a second call on the same workspace
+    (queue counters reset by the last block out) must repeat the bits."""
+    wl, L, D, cfg = mid
+    T = 4096
+    print(f"[forward mid T={T} tile queue]", flush=True)
+    xh, x = _x(wl, T, rep=41)
+    out, (ids, w) = mx.forward(cfg, x, D, out_fp32=True, return_routing=True)
+    again = mx.forward(cfg, x, D, out_fp32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    ids_h = ids.cpu().numpy()
+    counts = np.bincount(ids_h.ravel(), minlength=wl.E)
+    live = int(np.sum((counts + 127) // 128))
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    assert live * (wl.I // 128) > 2 * grid, (live, grid)
+    rows = np.arange(T, dtype=np.int32)
+    r, ref = reference_rows(L, xh, rows)
+    rt = compare_routing(ids_h, w.cpu().numpy(), r["ids"], r["w"], r["gap"], r["next"])
+    if rt["alt_rows"]:
+        r, ref = reference_rows(L, xh, rows, routing=rt)
+    assert_outputs_close(out.cpu().numpy(), ref, f"forward mid T={T}")
+
+
 def test_forward_gemm_deterministic(mid):
     wl, L, D, cfg = mid
     xh, x = _x(wl, 500, rep=2)
