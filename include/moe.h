@@ -42,8 +42,15 @@
  *   - The return value reports host-side argument checks and launch errors
  *     only: MOE_OK, or a negative MOE_E* code, in which case nothing was
  *     launched (argument errors) or a launch failed (MOE_EHIP).
- *   - Device-side values are trusted: expert ids must lie in [0, E), token
- *     ids in [0, V); E8M0 scale bytes should not be 0xFF (NaN).
+ *   - Device-side values are checked where an index comes from the caller:
+ *     a token id outside [0, V), a tid2eid entry outside [0, E), an expert
+ *     id outside [0, E) given to moe_permute, or an inconsistent permutation
+ *     given to moe_expert_ffn is never used to index memory. The kernels
+ *     substitute an in-range value (token row 0, expert 0, slot 0), write NaN
+ *     routing weights for such a hash-layer token, and set a bit of the
+ *     device error flags (MOE_FLAG_*, read with moe_device_flags); the
+ *     return code cannot report them, since it is produced before the
+ *     kernels run. E8M0 scale bytes should not be 0xFF (NaN).
  *   - `workspace` is device scratch of at least moe_workspace_size() bytes,
  *     256-byte aligned. Zero-fill it once before its first use
  *     (moe_workspace_init, or any zero fill): bytes 64 .. 67 count the
@@ -51,10 +58,13 @@
  *     queues of the grouped GEMMs (MOE_SCHED_LARGE), and bytes 256 ..
  *     136447 hold the hand-off state of the single-launch layer
  *     (MOE_SCHED_SINGLE); every call leaves all three ready for the next,
- *     and every other workspace value is written before it is read. Calls that share one workspace must be
- *     ordered on one stream. If a single-launch call's bounded wait for
- *     another block of its grid expires (about a second), its output is
- *     NaN; the hand-off state stays consistent.
+ *     and every other workspace value is written before it is read. Calls
+ *     that share one workspace must be ordered on one stream. If a bounded
+ *     wait of one block for another block of the same launch expires (about
+ *     a second; it does not happen when the whole grid is resident, which
+ *     the launchers check), the outputs that depend on it are NaN, the
+ *     device flag MOE_FLAG_WAIT_EXPIRED is set, and the hand-off state stays
+ *     consistent for the next call.
  *   - Supported shapes: H and I multiples of 128, 1 <= top_k <= 8,
  *     top_k <= E <= 256, 0 <= T <= 65536. Device pointers must be 16-byte
  *     aligned.
@@ -86,6 +96,22 @@ enum {
   MOE_EWORKSPACE = -3,   /* workspace too small */
   MOE_EHIP = -4          /* a HIP launch or runtime call failed */
 };
+
+/* Device error flags: bits of a word kept by the library in device memory,
+ * one per GPU, set by kernels (atomic OR) and cleared only by
+ * moe_device_flags(..., clear = 1, ...). */
+enum {
+  MOE_FLAG_TOKEN_ID = 1,      /* a hash-layer token id outside [0, V) */
+  MOE_FLAG_TABLE_ENTRY = 2,   /* a tid2eid entry outside [0, E) */
+  MOE_FLAG_EXPERT_ID = 4,     /* an expert id outside [0, E) given to moe_permute */
+  MOE_FLAG_WAIT_EXPIRED = 8,  /* a bounded wait between blocks of one launch expired */
+  MOE_FLAG_PERMUTATION = 16   /* offsets or sorted slots given to moe_expert_ffn are inconsistent */
+};
+
+/* Reads the current device's error flags into *flags (if not NULL) after the
+ * work queued on `stream` so far, and clears them if clear != 0. Waits for
+ * the stream (host synchronisation): a diagnostic, not for the hot path. */
+int moe_device_flags(uint32_t* flags, int32_t clear, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(int status);

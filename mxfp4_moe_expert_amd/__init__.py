@@ -64,6 +64,7 @@ _SIGNATURES = {
     "moe_expert_ffn": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                        ctypes.c_int),
     "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
+    "moe_device_flags": ([ctypes.POINTER(ctypes.c_uint32), _I32, _VP], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                      _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
@@ -131,6 +132,18 @@ def set_kernel_events(kernel: str | None, start_event=None, stop_event=None):
     hipEvent_t handles (ints or c_void_p); None stops. Measurement only."""
     kid = 0 if kernel is None else KERNELS[kernel]
     _check(lib().moe_set_kernel_events(kid, start_event, stop_event), "moe_set_kernel_events")
+
+
+FLAGS = {"token_id": 1, "table_entry": 2, "expert_id": 4, "wait_expired": 8, "permutation": 16}
+
+
+def device_flags(clear: bool = False, device=None) -> set:
+    """Names of the device error flags (``FLAGS``) set on the current device
+    by work queued so far on the current stream; waits for that stream.
+    ``clear`` resets them afterwards."""
+    v = ctypes.c_uint32(0)
+    _check(lib().moe_device_flags(ctypes.byref(v), 1 if clear else 0, _stream(device)), "moe_device_flags")
+    return {name for name, bit in FLAGS.items() if v.value & bit}
 
 
 SCHEDULES = {1: "single", 2: "tiny", 3: "decode", 4: "large"}

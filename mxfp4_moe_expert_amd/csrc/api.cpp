@@ -156,6 +156,7 @@ Perm perm_of(void* ws, const Layout& L, int32_t* offsets, int32_t* sorted, int32
   p.done = at<int32_t>(ws, L.done);
   p.tile_n = L.tile_n;
   p.max_tiles = L.max_tiles;
+  p.flags = device_flags();
   return p;
 }
 
@@ -164,6 +165,7 @@ SkinnyArgs skinny_common(const moe_config& c, int T) {
   memset(&a, 0, sizeof(a));
   a.T = T;
   a.limit = c.swiglu_limit;
+  a.flags = device_flags();
   return a;
 }
 
@@ -420,7 +422,20 @@ const char* moe_status_string(int s) {
   }
 }
 
-const char* moe_version(void) { return "0.1.0"; }
+const char* moe_version(void) { return "0.2.0"; }
+
+int moe_device_flags(uint32_t* flags, int32_t clear, void* stream) {
+  uint32_t* f = device_flags();
+  if (!f) return MOE_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, f, sizeof(v), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && clear) e = launch_fill_zero(f, sizeof(uint32_t), st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (flags) *flags = v;
+  return MOE_OK;
+}
 
 int moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
   if (kernel_id < MOE_KERNEL_NONE || kernel_id > MOE_KERNEL_COMBINE) return MOE_EINVAL;
@@ -487,6 +502,7 @@ int moe_hash_route(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   a.gate_w = gate_w;
   a.ids = topk_ids;
   a.w = topk_w;
+  a.flags = device_flags();
   return status(launch_hash_route(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -524,9 +540,10 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(*cfg, T);
-  Perm p = perm_of(workspace, L, const_cast<int32_t*>(expert_offsets), const_cast<int32_t*>(sorted_slots),
+  // the caller's permutation is checked and copied into the workspace
+  Perm p = perm_of(workspace, L, at<int32_t>(workspace, L.offsets), at<int32_t>(workspace, L.sorted),
                    at<int32_t>(workspace, L.slot_pos));
-  rc = status(launch_tiles_from_offsets(T, cfg->n_routed_experts, cfg->top_k, p, st));
+  rc = status(launch_tiles_from_offsets(T, cfg->n_routed_experts, cfg->top_k, expert_offsets, sorted_slots, p, st));
   if (rc) return rc;
   uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
   float* ybuf = at<float>(workspace, L.ybuf);
@@ -646,6 +663,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     la.ids_out = ids;
     la.w_out = w;
     la.xfer = at<uint32_t>(workspace, L.xfer);
+    la.flags = p.flags;
     return status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_layer_small(la, st); }));
   }
   if (tiny) {
@@ -725,6 +743,7 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       h.gate_w = gate_w;
       h.ids = ids;
       h.w = w;
+      h.flags = p.flags;
       rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_hash_route(h, st); }));
     } else {
       RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);

@@ -529,6 +529,7 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     for (int j = 0; j < KK; ++j) o += L.sw[t * KK + j] * L.ycol[rr * 16 + t * KK + j];
     o += s2n * L.ycol[rr * 16 + NS + t];
     if (!ok) o = __builtin_nanf("");  // a hand-off timed out: never a silent wrong value
+    if (!ok && tid == 0 && a.flags) atomicOr(a.flags, kFlagWaitExpired);
     if (b < H / 16) {
       if (a.out_is_fp32) static_cast<float*>(a.out)[(size_t)t * H + n] = o;
       else static_cast<uint16_t*>(a.out)[(size_t)t * H + n] = f32_to_bf16(o);

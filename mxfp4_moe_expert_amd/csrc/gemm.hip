@@ -287,6 +287,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   // tiles ahead, so that while a tile computes the block already knows the
   // next one and requests its record and gathered row ids.
   const int nblk = p.routed ? *p.n_tiles * p.n_ntiles : ((p.T + kBM - 1) / kBM) * p.n_ntiles;
+  if (nblk <= 0) return;  // no tiles (a rejected permutation): the whole grid leaves, the queue untouched
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, inx = blockIdx.x >> 3;
   const int nx = (G - xcd + 7) >> 3;  // blocks on this XCD

@@ -29,6 +29,7 @@ struct Perm {
   int32_t* done;          // [max_tiles + kSmallT] finished w13 units per routed, then shared, tile
   int tile_n;
   int max_tiles;
+  uint32_t* flags;        // device error-flag word (MOE_FLAG_* bits)
 };
 
 // Tile record, one per routed tile, written with the tile table at decode
@@ -64,6 +65,7 @@ struct HashArgs {
   const float* gate_w;
   int32_t* ids;
   float* w;
+  uint32_t* flags;  // device error-flag word: out-of-range token ids / table entries
 };
 
 // One expert GEMM pass on the "skinny" kernel: 16 weight rows per block (for
@@ -105,6 +107,7 @@ struct SkinnyArgs {
   int E, topk;
   int32_t* ids_out;           // [T][k]
   float* w_out;               // [T][k]
+  uint32_t* flags;            // device error-flag word (expired waits of the fused passes)
 };
 
 // Routed w2 + shared w2 + combine for T*(k+1) <= 16 ("output-stationary"):
@@ -199,7 +202,13 @@ hipError_t launch_hash_route(const HashArgs& a, hipStream_t st);
 // Permutation and tiles
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p, int32_t* blk_counts,
                           hipStream_t st);
-hipError_t launch_tiles_from_offsets(int T, int E, int k, const Perm& p, hipStream_t st);
+// Tile table from a permutation given by the caller: user_offsets and
+// user_sorted are checked (offsets from 0 to T*k, non-decreasing; slots in
+// [0, T*k)) and copied into p.offsets / p.sorted_slots, so the expert
+// kernels never index with a caller's value; a violation sets
+// kFlagPermutation and leaves no tiles (or the slot clamped).
+hipError_t launch_tiles_from_offsets(int T, int E, int k, const int32_t* user_offsets, const int32_t* user_sorted,
+                                     const Perm& p, hipStream_t st);
 // Expert passes; `b` (optional) runs in the same launch as `a`
 hipError_t launch_w13(const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks, bool b_is_shared_w2,
                       hipStream_t st);
@@ -255,11 +264,19 @@ struct LayerArgs {
   int32_t* ids_out;            // [T][k]
   float* w_out;                // [T][k]
   uint32_t* xfer;              // hand-off region (kXferBytes, workspace)
+  uint32_t* flags;             // device error-flag word (expired hand-off waits)
 };
 // Whether the single-launch layer has a kernel for this shape whose whole
 // grid the current device holds at once.
 bool layer_small_supported(int H, int I, int E, int T, int k);
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Device error flags (values of MOE_FLAG_* in moe.h), one word per GPU in
+// library-owned device memory; the address for the current device, or null
+// if it cannot be obtained.
+constexpr uint32_t kFlagTokenId = 1u, kFlagTableEntry = 2u, kFlagExpertId = 4u, kFlagWaitExpired = 8u,
+                   kFlagPermutation = 16u;
+uint32_t* device_flags();
 
 }  // namespace moe

@@ -48,7 +48,14 @@ __global__ __launch_bounds__(256) void k_perm_count(PermArgs a) {
   hist[tid] = 0;
   __syncthreads();
   const int beg = b * kPermBlock, end = min(n, beg + kPermBlock);
-  for (int i = beg + tid; i < end; i += 256) atomicAdd(&hist[a.ids[i]], 1);
+  bool bad = false;
+  for (int i = beg + tid; i < end; i += 256) {
+    const int e = a.ids[i];
+    const bool ok = (unsigned)e < (unsigned)a.E;  // an id outside [0, E) counts as expert 0, flagged
+    bad = bad || !ok;
+    atomicAdd(&hist[ok ? e : 0], 1);
+  }
+  if (bad && a.p.flags) atomicOr(a.p.flags, kFlagExpertId);
   __syncthreads();
   if (tid < a.E) a.blk_counts[(size_t)b * a.E + tid] = hist[tid];
 }
@@ -98,7 +105,8 @@ __global__ __launch_bounds__(256) void k_perm_scatter(PermArgs a) {
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int c0 = beg; c0 < end; c0 += 256) {
     const int i = c0 + tid;
-    const int e = i < end ? a.ids[i] : -1;
+    int e = i < end ? a.ids[i] : -1;
+    if (i < end && (unsigned)e >= (unsigned)a.E) e = 0;  // as in k_perm_count
     unsigned long long m = __ballot(e >= 0);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
@@ -127,19 +135,40 @@ __global__ __launch_bounds__(256) void k_perm_scatter(PermArgs a) {
 }
 
 // Tile table and token-of-position from expert offsets and sorted slots given
-// by the caller (moe_expert_ffn): block 0 writes the tiles, every block a
-// slice of sorted_tok.
-__global__ __launch_bounds__(256) void k_tiles_from_offsets(int T, int E, int k, const int32_t* sorted_slots,
-                                                            Perm p) {
+// by the caller (moe_expert_ffn), copied into the workspace's permutation
+// after checking them: block 0 checks the offsets (0 first, T*k last,
+// non-decreasing) and writes the tiles (none if the check fails), every
+// block a slice of the sorted slots (each in [0, T*k), else clamped to 0)
+// and of sorted_tok. Any violation sets kFlagPermutation.
+__global__ __launch_bounds__(256) void k_tiles_from_offsets(int T, int E, int k, const int32_t* user_offsets,
+                                                            const int32_t* user_sorted, Perm p) {
   __shared__ int tmp[256];
+  __shared__ int bad;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0) {
-    const int c = tid < E ? p.offsets[tid + 1] - p.offsets[tid] : 0;
-    const int off = tid < E ? p.offsets[tid] : 0;
-    write_tiles(c, off, E, p, tmp);
-  }
   const int n = T * k;
-  for (int i = blockIdx.x * 256 + tid; i < n; i += gridDim.x * 256) p.sorted_tok[i] = sorted_slots[i] / k;
+  if (blockIdx.x == 0) {
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    const int lo = tid < E ? user_offsets[tid] : 0, hi = tid < E ? user_offsets[tid + 1] : 0;
+    if (tid < E && (hi < lo || lo < 0 || hi > n || (tid == 0 && lo != 0) || (tid == E - 1 && hi != n))) bad = 1;
+    __syncthreads();
+    const bool ok = bad == 0;
+    if (tid < E) p.offsets[tid] = ok ? lo : 0;
+    if (tid == 0) p.offsets[E] = ok ? n : 0;
+    if (!ok && tid == 0 && p.flags) atomicOr(p.flags, kFlagPermutation);
+    write_tiles(ok && tid < E ? hi - lo : 0, ok && tid < E ? lo : 0, E, p, tmp);
+  }
+  bool clamped = false;
+  for (int i = blockIdx.x * 256 + tid; i < n; i += gridDim.x * 256) {
+    int s = user_sorted[i];
+    if ((unsigned)s >= (unsigned)n) {
+      s = 0;
+      clamped = true;
+    }
+    p.sorted_slots[i] = s;
+    p.sorted_tok[i] = s / k;
+  }
+  if (clamped && p.flags) atomicOr(p.flags, kFlagPermutation);
 }
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, const Perm& p, int32_t* blk_counts,
@@ -169,11 +198,13 @@ hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_tiles_from_offsets(int T, int E, int k, const Perm& p, hipStream_t st) {
+hipError_t launch_tiles_from_offsets(int T, int E, int k, const int32_t* user_offsets, const int32_t* user_sorted,
+                                     const Perm& p, hipStream_t st) {
+  if (E > 256 || !user_offsets || !user_sorted) return hipErrorInvalidValue;  // one thread per expert
   const int n = T * k;
   int blocks = (n + 255) / 256;
   blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-  k_tiles_from_offsets<<<blocks, 256, 0, st>>>(T, E, k, p.sorted_slots, p);
+  k_tiles_from_offsets<<<blocks, 256, 0, st>>>(T, E, k, user_offsets, user_sorted, p);
   return hipGetLastError();
 }
 

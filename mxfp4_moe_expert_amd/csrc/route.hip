@@ -327,15 +327,27 @@ __global__ __launch_bounds__(256) void k_hash_route(HashArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= a.T) return;
-  const int32_t* row = a.tid2eid + (size_t)a.token_ids[t] * a.k;
+  // a token id outside [0, V) or a table entry outside [0, E) is flagged;
+  // the token then reads table row 0 / router row 0 (nothing is indexed out
+  // of range), keeps in-range ids and gets NaN weights
+  const int tok = a.token_ids[t];
+  const bool tok_ok = (unsigned)tok < (unsigned)a.V;
+  const int32_t* row = a.tid2eid + (size_t)(tok_ok ? tok : 0) * a.k;
   const uint16_t* xt = a.x + (size_t)t * a.H;
   float s[kMaxTopK];
+  int ids[kMaxTopK];
+  bool ent_ok = true;
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     s[j] = 0.0f;
+    ids[j] = 0;
     if (j >= a.k) continue;
-    const float* we = a.gate_w + (size_t)row[j] * a.H;
+    const int e = row[j];
+    const bool e_ok = (unsigned)e < (unsigned)a.E;
+    ent_ok = ent_ok && e_ok;
+    ids[j] = e_ok ? e : 0;
+    const float* we = a.gate_w + (size_t)ids[j] * a.H;
     float acc = 0.0f;
     for (int k0 = lane * 8; k0 < a.H; k0 += 512) {
       const uint4 xv = *reinterpret_cast<const uint4*>(xt + k0);
@@ -353,13 +365,19 @@ __global__ __launch_bounds__(256) void k_hash_route(HashArgs a) {
     s[j] = sqrtf(softplus(wave_sum(acc)));
     sum += s[j];
   }
+  const bool ok = tok_ok && ent_ok;
+  if (!ok && lane == 0 && a.flags) atomicOr(a.flags, (tok_ok ? 0u : kFlagTokenId) | (ent_ok ? 0u : kFlagTableEntry));
   if (lane < a.k) {
     float sj = s[0];
+    int ej = ids[0];
 #pragma unroll
     for (int j = 1; j < kMaxTopK; ++j)
-      if (j == lane) sj = s[j];
-    a.ids[(size_t)t * a.k + lane] = row[lane];
-    a.w[(size_t)t * a.k + lane] = a.scale * sj / sum;
+      if (j == lane) {
+        sj = s[j];
+        ej = ids[j];
+      }
+    a.ids[(size_t)t * a.k + lane] = ej;
+    a.w[(size_t)t * a.k + lane] = ok ? a.scale * sj / sum : __builtin_nanf("");
   }
 }
 

@@ -176,14 +176,21 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     if constexpr (FUSED && MODE == kW2) return (int)load_agent(reinterpret_cast<const uint32_t*>(done + tile_of(i)));
     else return 0;
   };
-  auto wait_tile = [&](int i, int seen) __attribute__((always_inline)) {
+  // returns false if the wait expired: the unit's outputs are then NaN and
+  // the device error flag is set (never a silent value from a stale h)
+  auto wait_tile = [&](int i, int seen) __attribute__((always_inline)) -> bool {
     if constexpr (FUSED && MODE == kW2) {
       int v = __builtin_amdgcn_readfirstlane(seen);
       for (int it = 0; v < done_target && it < (1 << 22); ++it) {
         __builtin_amdgcn_s_sleep(2);
         v = __builtin_amdgcn_readfirstlane(poll(i));
       }
+      if (v < done_target) {
+        if (threadIdx.x == 0 && p.flags) atomicOr(p.flags, kFlagWaitExpired);
+        return false;
+      }
     }
+    return true;
   };
   int pub = -1;  // FUSED w13: tile of the unit whose completion is counted at the next boundary
 
@@ -257,7 +264,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     stream_load<FMT>(qA, i, wA[i]);
     stream_load<FMT>(qB, i, wB[i]);
   }
-  wait_tile(idx[0], poll(idx[0]));
+  bool cur_ok = wait_tile(idx[0], poll(idx[0]));
   int poll_nxt = poll(idx[1]);
   load_ops(cur);
   store_ops(cur);
@@ -322,7 +329,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
       if (deep) __builtin_amdgcn_s_waitcnt((1 << 14) | (15 << 8) | (7 << 4));
       else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
     }
-    if (more) wait_tile(idx[1], poll_nxt);
+    const bool nxt_ok = more ? wait_tile(idx[1], poll_nxt) : true;
     load_ops(nxt);
     const int rec_after = rec_of(idx[2]);
     const int poll_after = poll(idx[2]);
@@ -372,11 +379,16 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
         const int n0 = cur.rg * kUnitRows + wave * 32 + 4 * g;
         float* dst;
         float4 ya, yb;
+        if (!cur_ok) wv = __builtin_nanf("");  // the wait for this unit's h expired
         if (FMT == kFmtMx) {
           ya = make_float4(accA[0] * wv, accA[1] * wv, accA[2] * wv, accA[3] * wv);
           yb = make_float4(accB[0] * wv, accB[1] * wv, accB[2] * wv, accB[3] * wv);
           dst = p.yout + (size_t)slot * p.yout_ld;
         } else {
+          if (!cur_ok) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ec[i] = __builtin_nanf("");
+          }
           ya = make_float4(accA[0] * ec[0], accA[1] * ec[1], accA[2] * ec[2], accA[3] * ec[3]);
           yb = make_float4(accB[0] * ec[4], accB[1] * ec[5], accB[2] * ec[6], accB[3] * ec[7]);
           dst = p.yout + (size_t)(cur.pos0 + r) * p.yout_ld;
@@ -399,6 +411,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     idx[2] = __builtin_amdgcn_readfirstlane(sh[0]);
     if (!more) break;
     cur = nxt;
+    cur_ok = nxt_ok;
     rec_nxt = rec_after;
     poll_nxt = poll_after;
     qA = nA;
