@@ -189,6 +189,29 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Its workspace is a fixed scratch array
+ * in the library's device memory, one per GPU, held until the process ends
+ * (moe_noalloc_max_bytes() bytes, 16 MiB: enough for T <= 64 at the full
+ * shape). The first call on a device zero-fills it on `stream` (and waits,
+ * unless the stream is being captured). It allocates nothing and calls no
+ * allocating routine. Every call on one GPU shares that GPU's scratch: calls
+ * that overlap in time on one GPU (different streams, no ordering) race;
+ * order them on one stream. Returns MOE_EWORKSPACE, launching nothing, when
+ * moe_workspace_size(cfg, T) exceeds the scratch; otherwise as moe_forward,
+ * with the same kernels and outputs. */
+int moe_forward_noalloc(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w,
+                        const float* bias, const float* logit_offset, const int32_t* token_ids,
+                        const int32_t* tid2eid, int32_t V, const uint8_t* w13_codes,
+                        const uint8_t* w13_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                        const int8_t* sh_w13, const float* sh_w13_scale, const int8_t* sh_w2,
+                        const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
+                        float* topk_w_out, void* stream);
+
+/* Size in bytes of moe_forward_noalloc's scratch (its largest workspace). */
+size_t moe_noalloc_max_bytes(void);
+
 /* The launch sequence moe_forward takes. */
 enum {
   MOE_SCHED_SINGLE = 1,  /* T <= 2, learned router, shapes with a single-launch kernel whose whole

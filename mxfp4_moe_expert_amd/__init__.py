@@ -66,6 +66,9 @@ _SIGNATURES = {
     "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
     "moe_device_flags": ([ctypes.POINTER(ctypes.c_uint32), _I32, _VP], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
+    "moe_noalloc_max_bytes": ([], _SZ),
+    "moe_forward_noalloc": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
+                             _VP, _VP, _VP, _I32, _VP, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                      _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -337,4 +340,32 @@ def forward(cfg: MoeConfig, x, layer: DeviceLayer, token_ids=None, out_fp32=Fals
         _ptr(ids), _ptr(w), _ptr(buf), nb, _stream(dev)), "moe_forward")
     if return_routing:
         return out, (ids, w)
+    return out
+
+
+def forward_noalloc(cfg: MoeConfig, x, layer: DeviceLayer, token_ids=None, out_fp32=False, out=None,
+                    routing_out=None):
+    """``forward`` through moe_forward_noalloc (no workspace: the library's
+    fixed per-GPU scratch). ``out`` and ``routing_out`` may be preallocated
+    so that the call itself allocates nothing."""
+    T, H, E, k, I = x.shape[0], cfg.hidden_size, cfg.n_routed_experts, cfg.top_k, cfg.moe_intermediate
+    dev = x.device
+    _need(x, _BF16, (T, H), "x")
+    _need(layer.w13_codes, torch.uint8, (E, 2 * I, H // 2), "w13_codes")
+    _need(layer.w2_codes, torch.uint8, (E, H, I // 2), "w2_codes")
+    _need(layer.sh_w13, torch.int8, (2 * I, H), "sh_w13")
+    _need(layer.sh_w2, torch.int8, (H, I), "sh_w2")
+    V = 0
+    if token_ids is not None:
+        _need(token_ids, torch.int32, (T,), "token_ids")
+        V = layer.tid2eid.shape[0]
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=dev)
+    ids, w = routing_out if routing_out is not None else (None, None)
+    _check(lib().moe_forward_noalloc(
+        ctypes.byref(cfg), T, _ptr(x), _ptr(layer.gate_w), _ptr(layer.bias), _ptr(layer.logit_offset),
+        _ptr(token_ids), _ptr(layer.tid2eid if token_ids is not None else None), V, _ptr(layer.w13_codes),
+        _ptr(layer.w13_scales), _ptr(layer.w2_codes), _ptr(layer.w2_scales), _ptr(layer.sh_w13),
+        _ptr(layer.sh_w13_scale), _ptr(layer.sh_w2), _ptr(layer.sh_w2_scale), _ptr(out), int(out_fp32),
+        _ptr(ids), _ptr(w), _stream(dev)), "moe_forward_noalloc")
     return out

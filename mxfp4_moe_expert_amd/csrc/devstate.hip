@@ -30,3 +30,66 @@ uint32_t* device_flags() {
 }
 
 }  // namespace moe
+
+// ---------------------------------------------------------------------------
+// moe_forward_noalloc: moe_forward with its workspace in library-owned device
+// memory, for callers that cannot allocate (graph capture, tight serving
+// loops). The workspace is the file-scope array `scratch`, one copy per GPU,
+// kept until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // the full-shape layer needs 9.1 MiB at T = 64
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// The current device's scratch address, set up on first use: the symbol's
+// address, then one zero fill (the workspace contract: zero before its first
+// use), queued on `st` and, unless `st` is being captured, waited for.
+static void* scratch_for_current_device(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  if (launch_fill_zero(p, kScratchBytes, st) != hipSuccess) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return nullptr;
+  if (cs == hipStreamCaptureStatusNone && hipStreamSynchronize(st) != hipSuccess) return nullptr;
+  g_scratch_ptr[dev] = p;
+  return p;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_noalloc_max_bytes(void) { return moe::kScratchBytes; }
+
+extern "C" int moe_forward_noalloc(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w,
+                                   const float* bias, const float* logit_offset, const int32_t* token_ids,
+                                   const int32_t* tid2eid, int32_t V, const uint8_t* w13_codes,
+                                   const uint8_t* w13_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                   const int8_t* sh_w13, const float* sh_w13_scale, const int8_t* sh_w2,
+                                   const float* sh_w2_scale, void* out, int32_t out_is_fp32,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  if (!cfg) return MOE_EINVAL;
+  if (T < 0) return MOE_EINVAL;
+  const size_t need = moe_workspace_size(cfg, T);
+  if (need == 0) return MOE_EUNSUPPORTED;
+  if (need > moe::kScratchBytes) return MOE_EWORKSPACE;  // beyond the fixed scratch: use moe_forward
+  if (T == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = moe::scratch_for_current_device(st);
+  if (!ws) return MOE_EHIP;
+  return moe_forward(cfg, T, x, gate_w, bias, logit_offset, token_ids, tid2eid, V, w13_codes, w13_scales, w2_codes,
+                     w2_scales, sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, out, out_is_fp32, topk_ids_out, topk_w_out,
+                     ws, moe::kScratchBytes, stream);
+}
