@@ -60,12 +60,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_t1", choices=sorted(DEFAULTS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(DEFAULTS),
+                    help="all (default): decode_t1 as the headline line, the other workloads under 'workloads'")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated through")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"],
                     help="graph: steps captured in HIP graphs and replayed; eager: one launch sequence per step")
     ap.add_argument("--graph-steps", type=int, default=50, help="steps per captured graph")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample (headline)")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=3.0,
+                    help="budget of the CPU oracle sample of each further workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--peaks", action="store_true",
@@ -75,7 +78,7 @@ def parse():
                     % COPY_CAL_BYTES)
     ap.add_argument("--summarize", metavar="OUTDIR", default=None,
                     help="write the profiles/ summaries of --workload from the rocprofv3 output under OUTDIR "
-                    "(kernel_trace/, pmc_fetch/, pmc_write/, copy_fetch/, copy_write/) and exit")
+                    "(kernel_trace/, pmc_read/, pmc_write/, copy_read/, copy_write/) and exit")
     ap.add_argument("--commands", default=None, help="with --summarize: JSON file of the commands that ran")
     return ap.parse_args()
 
@@ -251,7 +254,7 @@ def _find(outdir, sub, name):
 
 
 def _counter_avg(path, counter, match):
-    """Mean counter value (KiB) per dispatch of the kernels whose name holds
+    """Mean counter value per dispatch of the kernels whose name holds
     `match`."""
     vals = [float(r["Counter_Value"]) for r in _csv_rows(path)
             if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
@@ -260,50 +263,83 @@ def _counter_avg(path, counter, match):
     return sum(vals) / len(vals), len(vals)
 
 
+# rocprofv3 counter passes (one --pmc run each; at most 4 TCC counters per run)
+PMC_READ = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
+PMC_WRITE = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+             "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def _read_bytes(path, match):
+    n = {c: _counter_avg(path, c, match)[0] for c in PMC_READ}
+    b = 32 * n["TCC_EA0_RDREQ_32B_sum"] + 64 * n["TCC_EA0_RDREQ_64B_sum"] + 128 * n["TCC_EA0_RDREQ_128B_sum"]
+    return b, n
+
+
+def _write_bytes(path, match):
+    n = {c: _counter_avg(path, c, match)[0] for c in PMC_WRITE}
+    w64 = n["TCC_EA0_WRREQ_64B_sum"]
+    return 32 * (n["TCC_EA0_WRREQ_sum"] - w64) + 64 * w64, n
+
+
 def summarize(workload, outdir, commands):
     """Turn one workload's rocprofv3 runs into the committed summaries:
     profiles/moe_forward_<workload>_kernels.md (per-kernel durations) and,
-    when the counter runs exist, profiles/<kernel>_<workload>_traffic.txt
-    (HBM bytes per launch of the dominant kernel, calibrated by a plain copy
-    of known size, stamped with the hash of the kernel sources)."""
+    when the counter runs exist, profiles/<kernel>_<workload>_traffic.txt:
+    HBM bytes per launch of the dominant kernel from the EA request counts by
+    size (32/64/128-byte reads, 32/64-byte writes), each scaled by what the
+    same counters read for a plain copy of known size; MFMA busy fraction,
+    executed bf16 MFMA flops and LDS bank-conflict cycles; stamped with the
+    hash of the kernel sources."""
     kname, what, _ = DOMINANT[workload]
     short = kname.split("::")[1].split("<")[0]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    stats = _csv_rows(_find(outdir, "kernel_trace", "kernel_stats.csv"))
-    lines = [f"# Kernel durations, moe_forward, workload {workload}", "",
-             f"Source hash of the dominant kernel ({', '.join(kernel_files(workload))}): "
-             f"`{source_hash(workload)}`", "",
-             "Command:", "", "```", commands.get("kernel_trace", "?"), "```", "",
-             f"Dominant kernel: `{kname}` ({what}).", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in stats:
-        nm = r["Name"]
-        if len(nm) > 90:
-            nm = nm[:87] + "..."
-        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
-    with open(os.path.join(ROOT, "profiles", f"moe_forward_{workload}_kernels.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
     try:
-        fk, nf = _counter_avg(_find(outdir, "pmc_fetch", "counter_collection.csv"), "FETCH_SIZE", kname)
-        wk, nw = _counter_avg(_find(outdir, "pmc_write", "counter_collection.csv"), "WRITE_SIZE", kname)
-        cf, _ = _counter_avg(_find(outdir, "copy_fetch", "counter_collection.csv"), "FETCH_SIZE",
-                             "__amd_rocclr_copyBuffer")
-        cw, _ = _counter_avg(_find(outdir, "copy_write", "counter_collection.csv"), "WRITE_SIZE",
-                             "__amd_rocclr_copyBuffer")
+        stats = _csv_rows(_find(outdir, "kernel_trace", "kernel_stats.csv"))
+    except FileNotFoundError:
+        stats = None
+    if stats is not None:
+        lines = [f"# Kernel durations, moe_forward, workload {workload}", "",
+                 f"Source hash of the dominant kernel ({', '.join(kernel_files(workload))}): "
+                 f"`{source_hash(workload)}`", "",
+                 "Command:", "", "```", commands.get("kernel_trace", "?"), "```", "",
+                 f"Dominant kernel: `{kname}` ({what}).", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+        for r in stats:
+            nm = r["Name"]
+            if len(nm) > 90:
+                nm = nm[:87] + "..."
+            lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.2f}% |")
+        with open(os.path.join(ROOT, "profiles", f"moe_forward_{workload}_kernels.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    try:
+        rb, rn = _read_bytes(_find(outdir, "pmc_read", "counter_collection.csv"), kname)
+        wb, wn = _write_bytes(_find(outdir, "pmc_write", "counter_collection.csv"), kname)
+        crb, crn = _read_bytes(_find(outdir, "copy_read", "counter_collection.csv"), "__amd_rocclr_copyBuffer")
+        cwb, cwn = _write_bytes(_find(outdir, "copy_write", "counter_collection.csv"), "__amd_rocclr_copyBuffer")
     except (FileNotFoundError, ValueError) as e:
         print(f"no traffic summary: {e}")
         return
-    f_fac = COPY_CAL_BYTES / (cf * 1024.0)
-    w_fac = COPY_CAL_BYTES / (cw * 1024.0)
+    r_fac = COPY_CAL_BYTES / crb
+    w_fac = COPY_CAL_BYTES / cwb
     rec = {
         "workload": workload, "kernel": kname, "source_hash": source_hash(workload),
         "source_files": kernel_files(workload),
-        "fetch_kib_per_dispatch": round(fk, 2), "write_kib_per_dispatch": round(wk, 2),
-        "dispatches": [nf, nw],
-        "copy_bytes": COPY_CAL_BYTES, "copy_fetch_kib": round(cf, 2), "copy_write_kib": round(cw, 2),
-        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
-        "bytes_per_launch": int(round(fk * 1024.0 * f_fac + wk * 1024.0 * w_fac)),
+        "read_requests": {k: round(v, 1) for k, v in rn.items()},
+        "write_and_compute": {k: round(v, 3) for k, v in wn.items()},
+        "read_bytes_counted": int(rb), "write_bytes_counted": int(wb),
+        "copy_bytes": COPY_CAL_BYTES,
+        "copy_read_requests": {k: round(v, 1) for k, v in crn.items()},
+        "copy_write_requests": {k: round(v, 1) for k in ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+                                for v in [cwn[k]]},
+        "copy_read_bytes_counted": int(crb), "copy_write_bytes_counted": int(cwb),
+        "read_factor": round(r_fac, 4), "write_factor": round(w_fac, 4),
+        "bytes_per_launch": int(round(rb * r_fac + wb * w_fac)),
+        "mfma_busy_pct": round(wn["MfmaUtil"], 2),
+        "mfma_bf16_flops_executed": wn["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+        "lds_bank_conflict_cycles": wn["SQ_LDS_BANK_CONFLICT"],
+        "lds_active_cycles": wn["SQ_LDS_IDX_ACTIVE"],
         "commands": {k: v for k, v in commands.items() if k != "kernel_trace"},
     }
     with open(os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt"), "w") as f:
@@ -312,32 +348,245 @@ def summarize(workload, outdir, commands):
     print(json.dumps(rec))
 
 
-def cpu_baseline(layer, batches, tids, budget_s):
-    """Time the CPU oracle on whole token batches of this workload until the
-    budget is spent (sampled rows for large batches)."""
+def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids):
+    """The CPU-oracle leg of one workload: time the oracle, as it stands, on a
+    bounded sample of the workload's batches (whole batches at T <= 64,
+    sampled rows above), and grade the GPU's first batch against it: routing
+    of every token of that batch (sets equal except near-ties, counted) and
+    the fp32 outputs of the sampled rows (relative L2, max abs / rms)."""
     import numpy as np
 
     import oracle
 
-    threads = oracle.lib().or_num_threads() if hasattr(oracle.lib(), "or_num_threads") else os.cpu_count()
+    threads = oracle.lib().or_num_threads()
     T = batches[0].shape[0]
-    rows = None if T <= 64 else np.linspace(0, T - 1, 8).astype(np.int32)
+    rows = None if T <= 64 else np.unique(np.linspace(0, T - 1, 16).astype(np.int32))
     done_tokens, t0, i = 0, time.perf_counter(), 0
-    outs = []
+    first = None
     while True:
         xb = batches[i % len(batches)]
         tb = None if tids is None else tids[i % len(tids)]
         r = oracle.forward(layer, xb, token_ids=tb, rows=rows)
-        outs.append((i % len(batches), rows, r["out"]))
+        if i == 0:
+            first = r
         done_tokens += T if rows is None else len(rows)
         i += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     sample = (f"{done_tokens} tokens: {i} batch(es) of T={T}" +
-              ("" if rows is None else f", {len(rows)} sampled rows each (route + experts + shared)"))
-    return dict(value=done_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
-                seconds=round(dt, 2)), outs
+              ("" if rows is None else f", {len(rows)} evenly spaced rows each (route + experts + shared)"))
+    base = dict(value=done_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
+                seconds=round(dt, 2))
+
+    # grading of batch 0
+    near = swapped = 0
+    ref = first["out"]
+    sel = np.arange(T) if rows is None else rows
+    if tids is None:
+        oi, _, gap, _ = oracle.route(batches[0], layer.gate_w, layer.bias, layer.logit_offset, k=layer.wl.k)
+        near = int(np.sum(gap < 1e-5))
+        for j, t in enumerate(sel):
+            if set(gpu_ids[t].tolist()) != set(first["ids"][j].tolist()):
+                swapped += 1
+                r2 = oracle.forward(layer, batches[0], rows=np.array([t], np.int32), force_ids=gpu_ids[t][None, :])
+                ref[j] = r2["out"][0]
+        # every token of the batch whose set differs (near-ties only, at the bar)
+        differ = [t for t in range(T) if set(gpu_ids[t].tolist()) != set(oi[t].tolist())]
+        bad = [t for t in differ if gap[t] >= 1e-5]
+    else:
+        oi, _ = oracle.hash_route(batches[0], tids[0], layer.tid2eid, layer.gate_w)
+        differ = [t for t in range(T) if not np.array_equal(gpu_ids[t], oi[t])]
+        bad = differ
+    g = gpu_out32[sel]
+    d = g - ref
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    check = dict(rows_compared=int(len(sel)), rel_l2=float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                 max_abs_over_rms=float(np.abs(d).max() / rms), near_ties=near, routing_sets_differ=len(differ),
+                 routing_mismatch_not_near_tie=len(bad),
+                 within_bar=bool(np.linalg.norm(d) / np.linalg.norm(ref) <= 5e-3 and np.abs(d).max() <= 2e-2 * rms
+                                 and not bad))
+    return base, check
+
+
+def workload_variant(base_host, base_copies, wl):
+    """The base layer's expert, shared and router weights with this workload's
+    own router bias, logit offset and hash table (host, and each device copy)."""
+    import dataclasses
+
+    import torch
+
+    import synth
+
+    bias = synth.normal_f32(wl.seed, synth.S_BIAS, 0, wl.E, wl.bias_sigma)
+    off = synth.normal_f32(wl.seed, synth.S_OFFSET, 0, wl.E, wl.offset_sigma) if wl.offset_sigma > 0 else None
+    t2e = synth.tid2eid(wl.seed, synth.S_TID2EID, 0, wl.V, wl.E, wl.k) if wl.hash_layer else None
+    host = dataclasses.replace(base_host, wl=wl, bias=bias, logit_offset=off, tid2eid=t2e)
+    dev = base_copies[0].gate_w.device
+    b_d = torch.from_numpy(bias).to(dev)
+    o_d = None if off is None else torch.from_numpy(off).to(dev)
+    t_d = None if t2e is None else torch.from_numpy(t2e).to(dev)
+    copies = [dataclasses.replace(c, bias=b_d, logit_offset=o_d, tid2eid=t_d) for c in base_copies]
+    return host, copies
+
+
+def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
+    """Time K steps of one workload (after W warm-up steps) and measure its
+    dominant kernel; returns the workload's record."""
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_amd as mx
+    import synth
+
+    _, _, _, kernel, bound = DEFAULTS[name]
+    wl = synth.WORKLOADS[name]
+    T, H, k = wl.T, wl.H, wl.k
+    dev = base_copies[0].gate_w.device
+    cfg = mx.config_of(wl)
+    layer, copies = workload_variant(base_host, base_copies[:C], wl)
+    sched = mx.forward_schedule(cfg, T, hash_layer=wl.hash_layer)
+    nb = min(K + W, max(2, (1 << 27) // (T * H)))
+    batches = [synth.make_tokens(wl, rep=r) for r in range(nb)]
+    tids = [synth.make_token_ids(wl, rep=r) for r in range(nb)] if wl.hash_layer else None
+    x_dev = torch.stack([mx.bf16_from_numpy(b, dev) for b in batches])
+    t_dev = torch.stack([torch.from_numpy(t).to(dev) for t in tids]) if tids else None
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ids_all = torch.empty(K, T, k, dtype=torch.int32, device=dev)
+    w_all = torch.empty(K, T, k, dtype=torch.float32, device=dev)
+    ws = mx.Workspace(dev)
+    buf = ws.get(cfg, T)
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+
+    def call_args(s, st):
+        D = copies[s % C]
+        xb = x_dev[s % nb]
+        tb = None if t_dev is None else t_dev[s % nb]
+        P = mx._ptr
+        return (ctypes.byref(cfg), T, P(xb), P(D.gate_w), P(D.bias), P(D.logit_offset), P(tb),
+                P(D.tid2eid if tb is not None else None), 0 if D.tid2eid is None else D.tid2eid.shape[0],
+                P(D.w13_codes), P(D.w13_scales), P(D.w2_codes), P(D.w2_scales), P(D.sh_w13), P(D.sh_w13_scale),
+                P(D.sh_w2), P(D.sh_w2_scale), P(out), 0, P(ids_all[s % K]), P(w_all[s % K]), P(buf), buf.numel(),
+                ctypes.c_void_p(st))
+
+    argv = [call_args(s, stream.cuda_stream) for s in range(max(K, W))]
+
+    def step(s):
+        rc = L.moe_forward(*argv[s])
+        if rc != 0:
+            raise mx.MoEError(rc, "moe_forward")
+
+    hip = Hip()
+    ev_a = [hip.event() for _ in range(K)]
+    ev_b = [hip.event() for _ in range(K)]
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize(dev)
+
+    # eager pass: timing-only events bracket the dominant kernel on its launch stream, every step
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(K):
+        mx.set_kernel_events(kernel, ev_a[s], ev_b[s])
+        step(s)
+    t1.record(stream)
+    mx.set_kernel_events(None)
+    torch.cuda.synchronize(dev)
+    eager_ms = t0.elapsed_time(t1)
+    kern_ms = [hip.elapsed_ms(ev_a[s], ev_b[s]) for s in range(K)]
+    for e in ev_a + ev_b:
+        hip.destroy(e)
+
+    graph_ms = None
+    if args.mode == "graph":
+        G = max(1, min(args.graph_steps, K))
+        graphs = []
+        cs = torch.cuda.Stream(dev)
+        argv_g = [call_args(s, cs.cuda_stream) for s in range(K)]
+        with torch.cuda.stream(cs):
+            for g0 in range(0, K, G):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cs):
+                    for s in range(g0, min(K, g0 + G)):
+                        rc = L.moe_forward(*argv_g[s])
+                        if rc != 0:
+                            raise mx.MoEError(rc, "moe_forward (capture)")
+                graphs.append(gr)
+        torch.cuda.synchronize(dev)
+        graphs[0].replay()  # warm replay
+        torch.cuda.synchronize(dev)
+        t0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        t1.record(stream)
+        torch.cuda.synchronize(dev)
+        graph_ms = t0.elapsed_time(t1)
+        del graphs
+
+    total_ms = graph_ms if graph_ms is not None else eager_ms
+    ms_step = total_ms / K
+    ids_np = ids_all.cpu().numpy()
+    alg = algorithmic(wl, ids_np)
+    # The dominant kernel's average duration: in the single-launch schedule
+    # the kernel is the whole step, so it is the timed region over K steps
+    # (the event pair around each eager launch adds its own recording time);
+    # otherwise the mean of the per-launch event pairs of the eager pass.
+    if sched == "single":
+        kern_avg_ms = ms_step
+        ksrc = ("timed region / steps (one launch per step, events on the launch stream around "
+                + ("the graph replays)" if graph_ms is not None else "the eager steps)"))
+    else:
+        kern_avg_ms = sum(kern_ms) / K
+        ksrc = "mean of per-launch event pairs on the launch stream (eager pass)"
+    scope = DOMINANT[name][2]
+    if bound == "hbm":
+        achieved = alg[scope + "_bytes"] / (kern_avg_ms / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), algorithmic=int(alg[scope + "_bytes"]))
+    else:
+        achieved = alg[scope + "_flops"] / (kern_avg_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), algorithmic=alg[scope + "_flops"])
+    roof["traffic"] = traffic_from_profiles(name)
+    roof["kernel"] = DOMINANT[name][0]
+    roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
+    roof["kernel_time"] = ksrc
+    ks = sorted(kern_ms)
+    roof["kernel_event_p50_us"] = round(ks[len(ks) // 2] * 1e3, 2)
+    roof["kernel_event_p99_us"] = round(ks[min(len(ks) - 1, (len(ks) * 99) // 100)] * 1e3, 2)
+    if kern_avg_ms > ms_step * 1.001:
+        print(f"warning: {name}: kernel time {kern_avg_ms * 1e3:.2f} us exceeds the step {ms_step * 1e3:.2f} us",
+              file=sys.stderr, flush=True)
+        roof["warning"] = "kernel time exceeds the timed step"
+    layer_bw = alg["layer_bytes"] / (ms_step / 1e3) / 1e9
+    layer_tf = alg["layer_flops"] / (ms_step / 1e3) / 1e12
+    rec = {
+        "T": T, "schedule": sched, "steps": K, "warmup": W, "weight_copies": C, "mode": args.mode,
+        "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T * K / (total_ms / 1e3), 1),
+        "roofline": roof,
+        "layer": {"bytes_per_step": int(alg["layer_bytes"]), "hbm_GBps": round(layer_bw, 1),
+                  "hbm_frac": round(layer_bw / PEAK_HBM_GBS, 4), "flops_per_step": alg["layer_flops"],
+                  "mfma_TFLOPs": round(layer_tf, 2), "mfma_frac": round(layer_tf / PEAK_BF16_TFLOPS, 4),
+                  "distinct_experts": round(alg["distinct_experts"], 2),
+                  "eager_ms_per_step": round(eager_ms / K, 5),
+                  "graph_ms_per_step": None if graph_ms is None else round(graph_ms / K, 5)},
+    }
+    if cpu_budget > 0:
+        o32 = mx.forward(cfg, x_dev[0], copies[0], token_ids=None if t_dev is None else t_dev[0], out_fp32=True,
+                         ws=ws)
+        ids0 = mx.forward(cfg, x_dev[0], copies[0], token_ids=None if t_dev is None else t_dev[0],
+                          return_routing=True, ws=ws)[1][0]
+        torch.cuda.synchronize(dev)
+        cb, check = cpu_leg(layer, batches, tids, cpu_budget, o32.cpu().double().numpy(), ids0.cpu().numpy())
+        rec["cpu_baseline"] = cb
+        rec["parity"] = check
+    del x_dev, t_dev, out, ids_all, w_all, ws, buf
+    torch.cuda.empty_cache()
+    return rec
+
+
+ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096"]
 
 
 def main():
@@ -358,167 +607,55 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    import numpy as np
     import torch
 
     import mxfp4_moe_expert_amd as mx
     import synth
 
-    steps0, warm0, copies0, kernel, bound = DEFAULTS[args.workload]
-    K = args.steps if args.steps is not None else steps0
-    W = args.warmup if args.warmup is not None else warm0
-    C = max(1, args.copies if args.copies is not None else copies0)
-    wl = synth.WORKLOADS[args.workload]
-    T, H, E, k = wl.T, wl.H, wl.E, wl.k
+    names = ORDER if args.workload == "all" else [args.workload]
+    main_name = names[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = mx.config_of(wl)
+    plan = {}
+    for i, n in enumerate(names):
+        steps0, warm0, copies0, _, _ = DEFAULTS[n]
+        K = args.steps if (args.steps is not None and i == 0) else steps0
+        W = args.warmup if (args.warmup is not None and i == 0) else warm0
+        C = max(1, args.copies if args.copies is not None else copies0)
+        plan[n] = (K, W, C)
     t_gen = time.perf_counter()
-    layer = synth.make_layer(wl)
+    base_host = synth.make_layer(synth.WORKLOADS["decode_t1"])  # seed 0: the same weights for every workload
     t_gen = time.perf_counter() - t_gen
-    base = mx.DeviceLayer.from_host(layer, dev)
-    copies = [base] + [mx.DeviceLayer(*[None if t is None else t.clone() for t in vars(base).values()])
-                       for _ in range(C - 1)]
-    nb = min(K + W, max(2, (1 << 27) // (T * H)))
-    batches = [synth.make_tokens(wl, rep=r) for r in range(nb)]
-    tids = [synth.make_token_ids(wl, rep=r) for r in range(nb)] if wl.hash_layer else None
-    x_dev = torch.stack([mx.bf16_from_numpy(b, dev) for b in batches])
-    t_dev = torch.stack([torch.from_numpy(t).to(dev) for t in tids]) if tids else None
-    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-    ids_all = torch.empty(K, T, k, dtype=torch.int32, device=dev)
-    w_all = torch.empty(K, T, k, dtype=torch.float32, device=dev)
-    ws = mx.Workspace(dev)
-    buf = ws.get(cfg, T)
-    L = mx.lib()
-    stream = torch.cuda.current_stream(dev)
-
-    def call_args(step):
-        D = copies[step % C]
-        xb = x_dev[step % nb]
-        tb = None if t_dev is None else t_dev[step % nb]
-        ids = ids_all[step % K]
-        w = w_all[step % K]
-        P = mx._ptr
-        return (ctypes.byref(cfg), T, P(xb), P(D.gate_w), P(D.bias), P(D.logit_offset), P(tb),
-                P(D.tid2eid if tb is not None else None), 0 if D.tid2eid is None else D.tid2eid.shape[0],
-                P(D.w13_codes), P(D.w13_scales), P(D.w2_codes), P(D.w2_scales), P(D.sh_w13), P(D.sh_w13_scale),
-                P(D.sh_w2), P(D.sh_w2_scale), P(out), 0, P(ids), P(w), P(buf), buf.numel(),
-                ctypes.c_void_p(stream.cuda_stream))
-
-    argv = [call_args(s) for s in range(max(K, W))]
-
-    def step(s):
-        rc = L.moe_forward(*argv[s])
-        if rc != 0:
-            raise mx.MoEError(rc, "moe_forward")
-
-    hip = Hip()
-    ev_a = [hip.event() for _ in range(K)]
-    ev_b = [hip.event() for _ in range(K)]
-
-    # warm-up (also checks the path runs)
-    for s in range(W):
-        step(s)
-    torch.cuda.synchronize(dev)
-
-    # eager timed pass: kernel events bracket the dominant kernel on every step
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    t0.record(stream)
-    for s in range(K):
-        mx.set_kernel_events(kernel, ev_a[s], ev_b[s])
-        step(s)
-    t1.record(stream)
-    mx.set_kernel_events(None)
-    torch.cuda.synchronize(dev)
-    eager_ms = t0.elapsed_time(t1)
-    kern_ms = [hip.elapsed_ms(ev_a[s], ev_b[s]) for s in range(K)]
-    kern_avg_ms = sum(kern_ms) / K
-
-    graph_ms = None
-    if args.mode == "graph":
-        G = max(1, min(args.graph_steps, K))
-        graphs = []
-        cs = torch.cuda.Stream(dev)
-        with torch.cuda.stream(cs):
-            argv_g = [list(a) for a in argv]
-            for a in argv_g:
-                a[-1] = ctypes.c_void_p(cs.cuda_stream)
-            for g0 in range(0, K, G):
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr, stream=cs):
-                    for s in range(g0, min(K, g0 + G)):
-                        rc = L.moe_forward(*argv_g[s])
-                        if rc != 0:
-                            raise mx.MoEError(rc, "moe_forward (capture)")
-                graphs.append(gr)
-        torch.cuda.synchronize(dev)
-        for gr in graphs[:1]:  # warm replay
-            gr.replay()
-        torch.cuda.synchronize(dev)
-        t0.record(stream)
-        for gr in graphs:
-            gr.replay()
-        t1.record(stream)
-        torch.cuda.synchronize(dev)
-        graph_ms = t0.elapsed_time(t1)
-
-    total_ms = graph_ms if graph_ms is not None else eager_ms
-    ms_step = total_ms / K
-    ids_np = ids_all.cpu().numpy()
-    alg = algorithmic(wl, ids_np)
-    value = T * K / (total_ms / 1e3)
-    scope = DOMINANT[args.workload][2]
-    if bound == "hbm":
-        achieved = alg[scope + "_bytes"] / (kern_avg_ms / 1e3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4))
-    else:
-        achieved = alg[scope + "_flops"] / (kern_avg_ms / 1e3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
-    traffic = traffic_from_profiles(args.workload)
-    roof["traffic"] = traffic
-    roof["kernel"] = DOMINANT[args.workload][0]
-    roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
-    ks = sorted(kern_ms)
-    roof["kernel_p50_us"] = round(ks[len(ks) // 2] * 1e3, 2)
-    roof["kernel_p99_us"] = round(ks[min(len(ks) - 1, (len(ks) * 99) // 100)] * 1e3, 2)
-    layer_bw = alg["layer_bytes"] / (ms_step / 1e3) / 1e9
-    layer_tf = alg["layer_flops"] / (ms_step / 1e3) / 1e12
-
+    print(f"[bench] layer generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    base = mx.DeviceLayer.from_host(base_host, dev)
+    Cmax = max(c for _, _, c in plan.values())
+    base_copies = [base] + [mx.DeviceLayer(*[None if t is None else t.clone() for t in vars(base).values()])
+                            for _ in range(Cmax - 1)]
+    recs = {}
+    for i, n in enumerate(names):
+        K, W, C = plan[n]
+        budget = 0.0 if args.no_cpu_baseline else (args.cpu_seconds if i == 0 else args.extra_cpu_seconds)
+        print(f"[bench] {n}: {K} steps after {W} warm-up, {C} weight copies", file=sys.stderr, flush=True)
+        recs[n] = run_workload(args, n, base_host, base_copies, K, W, C, budget)
+        print(f"[bench] {n}: {recs[n]['ms_per_step']} ms/step, {recs[n]['tokens_per_s']} tokens/s",
+              file=sys.stderr, flush=True)
+    m = recs[main_name]
+    wl = synth.WORKLOADS[main_name]
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "hidden_size": H, "n_routed_experts": E, "top_k": k,
-                   "moe_intermediate": wl.I, "routed": "mxfp4 (E2M1 + E8M0/32)", "shared": "int8 per-channel",
-                   "weight_copies": C, "mode": args.mode, "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer": {"bytes_per_step": int(alg["layer_bytes"]), "hbm_GBps": round(layer_bw, 1),
-                  "hbm_frac": round(layer_bw / PEAK_HBM_GBS, 4), "flops_per_step": alg["layer_flops"],
-                  "mfma_TFLOPs": round(layer_tf, 2), "mfma_frac": round(layer_tf / PEAK_BF16_TFLOPS, 4),
-                  "distinct_experts": round(alg["distinct_experts"], 2), "eager_ms_per_step": round(eager_ms / K, 5),
-                  "graph_ms_per_step": None if graph_ms is None else round(graph_ms / K, 5)},
+        "metric": METRIC, "value": m["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": m["steps"],
+        "warmup": m["warmup"], "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": main_name, "T": wl.T, "hidden_size": wl.H, "n_routed_experts": wl.E,
+                   "top_k": wl.k, "moe_intermediate": wl.I, "routed": "mxfp4 (E2M1 + E8M0/32)",
+                   "shared": "int8 per-channel", "weight_copies": m["weight_copies"], "mode": args.mode,
+                   "schedule": m["schedule"], "parallelism": "single GPU"},
+        "roofline": m["roofline"],
+        "layer": m["layer"],
+        "cpu_baseline": m.get("cpu_baseline"),
+        "parity": m.get("parity"),
         "gen_seconds": round(t_gen, 1),
+        "workloads": {n: r for n, r in recs.items() if n != main_name},
     }
-    if not args.no_cpu_baseline:
-        cb, outs = cpu_baseline(layer, batches, tids, args.cpu_seconds)
-        rec["cpu_baseline"] = cb
-        # parity of the sampled tokens (fp32 output of the same kernels)
-        import oracle as _o  # noqa: F401
-
-        errs = []
-        for bi, rows, ref in outs[:4]:
-            xb = x_dev[bi]
-            tb = None if t_dev is None else t_dev[bi]
-            o32 = mx.forward(cfg, xb, copies[0], token_ids=tb, out_fp32=True, ws=ws)
-            g = o32.cpu().double().numpy()
-            g = g if rows is None else g[rows]
-            errs.append(float(np.linalg.norm(g - ref) / np.linalg.norm(ref)))
-        rec["parity_rel_l2_max"] = max(errs)
-    else:
-        rec["cpu_baseline"] = None
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:
