@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s at T=1/64/8192; % of HBM BW (decode) / bf16 MFMA peak"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published (5.0 PFLOP/s): the block-scaled fp8 x fp4 rate
 
 DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), bound
     "decode_t1": (1000, 50, 12, "routed_w13", "hbm"),
@@ -52,6 +53,19 @@ DOMINANT = {
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
     "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
 }
+# with --prefill-mfma block-scaled (moe_set_option MOE_OPTION_PREFILL_BLOCK_SCALED)
+DOMINANT_MX = ("moe::k_gemm_mx<0>",
+               "routed w13: MXFP4 grouped GEMM on the block-scaled fp8 x fp4 MFMA (activations split exactly into "
+               "hi/lo fp8) + clamped SwiGLU", "w13")
+
+
+def dominant(workload: str):
+    if workload in ("prefill_t8192", "hash_t4096") and PREFILL_MX[0]:
+        return DOMINANT_MX
+    return DOMINANT[workload]
+
+
+PREFILL_MX = [False]
 COPY_CAL_BYTES = 1 << 28  # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
 
@@ -66,6 +80,8 @@ def parse():
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"],
                     help="graph: steps captured in HIP graphs and replayed; eager: one launch sequence per step")
     ap.add_argument("--graph-steps", type=int, default=50, help="steps per captured graph")
+    ap.add_argument("--prefill-mfma", default="bf16", choices=["bf16", "block-scaled"],
+                    help="routed GEMMs above 64 tokens: bf16 MFMA (default) or the block-scaled fp8 x fp4 MFMA")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample (headline)")
     ap.add_argument("--extra-cpu-seconds", type=float, default=3.0,
                     help="budget of the CPU oracle sample of each further workload")
@@ -141,12 +157,13 @@ def algorithmic(wl, ids_np):
 # Source file of each dominant kernel; its traffic record is keyed on this
 # file, the library headers it includes and the launcher (api.cpp, which sets
 # its launch configuration), so that a change elsewhere keeps the record.
-KERNEL_SOURCE = {"k_layer_small": "fused.hip", "k_stream_fused": "stream.hip", "k_gemm": "gemm.hip"}
+KERNEL_SOURCE = {"k_layer_small": "fused.hip", "k_stream_fused": "stream.hip", "k_gemm": "gemm.hip",
+                 "k_gemm_mx": "gemm_mx.hip"}
 
 
 def kernel_files(workload: str):
     csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
-    short = DOMINANT[workload][0].split("::")[1].split("<")[0]
+    short = dominant(workload)[0].split("::")[1].split("<")[0]
     todo, seen = [KERNEL_SOURCE[short], "api.cpp"], set()
     while todo:
         f = todo.pop()
@@ -174,7 +191,7 @@ def source_hash(workload: str) -> str:
 def traffic_from_profiles(workload: str):
     """HBM bytes per launch of the dominant kernel from committed counter
     summaries, if they were taken on the current kernel sources."""
-    short = DOMINANT[workload][0].split("::")[1].split("<")[0]
+    short = dominant(workload)[0].split("::")[1].split("<")[0]
     p = os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt")
     if not os.path.exists(p):
         return None
@@ -290,7 +307,7 @@ def summarize(workload, outdir, commands):
     same counters read for a plain copy of known size; MFMA busy fraction,
     executed bf16 MFMA flops and LDS bank-conflict cycles; stamped with the
     hash of the kernel sources."""
-    kname, what, _ = DOMINANT[workload]
+    kname, what, _ = dominant(workload)
     short = kname.split("::")[1].split("<")[0]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     try:
@@ -311,7 +328,8 @@ def summarize(workload, outdir, commands):
             lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.2f}% |")
-        with open(os.path.join(ROOT, "profiles", f"moe_forward_{workload}_kernels.md"), "w") as f:
+        tag = workload + ("_block_scaled" if PREFILL_MX[0] else "")
+    with open(os.path.join(ROOT, "profiles", f"moe_forward_{tag}_kernels.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     try:
         rb, rn = _read_bytes(_find(outdir, "pmc_read", "counter_collection.csv"), kname)
@@ -342,7 +360,7 @@ def summarize(workload, outdir, commands):
         "lds_active_cycles": wn["SQ_LDS_IDX_ACTIVE"],
         "commands": {k: v for k, v in commands.items() if k != "kernel_trace"},
     }
-    with open(os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt"), "w") as f:  # short names the kernel
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
@@ -539,17 +557,28 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
     else:
         kern_avg_ms = sum(kern_ms) / K
         ksrc = "mean of per-launch event pairs on the launch stream (eager pass)"
-    scope = DOMINANT[name][2]
+    scope = dominant(name)[2]
     if bound == "hbm":
         achieved = alg[scope + "_bytes"] / (kern_avg_ms / 1e3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), algorithmic=int(alg[scope + "_bytes"]))
+    elif "k_gemm_mx" in dominant(name)[0]:
+        # block-scaled fp8 x fp4 MFMA: every bf16 activation is split into two fp8 halves, so the
+        # matrix cores execute twice the method's flops at the fp8 rate; the fraction of the fp8
+        # peak equals the method's flops over the bf16 peak (the metric's definition)
+        algo = alg[scope + "_flops"]
+        achieved = 2.0 * algo / (kern_avg_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_FP8_TFLOPS, 4), algorithmic=algo, executed=2.0 * algo,
+                    dtype="fp8 x fp4 (block-scaled; activations as exact hi + lo fp8)",
+                    bf16_equivalent_TFLOPs=round(achieved / 2.0, 2),
+                    bf16_equivalent_frac=round(achieved / 2.0 / PEAK_BF16_TFLOPS, 4))
     else:
         achieved = alg[scope + "_flops"] / (kern_avg_ms / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4), algorithmic=alg[scope + "_flops"])
     roof["traffic"] = traffic_from_profiles(name)
-    roof["kernel"] = DOMINANT[name][0]
+    roof["kernel"] = dominant(name)[0]
     roof["kernel_avg_us"] = round(kern_avg_ms * 1e3, 2)
     roof["kernel_time"] = ksrc
     ks = sorted(kern_ms)
@@ -592,6 +621,7 @@ ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096"]
 def main():
     args = parse()
     if args.summarize:
+        PREFILL_MX[0] = args.prefill_mfma == "block-scaled"
         cmds = {}
         if args.commands:
             with open(args.commands) as f:
@@ -612,6 +642,9 @@ def main():
     import mxfp4_moe_expert_amd as mx
     import synth
 
+    if args.prefill_mfma == "block-scaled":
+        PREFILL_MX[0] = True
+        mx.set_option("prefill_block_scaled", 1)
     names = ORDER if args.workload == "all" else [args.workload]
     main_name = names[0]
     dev = torch.device("cuda:0")
@@ -648,6 +681,7 @@ def main():
         "config": {"workload": main_name, "T": wl.T, "hidden_size": wl.H, "n_routed_experts": wl.E,
                    "top_k": wl.k, "moe_intermediate": wl.I, "routed": "mxfp4 (E2M1 + E8M0/32)",
                    "shared": "int8 per-channel", "weight_copies": m["weight_copies"], "mode": args.mode,
+                   "prefill_mfma": args.prefill_mfma,
                    "schedule": m["schedule"], "parallelism": "single GPU"},
         "roofline": m["roofline"],
         "layer": m["layer"],

@@ -227,6 +227,28 @@ enum {
  * never launches anything. */
 int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash);
 
+/* Process-wide options (not thread-safe; set them before the calls they
+ * should affect, and query moe_workspace_size after setting them: the
+ * workspace size depends on them). */
+enum {
+  /* 1: the routed grouped GEMMs of batches above 64 tokens run on gfx950's
+   * block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4): MXFP4 weights as
+   * stored, E8M0 exponents as the hardware scales, and each bf16 activation
+   * split exactly into two fp8 (E4M3) values with their own E8M0 exponents
+   * per 32, so the sums equal the bf16 path's up to summation order
+   * (page "deepseek-v4-mxfp4-int8 config.json", quantization_config,
+   * experts_w4a16: scale_mode native_e8m0). Needs H % 256 == 0 and
+   * I % 128 == 0; other shapes keep the default. 0 (default): bf16 MFMA on
+   * weights converted to bf16 in registers. */
+  MOE_OPTION_PREFILL_BLOCK_SCALED = 1
+};
+
+/* Sets an option; MOE_EINVAL for an unknown option or value. */
+int moe_set_option(int32_t option, int32_t value);
+
+/* The current value of an option, or MOE_EINVAL for an unknown option. */
+int moe_get_option(int32_t option);
+
 /* Kernels that moe_set_kernel_events can bracket. */
 enum {
   MOE_KERNEL_NONE = 0,

@@ -65,6 +65,8 @@ _SIGNATURES = {
                        ctypes.c_int),
     "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
     "moe_device_flags": ([ctypes.POINTER(ctypes.c_uint32), _I32, _VP], ctypes.c_int),
+    "moe_set_option": ([_I32, _I32], ctypes.c_int),
+    "moe_get_option": ([_I32], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
     "moe_noalloc_max_bytes": ([], _SZ),
     "moe_forward_noalloc": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -135,6 +137,16 @@ def set_kernel_events(kernel: str | None, start_event=None, stop_event=None):
     hipEvent_t handles (ints or c_void_p); None stops. Measurement only."""
     kid = 0 if kernel is None else KERNELS[kernel]
     _check(lib().moe_set_kernel_events(kid, start_event, stop_event), "moe_set_kernel_events")
+
+
+OPTIONS = {"prefill_block_scaled": 1}
+
+
+def set_option(name: str, value: int):
+    """Set a process-wide option (``OPTIONS``); returns the previous value."""
+    prev = lib().moe_get_option(OPTIONS[name])
+    _check(lib().moe_set_option(OPTIONS[name], int(value)), "moe_set_option")
+    return prev
 
 
 FLAGS = {"token_id": 1, "table_entry": 2, "expert_id": 4, "wait_expired": 8, "permutation": 16}

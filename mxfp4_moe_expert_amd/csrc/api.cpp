@@ -18,9 +18,10 @@ constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, tile_rec, done, blk_counts, hbuf, hs, ybuf,
-      zbuf, total;
+  size_t counters, xfer, wsplit, plog, scores, ids, w, offsets, sorted, slot_pos, sorted_tok, tile_info, tile_rec,
+      done, blk_counts, hbuf, hs, ybuf, zbuf, xsplit, hscale, total;
   int tile_n, max_tiles;
+  bool mx;  // routed GEMMs on the block-scaled MFMA (activations split into fp8 hi/lo)
 };
 
 bool cfg_ok(const moe_config* c) {
@@ -57,8 +58,17 @@ int shared_stream_tile(int T, int K) {
 // the LDS activation tile stays no larger than the shared expert's.
 // Batches above kSmallT run the grouped GEMMs (256-row output tiles along H).
 bool use_gemm(const moe_config& c, int T) { return T > kSmallT && c.hidden_size % 256 == 0; }
+// Process-wide options (moe_set_option).
+int g_opt_prefill_block_scaled = 0;
+
+// the routed grouped GEMMs run on the block-scaled MFMA when that option is on and the shapes fit
+// its tiles
+bool use_gemm_mx(const moe_config& c, int T) {
+  return g_opt_prefill_block_scaled && use_gemm(c, T) && gemm_mx_supported(c.hidden_size, c.moe_intermediate);
+}
 
 int routed_tile_n(const moe_config& c, int T) {
+  if (use_gemm_mx(c, T)) return kGemmMxTokens;
   if (use_gemm(c, T)) return kGemmTokens;
   const int K = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
   int tn = T <= 1 ? 1 : 6;
@@ -106,6 +116,11 @@ Layout layout(const moe_config& c, int T) {
   L.hs = take((size_t)T * I * 2);
   L.ybuf = take(slots * H * 4);
   L.zbuf = take((size_t)T * H * 4);
+  // block-scaled routed GEMMs: x split into hi/lo fp8 [T][H] + E8M0 [T][H/32] each; the h split
+  // lives in hbuf (hi [slots][I], lo [slots][I]), its E8M0 bytes here ([slots][I/32] each)
+  L.mx = use_gemm_mx(c, T);
+  L.xsplit = take(L.mx ? (size_t)T * H * 2 + (size_t)T * (H / 32) * 2 : 0);
+  L.hscale = take(L.mx ? slots * (I / 32) * 2 : 0);
   L.total = o;
   return L;
 }
@@ -371,6 +386,79 @@ GemmArgs gemm_shared_w2_combine(const moe_config& c, int T, const int8_t* q2, co
   return g;
 }
 
+// Routed w13 + SwiGLU and w2 x routing weight on the block-scaled MFMA: x is
+// split into hi/lo fp8 first, the w13 epilogue writes h split the same way,
+// and w2 writes the weighted slot outputs in bf16 (ybuf, by slot).
+hipError_t routed_gemms_mx(const moe_config& c, int T, const uint16_t* x, const Perm& p, const float* slot_w,
+                           const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                           void* ws, const Layout& L, uint16_t* ybf, hipStream_t st) {
+  const int H = c.hidden_size, I = c.moe_intermediate;
+  const size_t slots = (size_t)T * c.top_k;
+  uint8_t* xh = at<uint8_t>(ws, L.xsplit);
+  uint8_t* xl = xh + (size_t)T * H;
+  uint8_t* xsh = xl + (size_t)T * H;
+  uint8_t* xsl = xsh + (size_t)T * (H / 32);
+  uint8_t* hh = at<uint8_t>(ws, L.hbuf);
+  uint8_t* hl = hh + slots * I;
+  uint8_t* hsh = at<uint8_t>(ws, L.hscale);
+  uint8_t* hsl = hsh + slots * (I / 32);
+  hipError_t e = launch_quant_rows(x, T, H, xh, xl, xsh, xsl, st);
+  if (e != hipSuccess) return e;
+  MxGemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.mode = kGemmW13;
+  a.wq = w13c;
+  a.wsc = w13s;
+  a.q_expert_stride = (long long)2 * I * (H / 2);
+  a.s_expert_stride = (long long)2 * I * (H / 32);
+  a.K = H;
+  a.half = I;
+  a.N = I;
+  a.I = I;
+  a.tile_info = p.tile_info;
+  a.n_tiles = p.n_tiles;
+  a.n_ntiles = I / 128;
+  a.a_hi = xh;
+  a.a_lo = xl;
+  a.as_hi = xsh;
+  a.as_lo = xsl;
+  a.act_row = p.sorted_tok;
+  a.h_hi = hh;
+  a.h_lo = hl;
+  a.hs_hi = hsh;
+  a.hs_lo = hsl;
+  a.limit = c.swiglu_limit;
+  a.order = 0;
+  a.queue = at<int32_t>(ws, L.counters) + kGemmQueueInts + 9 * kQRoutedW13;
+  e = timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm_mx(a, p.max_tiles, st); });
+  if (e != hipSuccess) return e;
+  MxGemmArgs b;
+  memset(&b, 0, sizeof(b));
+  b.mode = kGemmW2;
+  b.wq = w2c;
+  b.wsc = w2s;
+  b.q_expert_stride = (long long)H * (I / 2);
+  b.s_expert_stride = (long long)H * (I / 32);
+  b.K = I;
+  b.N = H;
+  b.tile_info = p.tile_info;
+  b.n_tiles = p.n_tiles;
+  b.n_ntiles = H / 256;
+  b.a_hi = hh;
+  b.a_lo = hl;
+  b.as_hi = hsh;
+  b.as_lo = hsl;
+  b.act_row = nullptr;
+  b.yout = ybf;
+  b.yout_ld = H;
+  b.sorted_slots = p.sorted_slots;
+  b.slot_w = slot_w;
+  b.limit = c.swiglu_limit;
+  b.order = 0;
+  b.queue = at<int32_t>(ws, L.counters) + kGemmQueueInts + 9 * kQRoutedW2;
+  return timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm_mx(b, p.max_tiles, st); });
+}
+
 int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
   if (!ws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EINVAL;
@@ -435,6 +523,24 @@ int moe_device_flags(uint32_t* flags, int32_t clear, void* stream) {
   if (e != hipSuccess) return MOE_EHIP;
   if (flags) *flags = v;
   return MOE_OK;
+}
+
+int moe_set_option(int32_t option, int32_t value) {
+  switch (option) {
+    case MOE_OPTION_PREFILL_BLOCK_SCALED:
+      if (value != 0 && value != 1) return MOE_EINVAL;
+      g_opt_prefill_block_scaled = value;
+      return MOE_OK;
+    default:
+      return MOE_EINVAL;
+  }
+}
+
+int moe_get_option(int32_t option) {
+  switch (option) {
+    case MOE_OPTION_PREFILL_BLOCK_SCALED: return g_opt_prefill_block_scaled;
+    default: return MOE_EINVAL;
+  }
 }
 
 int moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
@@ -547,7 +653,11 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   if (rc) return rc;
   uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
   float* ybuf = at<float>(workspace, L.ybuf);
-  if (use_gemm(*cfg, T)) {
+  if (L.mx) {
+    rc = status(routed_gemms_mx(*cfg, T, x, p, topk_w, w13_codes, w13_scales, w2_codes, w2_scales, workspace, L,
+                                reinterpret_cast<uint16_t*>(ybuf), st));
+    if (rc) return rc;
+  } else if (use_gemm(*cfg, T)) {
     GemmArgs g13 = gemm_routed_w13(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
     GemmArgs g2 = gemm_routed_w2(*cfg, T, p, topk_w, w2_codes, w2_scales, hbuf, reinterpret_cast<uint16_t*>(ybuf));
     g13.queue = gemm_queue(workspace, L, kQRoutedW13);
@@ -769,6 +879,14 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       g2.queue = gemm_queue(workspace, L, kQRoutedW2);
       h2.queue = gemm_queue(workspace, L, kQSharedW2);
       const int sh_tiles = (T + kGemmTokens - 1) / kGemmTokens;
+      if (L.mx) {
+        rc = status(routed_gemms_mx(*cfg, T, x, p, w, w13_codes, w13_scales, w2_codes, w2_scales, workspace, L, ybf,
+                                    st));
+        if (rc) return rc;
+        rc = status(timed(MOE_KERNEL_SHARED_W13, st, [&] { return launch_gemm(h13, sh_tiles, st); }));
+        if (rc) return rc;
+        return status(timed(MOE_KERNEL_SHARED_W2, st, [&] { return launch_gemm(h2, sh_tiles, st); }));
+      }
       rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_gemm(g13, p.max_tiles, st); }));
       if (rc) return rc;
       rc = status(timed(MOE_KERNEL_SHARED_W13, st, [&] { return launch_gemm(h13, sh_tiles, st); }));

@@ -162,6 +162,46 @@ struct GemmArgs {
 };
 constexpr int kGemmTokens = 128;  // token positions per GEMM tile
 
+// Routed grouped GEMM on the block-scaled MFMA (gemm_mx.hip): MXFP4 weights x
+// activations split exactly into hi and lo fp8 (E4M3) halves with E8M0
+// exponents per 32 along K. Tiles of kGemmMxTokens positions x 512 weight
+// rows (w13: 256 gate + the matching 256 up rows).
+constexpr int kGemmMxTokens = 128;
+struct MxGemmArgs {
+  int mode;                   // kGemmW13: SwiGLU -> h split (hi/lo + exponents); kGemmW2: x slot weight -> yout
+  const uint8_t* wq;          // codes [E][rows][K/2]
+  const uint8_t* wsc;         // E8M0 [E][rows][K/32]
+  long long q_expert_stride, s_expert_stride;
+  int K;                      // input features
+  int half;                   // w13: I (the up rows start there)
+  int N;                      // output features (w13: I, w2: H)
+  const int4* tile_info;
+  const int32_t* n_tiles;
+  int n_ntiles;               // N tiles (w13: I / 256, w2: H / 512)
+  const uint8_t* a_hi;        // activations fp8 [rows][K]
+  const uint8_t* a_lo;
+  const uint8_t* as_hi;       // E8M0 [rows][K/32]
+  const uint8_t* as_lo;
+  const int32_t* act_row;     // activation row of each sorted position (null: the position)
+  uint8_t* h_hi;              // w13: h by sorted position, fp8 [slots][I] and E8M0 [slots][I/32]
+  uint8_t* h_lo;
+  uint8_t* hs_hi;
+  uint8_t* hs_lo;
+  int I;
+  uint16_t* yout;             // w2: bf16 rows by slot (x routing weight)
+  int yout_ld;
+  const int32_t* sorted_slots;
+  const float* slot_w;
+  int* queue;                 // [9] as GemmArgs::queue
+  float limit;
+  int order;                  // 0: the N tiles of a token tile adjacent; 1: the token tiles of an N tile adjacent
+};
+bool gemm_mx_supported(int H, int I);
+// x [rows][K] bf16 -> hi, lo fp8 [rows][K] and E8M0 [rows][K/32] each (the exact split)
+hipError_t launch_quant_rows(const uint16_t* x, long long rows, int K, uint8_t* hi, uint8_t* lo, uint8_t* sh,
+                             uint8_t* sl, hipStream_t st);
+hipError_t launch_gemm_mx(const MxGemmArgs& p, int tiles, hipStream_t st);
+
 struct CombineArgs {
   int T, H, k;
   const void* ybuf;   // [T*k][H] weighted expert outputs in slot order: fp32, or bf16 if y_bf16
