@@ -214,11 +214,13 @@ size_t moe_noalloc_max_bytes(void);
 
 /* The launch sequence moe_forward takes. */
 enum {
-  MOE_SCHED_SINGLE = 1,  /* T <= 2, learned router, shapes with a single-launch kernel whose whole
-                          * grid the device holds at once: the layer in one launch */
-  MOE_SCHED_TINY = 2,    /* T * (top_k + 1) <= 16 otherwise: three launches */
-  MOE_SCHED_DECODE = 3,  /* T <= 64: router, top-k + permutation, streaming w13, streaming w2, combine */
-  MOE_SCHED_LARGE = 4    /* larger T or a hash layer: route, permutation, grouped GEMMs, combine */
+  MOE_SCHED_SINGLE = 1,  /* T * (top_k + 1) <= 16, shapes with a single-launch kernel whose whole
+                          * grid the device holds at once: the layer in one launch (learned
+                          * router or hash layer) */
+  MOE_SCHED_TINY = 2,    /* T * (top_k + 1) <= 16 otherwise, learned router: three launches */
+  MOE_SCHED_DECODE = 3,  /* T <= 64 otherwise: router, top-k (or the hash table) + permutation,
+                          * streaming w13, streaming w2, combine */
+  MOE_SCHED_LARGE = 4    /* T > 64: route, permutation, grouped GEMMs, combine */
 };
 
 /* Which of the MOE_SCHED_* sequences moe_forward takes for T tokens on the

@@ -482,16 +482,24 @@ RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const floa
   a.keys = scores + (size_t)T * c.n_routed_experts;
   a.ids = ids;
   a.w = w;
+  a.token_ids = nullptr;
+  a.tid2eid = nullptr;
+  a.V = 0;
+  a.flags = device_flags();
   return a;
 }
 
 // The launch sequence of moe_forward (MOE_SCHED_*).
+// Hash layers take the same schedules, with the token's table row in place
+// of the top-k, except the three-launch tiny schedule (its routed w13 blocks
+// redo the top-k themselves): there they take the decode schedule.
 int schedule(const moe_config& c, int T, bool hash) {
-  if (!hash && T * (c.top_k + 1) <= 16)
-    return layer_small_supported(c.hidden_size, c.moe_intermediate, c.n_routed_experts, T, c.top_k)
-               ? MOE_SCHED_SINGLE
-               : MOE_SCHED_TINY;
-  if (!hash && T <= kSmallT) return MOE_SCHED_DECODE;
+  if (T * (c.top_k + 1) <= 16) {
+    if (layer_small_supported(c.hidden_size, c.moe_intermediate, c.n_routed_experts, T, c.top_k))
+      return MOE_SCHED_SINGLE;
+    if (!hash) return MOE_SCHED_TINY;
+  }
+  if (T <= kSmallT) return MOE_SCHED_DECODE;
   return MOE_SCHED_LARGE;
 }
 
@@ -774,6 +782,13 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     la.w_out = w;
     la.xfer = at<uint32_t>(workspace, L.xfer);
     la.flags = p.flags;
+    la.token_ids = hash ? token_ids : nullptr;
+    la.tid2eid = hash ? tid2eid : nullptr;
+    la.V = hash ? V : 0;
+    if (hash) {
+      la.bias = nullptr;  // selection bias and logit offset do not apply to hash layers
+      la.logit_offset = nullptr;
+    }
     return status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_layer_small(la, st); }));
   }
   if (tiny) {
@@ -802,9 +817,15 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
     return status(timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_w2_combine_small(c2, st); }));
   }
   if (decode) {
-    // router | top-k + permutation | routed w13 + shared w13 | routed w2 + shared w2 | combine,
-    // the expert passes as streaming blocks
-    RouterArgs a = router_args(*cfg, T, x, gate_w, bias, logit_offset, at<float>(workspace, L.scores), ids, w);
+    // router | top-k (or the hash table) + permutation | routed w13 + shared w13 | routed w2 +
+    // shared w2 | combine, the expert passes as streaming blocks
+    RouterArgs a = router_args(*cfg, T, x, gate_w, hash ? nullptr : bias, hash ? nullptr : logit_offset,
+                               at<float>(workspace, L.scores), ids, w);
+    if (hash) {
+      a.token_ids = token_ids;
+      a.tid2eid = tid2eid;
+      a.V = V;
+    }
     rc = status(timed(MOE_KERNEL_ROUTER, st, [&] { return launch_router_dec(a, st); }));
     if (rc) return rc;
     rc = status(timed(MOE_KERNEL_PERMUTE, st, [&] {

@@ -225,6 +225,60 @@ __device__ __forceinline__ void wave_topk_row(const TopkRow& row, int E, int k, 
   }
 }
 
+// Hash-layer routing of one token by a wave (page "Tidalluna/DeepSeek-V4-
+// Flash-0731-Tina-CQ4KM", section "Compatibility", item 2: the first layers
+// take their experts from a token-id table): the k experts of the token's
+// table row, in table order, weighted by their renormalised scores x scale.
+// row.s holds the scores of experts lane + 64 q. trow is the token's table
+// row, or null for a token id out of range (the caller flags it): then the
+// weights are NaN and the experts 0. A table entry outside [0, E) is taken
+// as expert 0, with NaN weights for the token and kFlagTableEntry set. COH:
+// ids and weights are written through to memory, as wave_topk_row.
+template <bool COH = false>
+__device__ __forceinline__ void wave_hash_row(const TopkRow& row, const int32_t* trow, int E, int k, float scale,
+                                              int32_t* ids_out, float* w_out, int32_t* ids_lds, uint32_t* flags) {
+  const int lane = threadIdx.x & 63;
+  float sel_s[kTopKMax];
+  int sel_id[kTopKMax];
+  bool ok = trow != nullptr, ent_ok = true;
+#pragma unroll
+  for (int j = 0; j < kTopKMax; ++j) {
+    sel_s[j] = 0.0f;
+    sel_id[j] = 0;
+    if (j >= k) continue;  // uniform
+    int e = ok ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
+    if ((unsigned)e >= (unsigned)E) {
+      ent_ok = false;
+      e = 0;
+    }
+    const int owner = e & 63, q_of = e >> 6;
+    const float mys = (q_of == 0) ? row.s[0] : (q_of == 1) ? row.s[1] : (q_of == 2) ? row.s[2] : row.s[3];
+    sel_s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mys), owner));
+    sel_id[j] = e;
+  }
+  ok = ok && ent_ok;
+  if (lane == 0) {
+    if (!ent_ok && flags) atomicOr(flags, 2u);  // kFlagTableEntry
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j)
+      if (j < k) sum += sel_s[j];
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) {
+      if (j >= k) continue;
+      const float wj = ok ? scale * sel_s[j] / sum : __builtin_nanf("");
+      if constexpr (COH) {
+        store_agent(reinterpret_cast<uint32_t*>(ids_out) + j, (uint32_t)sel_id[j]);
+        store_agent(reinterpret_cast<uint32_t*>(w_out) + j, __float_as_uint(wj));
+      } else {
+        ids_out[j] = sel_id[j];
+        w_out[j] = wj;
+      }
+      if (ids_lds) ids_lds[j] = sel_id[j];
+    }
+  }
+}
+
 template <bool COH = false>
 __device__ __forceinline__ void wave_topk(const float* s_row, const float* b_row, int E, int k, float scale,
                                           int32_t* ids_out, float* w_out, int32_t* ids_lds) {

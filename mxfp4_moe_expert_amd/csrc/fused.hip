@@ -272,7 +272,7 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
   if (w < TT) {
     float bq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bq[q] = a.bias[min(lane + 64 * q, E - 1)];
+    for (int q = 0; q < 4; ++q) bq[q] = a.bias ? a.bias[min(lane + 64 * q, E - 1)] : 0.0f;
     const uint32_t* srow = X.scores + w * kXferBlocks;
     uint32_t v[4];
     int spins = 0;
@@ -293,7 +293,15 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
       row.s[q] = __uint_as_float(v[q] ^ kScoreTag);
       row.b[q] = row.s[q] + bq[q];
     }
-    wave_topk_row(row, E, KK, a.scale, L.sid + w * KK, L.sw + w * KK, nullptr);
+    if (a.tid2eid) {  // hash layer: the token's table row (page "Tidalluna/...Tina-CQ4KM", "Compatibility")
+      const int tok = __builtin_amdgcn_readfirstlane(a.token_ids[w]);
+      const bool tok_ok = (unsigned)tok < (unsigned)a.V;
+      if (!tok_ok && lane == 0 && b == 0 && a.flags) atomicOr(a.flags, kFlagTokenId);
+      wave_hash_row(row, tok_ok ? a.tid2eid + (size_t)tok * KK : nullptr, E, KK, a.scale, L.sid + w * KK,
+                    L.sw + w * KK, nullptr, b == 0 ? a.flags : nullptr);
+    } else {
+      wave_topk_row(row, E, KK, a.scale, L.sid + w * KK, L.sw + w * KK, nullptr);
+    }
   }
   __syncthreads();
   if (b == 0 && tid < S::NS) {

@@ -54,6 +54,12 @@ struct RouterArgs {
   float* keys;    // [T][E] selection values fp32(s + bias)
   int32_t* ids;   // [T][k]
   float* w;       // [T][k]
+  // hash layers (tid2eid != null): the experts come from the token-id table
+  // (the decode-size top-k kernel); bias may then be null
+  const int32_t* token_ids;  // [T]
+  const int32_t* tid2eid;    // [V][k]
+  int V;
+  uint32_t* flags;           // device error-flag word
 };
 
 struct HashArgs {
@@ -305,6 +311,9 @@ struct LayerArgs {
   float* w_out;                // [T][k]
   uint32_t* xfer;              // hand-off region (kXferBytes, workspace)
   uint32_t* flags;             // device error-flag word (expired hand-off waits)
+  const int32_t* token_ids;    // hash layer (tid2eid != null): [T] token ids
+  const int32_t* tid2eid;      // [V][k] token-id table, or null (learned router)
+  int V;
 };
 // Whether the single-launch layer has a kernel for this shape whose whole
 // grid the current device holds at once.

@@ -34,7 +34,7 @@ namespace moe {
 __device__ __forceinline__ void store_score(const RouterArgs& a, int t, int e, float logit) {
   const float sc = sqrtf(softplus(logit));
   a.scores[(size_t)t * a.E + e] = sc;
-  a.keys[(size_t)t * a.E + e] = sc + a.bias[e];
+  a.keys[(size_t)t * a.E + e] = sc + (a.bias ? a.bias[e] : 0.0f);  // no bias on hash layers
 }
 
 // Logits of expert e for 8 < T <= kSmallT tokens, H <= 4096: wave w takes
@@ -227,9 +227,19 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
   // stores before the block is counted, and the last block reads them with
   // coherent loads (no cache write-back or invalidation: the fences that
   // did this cost about 1.5 us)
-  if (t < a.T)
-    wave_topk<true>(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale,
-                    a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, nullptr);
+  if (t < a.T) {
+    if (a.tid2eid) {  // hash layer: the token's table row instead of the top-k
+      const int tok = __builtin_amdgcn_readfirstlane(a.token_ids[t]);
+      const bool tok_ok = (unsigned)tok < (unsigned)a.V;
+      if (!tok_ok && (tid & 63) == 0 && a.flags) atomicOr(a.flags, kFlagTokenId);
+      const float* srow = a.scores + (size_t)t * a.E;
+      wave_hash_row<true>(topk_load(srow, srow, a.E), tok_ok ? a.tid2eid + (size_t)tok * a.k : nullptr, a.E, a.k,
+                          a.scale, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, nullptr, a.flags);
+    } else {
+      wave_topk<true>(a.scores + (size_t)t * a.E, a.keys + (size_t)t * a.E, a.E, a.k, a.scale,
+                      a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, nullptr);
+    }
+  }
   __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));  // vmcnt(0): this wave's stores are done
   __syncthreads();
   if (tid == 0) is_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;

@@ -140,3 +140,15 @@ def test_clamp_large():
 
 def test_clamp_hash_large():
     _check(MID_HASH, 250, 206, "large", hash_layer=True)
+
+
+DEC2_HASH = synth.Workload("dec2_hash", T=17, H=2048, E=64, k=6, I=1024, V=5000, hash_layer=True, seed=3)
+LAY_HASH = synth.Workload("lay_hash", T=1, H=2048, E=64, k=6, I=1024, V=5000, hash_layer=True, seed=4)
+
+
+def test_clamp_hash_decode():
+    _check(DEC2_HASH, 17, 207, "decode", hash_layer=True)
+
+
+def test_clamp_hash_single_launch():
+    _check(LAY_HASH, 1, 208, "single", hash_layer=True)

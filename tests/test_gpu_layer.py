@@ -49,7 +49,9 @@ def test_single_launch_schedule_taken(lay, T):
     wl, L, D, cfg = lay
     assert mx.forward_schedule(cfg, T) == "single"
     assert mx.forward_schedule(cfg, 3) == "decode"
-    assert mx.forward_schedule(cfg, T, hash_layer=True) == "large"
+    assert mx.forward_schedule(cfg, T, hash_layer=True) == "single"
+    assert mx.forward_schedule(cfg, 3, hash_layer=True) == "decode"
+    assert mx.forward_schedule(cfg, 65, hash_layer=True) == "large"
 
 
 @pytest.mark.parametrize("T,rep", [(1, 0), (1, 1), (2, 0), (2, 1)])
