@@ -189,6 +189,45 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One MoE layer's parameters for moe_forward_stack (device pointers, layouts
+ * as for moe_forward). tid2eid != NULL makes it a hash layer (V rows); then
+ * bias and logit_offset are ignored. */
+typedef struct moe_layer_weights {
+  const float* gate_w;         /* [E][H] */
+  const float* bias;           /* [E] (learned router) */
+  const float* logit_offset;   /* [E] or NULL */
+  const int32_t* tid2eid;      /* [V][k] or NULL */
+  int32_t V;
+  const uint8_t* w13_codes;    /* [E][2I][H/2] */
+  const uint8_t* w13_scales;   /* [E][2I][H/32] */
+  const uint8_t* w2_codes;     /* [E][H][I/2] */
+  const uint8_t* w2_scales;    /* [E][H][I/32] */
+  const int8_t* sh_w13;        /* [2I][H] */
+  const float* sh_w13_scale;   /* [2I] */
+  const int8_t* sh_w2;         /* [H][I] */
+  const float* sh_w2_scale;    /* [H] */
+} moe_layer_weights;
+
+/* A stack of MoE layers run back to back on `stream`, as the model's 43 MoE
+ * layers are, the first num_hash_layers routed by the token-id table (page
+ * "DeepSeek-V4-Flash export design", section "Source configuration"; page
+ * "deepseek-v4-mxfp4-int8 config.json", num_hidden_layers,
+ * num_hash_layers): layer 0 reads x, layer l + 1 reads the bf16 output of
+ * layer l (the attention and residual steps the model has between its MoE
+ * layers are not part of this library), and the last layer writes out (bf16,
+ * or fp32 if out_is_fp32).
+ *   layers     host array of n_layers parameter sets (read during the call)
+ *   token_ids  [T] i32, used by the hash layers (may be NULL if none is)
+ *   act        [2][T][H] bf16 device scratch for the layers' outputs (the
+ *              output of layer l, l < n_layers - 1, is left in act[l % 2])
+ *   workspace  as for moe_forward (moe_workspace_size(cfg, T) bytes), shared
+ *              by the layers in turn
+ * Each layer takes the schedule moe_forward takes for it. Errors as for
+ * moe_forward; a failed layer stops the stack. */
+int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_weights* layers, int32_t T,
+                      const uint16_t* x, const int32_t* token_ids, uint16_t* act, void* out,
+                      int32_t out_is_fp32, void* workspace, size_t workspace_bytes, void* stream);
+
 /* moe_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). Its workspace is a fixed scratch array

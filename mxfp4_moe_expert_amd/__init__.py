@@ -31,6 +31,15 @@ class MoEError(RuntimeError):
         self.status = status
 
 
+class MoeLayerWeights(ctypes.Structure):
+    """Mirror of ``moe_layer_weights`` (device pointers of one layer)."""
+    _fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("logit_offset", ctypes.c_void_p),
+                ("tid2eid", ctypes.c_void_p), ("V", ctypes.c_int32), ("w13_codes", ctypes.c_void_p),
+                ("w13_scales", ctypes.c_void_p), ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p),
+                ("sh_w13", ctypes.c_void_p), ("sh_w13_scale", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p),
+                ("sh_w2_scale", ctypes.c_void_p)]
+
+
 class MoeConfig(ctypes.Structure):
     """Mirror of ``moe_config`` (names of the checkpoint's config.json)."""
     _fields_ = [("hidden_size", ctypes.c_int32), ("n_routed_experts", ctypes.c_int32),
@@ -69,6 +78,7 @@ _SIGNATURES = {
     "moe_get_option": ([_I32], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
     "moe_noalloc_max_bytes": ([], _SZ),
+    "moe_forward_stack": ([_CFGP, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _SZ, _VP], ctypes.c_int),
     "moe_forward_noalloc": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                              _VP, _VP, _VP, _I32, _VP, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -380,4 +390,37 @@ def forward_noalloc(cfg: MoeConfig, x, layer: DeviceLayer, token_ids=None, out_f
         _ptr(layer.w13_scales), _ptr(layer.w2_codes), _ptr(layer.w2_scales), _ptr(layer.sh_w13),
         _ptr(layer.sh_w13_scale), _ptr(layer.sh_w2), _ptr(layer.sh_w2_scale), _ptr(out), int(out_fp32),
         _ptr(ids), _ptr(w), _stream(dev)), "moe_forward_noalloc")
+    return out
+
+
+def layer_weights(layer: DeviceLayer) -> MoeLayerWeights:
+    """The ``moe_layer_weights`` of a device layer (hash layer if it has a tid2eid table)."""
+    def p(t):
+        return None if t is None else t.data_ptr()
+    V = 0 if layer.tid2eid is None else layer.tid2eid.shape[0]
+    return MoeLayerWeights(p(layer.gate_w), p(layer.bias), p(layer.logit_offset), p(layer.tid2eid), V,
+                           p(layer.w13_codes), p(layer.w13_scales), p(layer.w2_codes), p(layer.w2_scales),
+                           p(layer.sh_w13), p(layer.sh_w13_scale), p(layer.sh_w2), p(layer.sh_w2_scale))
+
+
+def forward_stack(cfg: MoeConfig, x, layers, token_ids=None, out_fp32=False, ws=None, act=None, out=None,
+                  weights=None):
+    """MoE layers back to back (moe_forward_stack): layer l + 1 reads layer l's
+    bf16 output. ``layers``: DeviceLayers (hash layers carry tid2eid);
+    ``weights``: their prebuilt ctypes array (optional, for repeated calls)."""
+    T, H = x.shape[0], cfg.hidden_size
+    dev = x.device
+    _need(x, _BF16, (T, H), "x")
+    n = len(layers)
+    if weights is None:
+        weights = (MoeLayerWeights * n)(*[layer_weights(L) for L in layers])
+    if token_ids is not None:
+        _need(token_ids, torch.int32, (T,), "token_ids")
+    if act is None:
+        act = torch.empty(2, T, H, dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=dev)
+    buf, nb = _ws(cfg, T, dev, ws)
+    _check(lib().moe_forward_stack(ctypes.byref(cfg), n, weights, T, _ptr(x), _ptr(token_ids), _ptr(act),
+                                   _ptr(out), int(out_fp32), _ptr(buf), nb, _stream(dev)), "moe_forward_stack")
     return out

@@ -704,6 +704,32 @@ int moe_expert_ffn(const moe_config* cfg, int32_t T, const uint16_t* x, const in
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
 }
 
+int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_weights* layers, int32_t T,
+                      const uint16_t* x, const int32_t* token_ids, uint16_t* act, void* out, int32_t out_is_fp32,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg || n_layers < 0 || T < 0) return MOE_EINVAL;
+  if (!cfg_ok(cfg) || T > kMaxT) return MOE_EUNSUPPORTED;
+  if (n_layers == 0 || T == 0) return MOE_OK;
+  if (!layers || !x || !out || (n_layers > 1 && !act)) return MOE_EINVAL;
+  if (act && !aligned16(act)) return MOE_EINVAL;
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l].tid2eid && !token_ids) return MOE_EINVAL;
+  const size_t plane = (size_t)T * cfg->hidden_size;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights& W = layers[l];
+    const bool hash = W.tid2eid != nullptr;
+    const bool last = l == n_layers - 1;
+    const uint16_t* in = l == 0 ? x : act + (size_t)((l - 1) & 1) * plane;
+    void* dst = last ? out : static_cast<void*>(act + (size_t)(l & 1) * plane);
+    const int rc = moe_forward(cfg, T, in, W.gate_w, W.bias, W.logit_offset, hash ? token_ids : nullptr,
+                               W.tid2eid, W.V, W.w13_codes, W.w13_scales, W.w2_codes, W.w2_scales, W.sh_w13,
+                               W.sh_w13_scale, W.sh_w2, W.sh_w2_scale, dst, last ? out_is_fp32 : 0, nullptr,
+                               nullptr, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+  }
+  return MOE_OK;
+}
+
 int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash) {
   if (!cfg) return MOE_EINVAL;
   if (!cfg_ok(cfg) || T > kMaxT) return MOE_EUNSUPPORTED;

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # Counter streams: one per tensor kind, so each tensor is regenerable alone.
 S_W13, S_W2, S_SH_W13, S_SH_W2, S_GATE, S_BIAS, S_OFFSET, S_TOKENS, S_TIDS, S_TID2EID = range(1, 11)
+S_STACK_PERM = 11  # per-layer expert order of a layer stack
 
 _lib = None
 
@@ -235,3 +236,49 @@ def make_token_ids(wl: Workload, rep: int = 0, T: int | None = None) -> np.ndarr
     """int32 [T] token ids, Zipf(wl.zipf_s) over the vocabulary."""
     T = wl.T if T is None else T
     return zipf_ids(wl.seed, S_TIDS, rep, T, wl.V, wl.zipf_s)
+
+
+# ---------------------------------------------------------------- layer stack
+
+# The model's MoE layers: 43, the first 3 routed by the token-id table
+# (page "DeepSeek-V4-Flash export design", section "Source configuration";
+# page "deepseek-v4-mxfp4-int8 config.json", num_hidden_layers, num_hash_layers).
+STACK_LAYERS, STACK_HASH_LAYERS = 43, 3
+
+
+def stack_expert_order(l: int, E: int) -> np.ndarray:
+    """Layer l's routed expert e is expert order[e] of the base layer: a
+    seeded permutation (Fisher-Yates on SplitMix64 draws, stream S_STACK_PERM,
+    sub-sequence l); layer 0 keeps the base order."""
+    order = np.arange(E, dtype=np.int64)
+    if l == 0:
+        return order
+    L = lib()
+    for i in range(E - 1, 0, -1):
+        j = int(L.synth_u64(0, S_STACK_PERM, l, i) % (i + 1))
+        order[i], order[j] = order[j], order[i]
+    return order
+
+
+def make_stack_layer(base: Layer, l: int, n_hash: int = STACK_HASH_LAYERS, routed: bool = True) -> Layer:
+    """Layer l of a stack built on ``base`` (its workload's shapes): routed
+    experts = the base layer's experts in the seeded order of
+    stack_expert_order (1/E of the generation cost per layer, every layer's
+    expert tensors in their own memory); router weight, bias, shared expert
+    and (layers below n_hash) the token-id table drawn fresh for the layer
+    (sub-sequence l + 1 of their streams). Layers below n_hash are hash-routed.
+    routed=False leaves the routed expert arrays out (None): the caller
+    builds them from the base layer's device copy with the same order."""
+    wl = base.wl
+    s, H, E, I, k = wl.seed, wl.H, wl.E, wl.I, wl.k
+    order = stack_expert_order(l, E)
+    hash_layer = l < n_hash
+    lw = replace(wl, name=f"{wl.name}_layer{l}", hash_layer=hash_layer)
+    sh13, sh13s = int8_normal(s, S_SH_W13, l + 1, 2 * I, H, wl.weight_sigma)
+    sh2, sh2s = int8_normal(s, S_SH_W2, l + 1, H, I, wl.weight_sigma)
+    gate = normal_f32(s, S_GATE, l + 1, E * H, wl.gate_sigma).reshape(E, H)
+    bias = normal_f32(s, S_BIAS, l + 1, E, wl.bias_sigma)
+    t2e = tid2eid(s, S_TID2EID, l + 1, wl.V, E, k) if hash_layer else None
+    pick = (lambda a: a[order]) if routed else (lambda a: None)
+    return Layer(lw, gate, bias, None, pick(base.w13_codes), pick(base.w13_scales), pick(base.w2_codes),
+                 pick(base.w2_scales), sh13, sh13s, sh2, sh2s, t2e, extra={"expert_order": order, "layer": l})

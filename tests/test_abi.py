@@ -126,7 +126,10 @@ def test_forward_schedule_host_logic():
     assert L.moe_forward_schedule(ctypes.byref(cfg), -1, 0) == mx.MOE_EINVAL
     assert L.moe_forward_schedule(ctypes.byref(cfg), 65537, 0) == mx.MOE_EUNSUPPORTED
     assert L.moe_forward_schedule(ctypes.byref(_cfg(top_k=9)), 1, 0) == mx.MOE_EUNSUPPORTED
-    assert mx.forward_schedule(cfg, 1, hash_layer=True) == "large"
+    small = _cfg(hidden_size=1024, moe_intermediate=512, n_routed_experts=32)
+    assert mx.forward_schedule(small, 1, hash_layer=True) == "decode"  # no single-launch kernel at hidden 1024
+    assert mx.forward_schedule(cfg, 17, hash_layer=True) == "decode"
+    assert mx.forward_schedule(cfg, 65, hash_layer=True) == "large"
     assert mx.forward_schedule(cfg, 3) == "decode"
     assert mx.forward_schedule(cfg, 64) == "decode"
     assert mx.forward_schedule(cfg, 65) == "large"
