@@ -40,6 +40,7 @@ DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), b
     "decode_t64": (200, 20, 12, "routed_w13", "hbm"),
     "prefill_t8192": (20, 3, 1, "routed_w13", "mfma"),
     "hash_t4096": (20, 3, 1, "routed_w13", "mfma"),
+    "stack43_t1": (100, 5, 1, "routed_w13", "hbm"),
 }
 # The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
 # names it, what it does there, and which algorithmic work it is priced on.
@@ -52,6 +53,9 @@ DOMINANT = {
                    "then routed MXFP4 (x routing weight) + shared int8 w2", "experts"),
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
     "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
+    "stack43_t1": ("moe::k_layer_small<4, 2, 1, 6>",
+                   "one layer of the 43-layer stack in one launch (three hash-routed layers, then learned-router "
+                   "layers), each layer reading the previous layer's output", "layer"),
 }
 # with --prefill-mfma block-scaled (moe_set_option MOE_OPTION_PREFILL_BLOCK_SCALED)
 DOMINANT_MX = ("moe::k_gemm_mx<0>",
@@ -615,7 +619,173 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
     return rec
 
 
-ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096"]
+def stack_cpu_leg(base_host, base_copies, layers_dev, budget_s):
+    """The oracle on the stack: checked layers (0, 1, 3 and the last) each on
+    its own seeded token against the GPU, the first two layers chained
+    (the oracle's layer 1 reads its own layer 0's bf16 output) against the
+    GPU stack, and the oracle's rate per token through all layers from its
+    time per layer."""
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_amd as mx
+    import oracle
+    import synth
+
+    wl = base_host.wl
+    cfg = mx.config_of(wl)
+    dev = base_copies[0].gate_w.device
+    nl = len(layers_dev)
+    checked = [0, 1, 3, nl - 1]
+    hosts = {l: synth.make_stack_layer(base_host, l) for l in checked}
+    tz = synth.WORKLOADS["hash_t4096"]
+    worst, times = 0.0, []
+    for l in checked:
+        L = hosts[l]
+        xh = synth.make_tokens(wl, rep=900 + l, T=1)
+        tid_h = synth.make_token_ids(tz, rep=900 + l, T=1)
+        hsh = L.wl.hash_layer
+        out = mx.forward(cfg, mx.bf16_from_numpy(xh, dev), layers_dev[l],
+                         token_ids=torch.from_numpy(tid_h).to(dev) if hsh else None, out_fp32=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = oracle.forward(L, xh, token_ids=tid_h if hsh else None)
+        times.append(time.perf_counter() - t0)
+        d = out.cpu().double().numpy() - r["out"]
+        worst = max(worst, float(np.linalg.norm(d) / np.linalg.norm(r["out"])))
+    # the first two layers chained
+    xh = synth.make_tokens(wl, rep=950, T=1)
+    tid_h = synth.make_token_ids(tz, rep=950, T=1)
+    r0 = oracle.forward(hosts[0], xh, token_ids=tid_h)
+    x1 = synth.f32_to_bf16(r0["out"].astype(np.float32))
+    r1 = oracle.forward(hosts[1], x1, token_ids=tid_h)
+    out = mx.forward_stack(cfg, mx.bf16_from_numpy(xh, dev), layers_dev[:2],
+                           token_ids=torch.from_numpy(tid_h).to(dev), out_fp32=True)
+    torch.cuda.synchronize()
+    d = out.cpu().double().numpy() - r1["out"]
+    chain = float(np.linalg.norm(d) / np.linalg.norm(r1["out"]))
+    per_layer = sum(times) / len(times)
+    threads = oracle.lib().or_num_threads()
+    cb = dict(value=1.0 / (nl * per_layer), unit="tokens/s", cores=int(threads), kind="oracle",
+              sample=f"{len(checked)} of {nl} layers at T=1 (layers {checked}), rate = 1 / ({nl} x mean layer time)",
+              seconds=round(sum(times), 2))
+    check = dict(layers_checked=checked, rel_l2_max=worst, chain_layers_0_1_rel_l2=chain,
+                 within_bar=bool(worst <= 5e-3 and chain <= 5e-3))
+    return cb, check
+
+
+def run_stack(args, name, base_host, base_copies, K, W, cpu_budget):
+    """K steps of one token through the 43-layer stack (moe_forward_stack),
+    every layer's weights in their own device memory (about 147 GB)."""
+    import torch
+
+    import mxfp4_moe_expert_amd as mx
+    import synth
+
+    wl = base_host.wl
+    cfg = mx.config_of(wl)
+    dev = base_copies[0].gate_w.device
+    nl = synth.STACK_LAYERS
+    t0 = time.perf_counter()
+    layers = []
+    for l in range(nl):
+        Lh = synth.make_stack_layer(base_host, l, routed=False)
+        order = torch.from_numpy(Lh.extra["expert_order"]).to(dev)
+        b = base_copies[0]
+        pick = (lambda t: t.index_select(0, order)) if l else (lambda t: t)
+
+        def d(a):
+            return None if a is None else torch.from_numpy(a).to(dev)
+        layers.append(mx.DeviceLayer(d(Lh.gate_w), d(Lh.bias), None, pick(b.w13_codes), pick(b.w13_scales),
+                                     pick(b.w2_codes), pick(b.w2_scales), d(Lh.sh_w13), d(Lh.sh_w13_scale),
+                                     d(Lh.sh_w2), d(Lh.sh_w2_scale), d(Lh.tid2eid)))
+    torch.cuda.synchronize(dev)
+    t_build = time.perf_counter() - t0
+    print(f"[bench] {name}: {nl} layers built in {t_build:.1f} s", file=sys.stderr, flush=True)
+    weights = (mx.MoeLayerWeights * nl)(*[mx.layer_weights(L) for L in layers])
+    nb = min(K + W, 256)
+    xs = torch.stack([mx.bf16_from_numpy(synth.make_tokens(wl, rep=r, T=1), dev) for r in range(nb)])
+    tz = synth.WORKLOADS["hash_t4096"]
+    tids = torch.stack([torch.from_numpy(synth.make_token_ids(tz, rep=r, T=1)) for r in range(nb)]).to(dev)
+    act = torch.empty(2, 1, wl.H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(1, wl.H, dtype=torch.bfloat16, device=dev)
+    ws = mx.Workspace(dev)
+    buf = ws.get(cfg, 1)
+    L = mx.lib()
+
+    def args_of(s, st):
+        P = mx._ptr
+        return (ctypes.byref(cfg), nl, weights, 1, P(xs[s % nb]), P(tids[s % nb]), P(act), P(out), 0, P(buf),
+                buf.numel(), ctypes.c_void_p(st))
+
+    stream = torch.cuda.current_stream(dev)
+    for s in range(W):
+        rc = L.moe_forward_stack(*args_of(s, stream.cuda_stream))
+        if rc != 0:
+            raise mx.MoEError(rc, "moe_forward_stack")
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(K):
+        rc = L.moe_forward_stack(*args_of(s, stream.cuda_stream))
+        if rc != 0:
+            raise mx.MoEError(rc, "moe_forward_stack")
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    eager_ms = e0.elapsed_time(e1)
+    graph_ms = None
+    if args.mode == "graph":
+        G = max(1, min(10, K))
+        cs = torch.cuda.Stream(dev)
+        graphs = []
+        with torch.cuda.stream(cs):
+            for g0 in range(0, K, G):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cs):
+                    for s in range(g0, min(K, g0 + G)):
+                        rc = L.moe_forward_stack(*args_of(s, cs.cuda_stream))
+                        if rc != 0:
+                            raise mx.MoEError(rc, "moe_forward_stack (capture)")
+                graphs.append(gr)
+        torch.cuda.synchronize(dev)
+        graphs[0].replay()
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        graph_ms = e0.elapsed_time(e1)
+        del graphs
+    total_ms = graph_ms if graph_ms is not None else eager_ms
+    ms_step = total_ms / K
+    import numpy as np
+    per_layer = algorithmic(wl, np.arange(wl.k, dtype=np.int32).reshape(1, 1, wl.k))  # 6 distinct experts per layer
+    launch_ms = ms_step / nl
+    achieved = per_layer["layer_bytes"] / (launch_ms / 1e3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(achieved / PEAK_HBM_GBS, 4), algorithmic=int(per_layer["layer_bytes"]), traffic=None,
+                kernel=DOMINANT[name][0], kernel_avg_us=round(launch_ms * 1e3, 2),
+                kernel_time=f"timed region / (steps x {nl} launches): every launch is one layer")
+    rec = {"T": 1, "layers": nl, "hash_layers": synth.STACK_HASH_LAYERS, "schedule": "single per layer",
+           "steps": K, "warmup": W, "weight_copies": "one per layer", "mode": args.mode,
+           "ms_per_step": round(ms_step, 5), "tokens_per_s": round(1e3 / ms_step, 1),
+           "roofline": roof,
+           "stack": {"bytes_per_step": int(nl * per_layer["layer_bytes"]),
+                     "hbm_GBps": round(nl * per_layer["layer_bytes"] / (ms_step / 1e3) / 1e9, 1),
+                     "eager_ms_per_step": round(eager_ms / K, 5),
+                     "graph_ms_per_step": None if graph_ms is None else round(graph_ms / K, 5),
+                     "build_seconds": round(t_build, 1), "device_bytes_of_weights": int(nl * 3422552064)}}
+    if cpu_budget > 0:
+        cb, check = stack_cpu_leg(base_host, base_copies, layers, cpu_budget)
+        rec["cpu_baseline"] = cb
+        rec["parity"] = check
+    del layers, weights, xs, tids, act, out, ws, buf
+    torch.cuda.empty_cache()
+    return rec
+
+
+ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096", "stack43_t1"]
 
 
 def main():
@@ -669,7 +839,12 @@ def main():
         K, W, C = plan[n]
         budget = 0.0 if args.no_cpu_baseline else (args.cpu_seconds if i == 0 else args.extra_cpu_seconds)
         print(f"[bench] {n}: {K} steps after {W} warm-up, {C} weight copies", file=sys.stderr, flush=True)
-        recs[n] = run_workload(args, n, base_host, base_copies, K, W, C, budget)
+        if n == "stack43_t1":
+            del base_copies[1:]  # the stack's layers take their own copies
+            torch.cuda.empty_cache()
+            recs[n] = run_stack(args, n, base_host, base_copies, K, W, budget)
+        else:
+            recs[n] = run_workload(args, n, base_host, base_copies, K, W, C, budget)
         print(f"[bench] {n}: {recs[n]['ms_per_step']} ms/step, {recs[n]['tokens_per_s']} tokens/s",
               file=sys.stderr, flush=True)
     m = recs[main_name]
@@ -684,7 +859,7 @@ def main():
                    "prefill_mfma": args.prefill_mfma,
                    "schedule": m["schedule"], "parallelism": "single GPU"},
         "roofline": m["roofline"],
-        "layer": m["layer"],
+        "layer": m.get("layer", m.get("stack")),
         "cpu_baseline": m.get("cpu_baseline"),
         "parity": m.get("parity"),
         "gen_seconds": round(t_gen, 1),

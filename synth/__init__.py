@@ -184,6 +184,8 @@ WORKLOADS = {
     "prefill_t8192": Workload("prefill_t8192", T=8192, offset_sigma=0.5),
     # full-shape hash-routed layer, 4096 Zipf tokens
     "hash_t4096": Workload("hash_t4096", T=4096, hash_layer=True),
+    # one token through the 43-layer stack (3 hash-routed layers, then learned-router layers)
+    "stack43_t1": Workload("stack43_t1", T=1),
 }
 
 
