@@ -82,8 +82,9 @@ def _open(path: str):
     L.or_shared_ffn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, dbl, i32, vp]
     L.or_forward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                              vp, vp, vp, vp, dbl, dbl, i32, vp, i32, vp, vp, vp, vp, vp, vp]
+    L.or_linear_w8a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
     for f in ("or_route", "or_hash_route", "or_permute", "or_expert_ffn", "or_shared_ffn",
-              "or_forward"):
+              "or_forward", "or_linear_w8a16"):
         getattr(L, f).restype = i32
     return L
 
@@ -253,3 +254,19 @@ def forward(layer, x, token_ids=None, rows=None, force_ids=None, round_h=True):
         wl.routed_scaling_factor, wl.swiglu_limit, int(round_h), _p(rows_a), n,
         _p(_c(force_ids, np.int32)), _p(ids), _p(w), _p(gap), _p(nxt), _p(out)), "forward")
     return dict(ids=ids, w=w, gap=gap, next=nxt, out=out)
+
+
+def linear_w8a16(x, q, s, groups=1):
+    """int8 per-channel linear (grouped if groups > 1): x [T][groups*K] bf16,
+    q [groups*N][K] int8 (group g's rows g*N .. g*N+N-1), s [groups*N] fp32
+    -> out [T][groups*N] fp64."""
+    x = _c(x, np.uint16)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    T = x.shape[0]
+    K = x.shape[1] // groups
+    N = q.shape[0] // groups
+    assert q.shape == (groups * N, K) and s.shape == (groups * N,)
+    out = np.empty((T, groups * N), np.float64)
+    _check(lib().or_linear_w8a16(T, K, N, groups, _p(x), _p(q), _p(s), _p(out)), "linear_w8a16")
+    return out

@@ -444,3 +444,32 @@ int or_forward(int T, int H, int E, int k, int I, const uint16_t* x, const float
   free(hbuf);
   return rc;
 }
+
+/* ---- int8 per-channel linear layers ("w8a16") --------------------------- */
+
+/* The attention projections of the model are int8, symmetric, one scale per
+ * output channel, with 16-bit activations (page "deepseek-v4-mxfp4-int8
+ * config.json", quantization_config, config group linears_w8a16: targets
+ * fused_wqa_wkv, wq_b, wo_a, wo_b, indexer.wq_b, indexer.compressor.wkv).
+ * groups > 1 is a block-diagonal (grouped) projection: group g maps input
+ * features [g*K, (g+1)*K) to output features [g*N, (g+1)*N) with its own
+ * weights.
+ *   x [T][groups*K] bf16, q [groups][N][K] int8, s [groups][N] fp32
+ *   out[t][g*N + n] = s[g][n] * sum_k q[g][n][k] * x[t][g*K + k]   (fp64) */
+int or_linear_w8a16(int T, int K, int N, int groups, const uint16_t* x, const int8_t* q, const float* s,
+                    double* out) {
+  if (T < 0 || K <= 0 || N <= 0 || groups <= 0) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; ++t) {
+    for (int g = 0; g < groups; ++g) {
+      const uint16_t* xt = x + ((int64_t)t * groups + g) * K;
+      for (int n = 0; n < N; ++n) {
+        const int8_t* row = q + ((int64_t)g * N + n) * K;
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) acc += (double)row[k] * or_bf16_value(xt[k]);
+        out[((int64_t)t * groups + g) * N + n] = (double)s[(int64_t)g * N + n] * acc;
+      }
+    }
+  }
+  return OR_OK;
+}

@@ -556,10 +556,33 @@ def check_forward_hash():
     assert np.allclose(r["out"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
 
 
+def check_linear_w8a16():
+    """The int8 per-channel linear against numpy's matmul of the decoded
+    weights (q times its row's scale), plain and grouped (block-diagonal):
+    each group reads only its own input slice and writes only its own output
+    slice; doubling one group's scales doubles exactly that group's outputs."""
+    rng = _rng(13)
+    for T, K, N, G in ((3, 64, 48, 1), (5, 32, 16, 4), (1, 96, 8, 2)):
+        q = rng.integers(-127, 128, size=(G * N, K), dtype=np.int8)
+        sc = rng.uniform(0.001, 0.05, size=G * N).astype(np.float32)
+        x = synth.f32_to_bf16(rng.standard_normal((T, G * K)).astype(np.float32))
+        got = oracle.linear_w8a16(x, q, sc, groups=G)
+        xd = bf16_to_f64(x)
+        W = q.astype(np.float64) * sc.astype(np.float64)[:, None]
+        want = np.concatenate([xd[:, g * K:(g + 1) * K] @ W[g * N:(g + 1) * N].T for g in range(G)], axis=1)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max()), (T, K, N, G)
+        if G > 1:
+            sc2 = sc.copy()
+            sc2[N:2 * N] *= 2
+            got2 = oracle.linear_w8a16(x, q, sc2, groups=G)
+            assert np.array_equal(got2[:, N:2 * N], 2 * got[:, N:2 * N])
+            assert np.array_equal(np.delete(got2, np.s_[N:2 * N], axis=1), np.delete(got, np.s_[N:2 * N], axis=1))
+
+
 ALL_CHECKS = [
     check_e2m1_codes, check_e8m0_bytes, check_mxfp4_layout, check_block_bytes, check_bf16_values,
     check_softplus_score, check_swiglu, check_topk_exhaustive, check_topk_random, check_fp32_decision,
     check_noaux_bias, check_weights_sum, check_hash_route, check_permute, check_expert_ffn,
     check_shared_ffn, check_linearity, check_special_case_dense, check_forward_tiny,
-    check_forward_forced_ids, check_forward_hash,
+    check_forward_forced_ids, check_forward_hash, check_linear_w8a16,
 ]

@@ -80,6 +80,12 @@ MUTATIONS = [
     ("forward_hash_uses_bias", "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);",
      "tid2eid + (int64_t)tids[t] * k, scale, idr, wr);"
      " for (int j = 0; j < k; ++j) wr[j] *= 1.0 + 0.5 * (double)bias[idr[j]];"),
+    ("linear_input_group", "const uint16_t* xt = x + ((int64_t)t * groups + g) * K;",
+     "const uint16_t* xt = x + (int64_t)t * groups * K;"),
+    ("linear_weight_group", "const int8_t* row = q + ((int64_t)g * N + n) * K;",
+     "const int8_t* row = q + (int64_t)n * K;"),
+    ("linear_scale_row", "out[((int64_t)t * groups + g) * N + n] = (double)s[(int64_t)g * N + n] * acc;",
+     "out[((int64_t)t * groups + g) * N + n] = (double)s[n] * acc;"),
 ]
 
 
