@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--extra-cpu-seconds", type=float, default=3.0,
                     help="budget of the CPU oracle sample of each further workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--linears", action="store_true",
+                    help="also time the int8 attention projections (always with --workload all)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--peaks", action="store_true",
                     help="measure a 1 GiB device copy and a bf16 matmul (denominators beside the published peaks)")
@@ -785,6 +787,58 @@ def run_stack(args, name, base_host, base_copies, K, W, cpu_budget):
     return rec
 
 
+# The model's int8 attention projections (page "deepseek-v4-mxfp4-int8 config.json", config group
+# linears_w8a16) as (K, N, groups); the pages name them, the shapes are readings of the model's sizes.
+LINEARS = {"fused_wqa_wkv": (4096, 1536, 1), "wq_b": (1024, 32768, 1), "wo_a": (4096, 1024, 8),
+           "wo_b": (8192, 4096, 1), "indexer_wq_b": (1024, 8192, 1), "indexer_compressor_wkv": (4096, 256, 1)}
+
+
+def run_linears(reps=40, copies=4):
+    """moe_linear_w8a16 on each projection at T = 1, 64 (bound by the int8
+    weights' bytes) and 8192 (bf16 MFMA), weights rotated through `copies`
+    copies (together beyond the last-level cache), events around each call
+    on the launch stream; the mean per call."""
+    import torch
+
+    import mxfp4_moe_expert_amd as mx
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for i, (name, (K, N, G)) in enumerate(LINEARS.items()):
+        q, sc = synth.int8_normal(0, 12, i, G * N, K, 0.02)
+        qs = [torch.from_numpy(q).to(dev) for _ in range(copies)]
+        ss = [torch.from_numpy(sc).to(dev) for _ in range(copies)]
+        wbytes = G * N * K + G * N * 4
+        res[name] = {"K": K, "N": N, "groups": G}
+        for T in (1, 64, 8192):
+            x = mx.bf16_from_numpy(synth.normal_bf16(0, synth.S_TOKENS, 800 + T, T * G * K).reshape(T, G * K), dev)
+            out = torch.empty(T, G * N, dtype=torch.bfloat16, device=dev)
+            n = reps if T <= 64 else 10
+            for r in range(3):
+                mx.linear_w8a16(x, qs[r % copies], ss[r % copies], groups=G, out=out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record(stream)
+            for r in range(n):
+                mx.linear_w8a16(x, qs[r % copies], ss[r % copies], groups=G, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            us = e0.elapsed_time(e1) * 1e3 / n
+            if T <= 64:
+                b = wbytes + T * G * (K + N) * 2
+                res[name][f"T{T}"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                                      "hbm_frac": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+            else:
+                f = 2.0 * T * G * N * K
+                res[name][f"T{T}"] = {"us": round(us, 2), "TFLOPs": round(f / us / 1e6, 1),
+                                      "mfma_frac": round(f / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        del qs, ss
+    torch.cuda.empty_cache()
+    return res
+
+
 ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096", "stack43_t1"]
 
 
@@ -865,6 +919,9 @@ def main():
         "gen_seconds": round(t_gen, 1),
         "workloads": {n: r for n, r in recs.items() if n != main_name},
     }
+    if args.workload == "all" or args.linears:
+        print("[bench] w8a16 linears", file=sys.stderr, flush=True)
+        rec["w8a16_linears"] = run_linears()
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:

@@ -189,6 +189,28 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The model's other int8 linear layers ("w8a16": int8, symmetric, one fp32
+ * scale per output channel, 16-bit activations; page "deepseek-v4-mxfp4-int8
+ * config.json", quantization_config, config group linears_w8a16, targets
+ * attn.fused_wqa_wkv, attn.wq_b, attn.wo_a, attn.wo_b, attn.indexer.wq_b,
+ * attn.indexer.compressor.wkv), on the same kernels as the shared expert's
+ * w2: y = x W^T with W[n][k] = scale[n] * q[n][k].
+ *   groups > 1: a grouped (block-diagonal) projection such as wo_a
+ *   (o_groups): group g maps input features [g K, (g+1) K) to output
+ *   features [g N, (g+1) N) with its own rows q[g N .. g N + N) and scales.
+ *   x     [T][groups K] bf16
+ *   q     [groups N][K] int8;  scale [groups N] f32
+ *   out   [T][groups N] bf16 (out_is_fp32 = 0) or f32
+ *   workspace: moe_linear_workspace_size(T, K, N, groups) bytes, 256-byte
+ *   aligned, zero-filled before its first use (its counters are left at zero
+ *   by every call); calls sharing one must be ordered on one stream.
+ * Supported: K a multiple of 128, N of 256 (each at most 65536), groups at
+ * most 64, 0 <= T <= 65536. Errors as for moe_forward. */
+size_t moe_linear_workspace_size(int32_t T, int32_t K, int32_t N, int32_t groups);
+int moe_linear_w8a16(int32_t T, int32_t K, int32_t N, int32_t groups, const uint16_t* x, const int8_t* q,
+                     const float* scale, void* out, int32_t out_is_fp32, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* One MoE layer's parameters for moe_forward_stack (device pointers, layouts
  * as for moe_forward). tid2eid != NULL makes it a hash layer (V rows); then
  * bias and logit_offset are ignored. */

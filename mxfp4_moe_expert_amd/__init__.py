@@ -78,6 +78,8 @@ _SIGNATURES = {
     "moe_get_option": ([_I32], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
     "moe_noalloc_max_bytes": ([], _SZ),
+    "moe_linear_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
+    "moe_linear_w8a16": ([_I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _SZ, _VP], ctypes.c_int),
     "moe_forward_stack": ([_CFGP, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _SZ, _VP], ctypes.c_int),
     "moe_forward_noalloc": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                              _VP, _VP, _VP, _I32, _VP, _VP, _VP], ctypes.c_int),
@@ -423,4 +425,36 @@ def forward_stack(cfg: MoeConfig, x, layers, token_ids=None, out_fp32=False, ws=
     buf, nb = _ws(cfg, T, dev, ws)
     _check(lib().moe_forward_stack(ctypes.byref(cfg), n, weights, T, _ptr(x), _ptr(token_ids), _ptr(act),
                                    _ptr(out), int(out_fp32), _ptr(buf), nb, _stream(dev)), "moe_forward_stack")
+    return out
+
+
+_linear_ws: dict = {}
+
+
+def linear_w8a16(x, q, scale, groups=1, out_fp32=False, out=None, ws=None):
+    """int8 per-channel linear (moe_linear_w8a16): x [T][groups*K] bf16, q
+    [groups*N][K] int8, scale [groups*N] f32 -> [T][groups*N] (bf16 or f32)."""
+    T = x.shape[0]
+    dev = x.device
+    _need(x, _BF16, None, "x")
+    _need(q, torch.int8, None, "q")
+    _need(scale, torch.float32, None, "scale")
+    if x.dim() != 2 or q.dim() != 2 or x.shape[1] % groups or q.shape[0] % groups:
+        raise ValueError("x [T][groups*K], q [groups*N][K] expected")
+    K, N = x.shape[1] // groups, q.shape[0] // groups
+    if q.shape[1] != K or scale.shape != (groups * N,):
+        raise ValueError("shapes of q / scale do not match x")
+    need = lib().moe_linear_workspace_size(T, K, N, groups)
+    if need == 0:
+        raise MoEError(MOE_EUNSUPPORTED, "moe_linear_workspace_size")
+    if ws is None:
+        key = torch.device(dev).index or 0
+        ws = _linear_ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
+            _linear_ws[key] = ws
+    if out is None:
+        out = torch.empty(T, groups * N, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=dev)
+    _check(lib().moe_linear_w8a16(T, K, N, groups, _ptr(x), _ptr(q), _ptr(scale), _ptr(out), int(out_fp32),
+                                  _ptr(ws), ws.numel(), _stream(dev)), "moe_linear_w8a16")
     return out

@@ -730,6 +730,85 @@ int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_w
   return MOE_OK;
 }
 
+size_t moe_linear_workspace_size(int32_t T, int32_t K, int32_t N, int32_t groups) {
+  if (T < 0 || T > kMaxT || K <= 0 || N <= 0 || groups <= 0 || K % 128 || N % 256 || K > 65536 || N > 65536 ||
+      groups > 64)
+    return 0;
+  // counters (the GEMM's tile queue, the streaming pass's unit counter), then the streaming pass's
+  // fp32 outputs
+  return 256 + align256((size_t)(T <= kSmallT ? T : 0) * groups * N * 4);
+}
+
+int moe_linear_w8a16(int32_t T, int32_t K, int32_t N, int32_t groups, const uint16_t* x, const int8_t* q,
+                     const float* scale, void* out, int32_t out_is_fp32, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (T < 0 || K <= 0 || N <= 0 || groups <= 0) return MOE_EINVAL;
+  const size_t need = moe_linear_workspace_size(T, K, N, groups);
+  if (need == 0) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !q || !scale || !out || !workspace) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return MOE_EINVAL;
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  const int ldx = groups * K, ldo = groups * N;
+  if (T > kSmallT) {  // grouped-GEMM kernel of the shared expert's w2, with no routed slots to add
+    for (int g = 0; g < groups; ++g) {
+      GemmArgs a;
+      memset(&a, 0, sizeof(a));
+      a.T = T;
+      a.fmt = 1;
+      a.mode = kGemmW2Combine;
+      a.wq = reinterpret_cast<const uint8_t*>(q + (size_t)g * N * K);
+      a.row_scale = scale + (size_t)g * N;
+      a.K = K;
+      a.routed = 0;
+      a.n_ntiles = N / 256;
+      a.act = x + (size_t)g * K;
+      a.act_ld = ldx;
+      a.topk = 0;
+      a.out = out_is_fp32 ? static_cast<void*>(static_cast<float*>(out) + (size_t)g * N)
+                          : static_cast<void*>(static_cast<uint16_t*>(out) + (size_t)g * N);
+      a.out_ld = ldo;
+      a.out_is_fp32 = out_is_fp32 ? 1 : 0;
+      a.queue = counters;
+      const int rc = status(launch_gemm(a, (T + kGemmTokens - 1) / kGemmTokens, st));
+      if (rc) return rc;
+    }
+    return MOE_OK;
+  }
+  // batched decode: the streaming int8 pass (fp32 rows), then one cast of all groups' outputs
+  float* y = at<float>(workspace, 256);
+  for (int g = 0; g < groups; ++g) {
+    SkinnyArgs b;
+    memset(&b, 0, sizeof(b));
+    b.T = T;
+    b.routed = 0;
+    b.flags = device_flags();
+    b.wq = reinterpret_cast<const uint8_t*>(q + (size_t)g * N * K);
+    b.row_scale = scale + (size_t)g * N;
+    b.K = K;
+    b.half = 0;
+    b.rows = N;
+    b.n_rowblocks = N / 256;
+    b.tile_n = shared_stream_tile(T, K);
+    b.n_tiles_grid = (T + b.tile_n - 1) / b.tile_n;
+    b.act = x + (size_t)g * K;
+    b.act_ld = ldx;
+    b.yout = y + (size_t)g * N;
+    b.yout_ld = ldo;
+    SkinnyArgs none;
+    memset(&none, 0, sizeof(none));
+    int rc = status(launch_fill_zero(counters + kQueueInts, 4, st));  // the pass's unit counter
+    if (rc) return rc;
+    rc = status(launch_stream(kW2, none, 0, &b, b.n_tiles_grid * b.n_rowblocks, counters + kQueueInts, st));
+    if (rc) return rc;
+  }
+  CombineArgs cb{T, ldo, 0, nullptr, y, out, out_is_fp32 ? 1 : 0, 0};
+  return status(launch_combine(cb, st));
+}
+
 int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash) {
   if (!cfg) return MOE_EINVAL;
   if (!cfg_ok(cfg) || T > kMaxT) return MOE_EUNSUPPORTED;
