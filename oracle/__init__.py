@@ -83,8 +83,18 @@ def _open(path: str):
     L.or_forward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                              vp, vp, vp, vp, dbl, dbl, i32, vp, i32, vp, vp, vp, vp, vp, vp]
     L.or_linear_w8a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.or_fp16_value.argtypes = [ctypes.c_uint16]
+    L.or_fp16_value.restype = dbl
+    L.or_q3_code.argtypes = [vp, i32]
+    L.or_q3_code.restype = i32
+    L.or_q3_level.argtypes = [vp, i32]
+    L.or_q3_level.restype = dbl
+    L.or_q3_weight.argtypes = [vp, vp, vp, i64, i64, i64]
+    L.or_q3_weight.restype = dbl
+    L.or_forward_w2q3.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, dbl, dbl, i32, vp, i32, vp, vp, vp, vp, vp, vp]
     for f in ("or_route", "or_hash_route", "or_permute", "or_expert_ffn", "or_shared_ffn",
-              "or_forward", "or_linear_w8a16"):
+              "or_forward", "or_forward_w2q3", "or_linear_w8a16"):
         getattr(L, f).restype = i32
     return L
 
@@ -253,6 +263,67 @@ def forward(layer, x, token_ids=None, rows=None, force_ids=None, round_h=True):
         _p(layer.sh_w13), _p(layer.sh_w13_scale), _p(layer.sh_w2), _p(layer.sh_w2_scale),
         wl.routed_scaling_factor, wl.swiglu_limit, int(round_h), _p(rows_a), n,
         _p(_c(force_ids, np.int32)), _p(ids), _p(w), _p(gap), _p(nxt), _p(out)), "forward")
+    return dict(ids=ids, w=w, gap=gap, next=nxt, out=out)
+
+
+def fp16_value(bits: int) -> float:
+    return lib().or_fp16_value(bits)
+
+
+def q3_code(block: np.ndarray, i: int) -> int:
+    """3-bit code of weight i of one 12-byte block."""
+    b = _c(block, np.uint8)
+    assert b.size == 12
+    return lib().or_q3_code(_p(b), i)
+
+
+def q3_decode(codes: np.ndarray, scales: np.ndarray, levels=None) -> np.ndarray:
+    """Decode a whole 3-bit matrix [N, K] (fp64), one weight at a time:
+    codes [N, K/32*12] u8, scales [N, K/32] binary16 bits, levels [8] or None."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    lv = _c(levels, np.float32)
+    N, K = scales.shape[0], scales.shape[1] * 32
+    assert codes.shape == (N, K // 32 * 12)
+    out = np.empty((N, K), np.float64)
+    f = lib().or_q3_weight
+    pc, ps, pl = _p(codes), _p(scales), _p(lv)
+    for n in range(N):
+        for k in range(K):
+            out[n, k] = f(pc, ps, pl, K, n, k)
+    return out
+
+
+def forward_w2q3(layer, w2_codes, w2_scales, w2_levels, x, token_ids=None, rows=None, force_ids=None,
+                 round_h=True):
+    """``forward`` with the routed experts' w2 in 3-bit blocks: w2_codes
+    [E, H, I/32*12] u8, w2_scales [E, H, I/32] binary16 bits, w2_levels
+    [E, 8] fp32 or None (uniform). ``layer``'s own w2 is not used."""
+    wl = layer.wl
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    E, k, I = wl.E, wl.k, wl.I
+    c2 = _c(w2_codes, np.uint8)
+    s2 = _c(w2_scales, np.uint16)
+    lv = _c(w2_levels, np.float32)
+    assert c2.size == E * H * (I // 32) * 12 and s2.size == E * H * (I // 32)
+    assert lv is None or lv.size == E * 8
+    rows_a = None if rows is None else _c(rows, np.int32)
+    n = T if rows_a is None else len(rows_a)
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    gap = np.empty(n, np.float64)
+    nxt = np.empty(n, np.int32)
+    out = np.empty((n, H), np.float64)
+    tids = _c(token_ids, np.int32)
+    t2e = _c(layer.tid2eid, np.int32) if tids is not None else None
+    V = t2e.shape[0] if t2e is not None else 0
+    _check(lib().or_forward_w2q3(
+        T, H, E, k, I, _p(x), _p(layer.gate_w), _p(layer.bias), _p(layer.logit_offset), _p(tids), _p(t2e), V,
+        _p(layer.w13_codes), _p(layer.w13_scales), _p(c2), _p(s2), _p(lv),
+        _p(layer.sh_w13), _p(layer.sh_w13_scale), _p(layer.sh_w2), _p(layer.sh_w2_scale),
+        wl.routed_scaling_factor, wl.swiglu_limit, int(round_h), _p(rows_a), n,
+        _p(_c(force_ids, np.int32)), _p(ids), _p(w), _p(gap), _p(nxt), _p(out)), "forward_w2q3")
     return dict(ids=ids, w=w, gap=gap, next=nxt, out=out)
 
 

@@ -45,6 +45,17 @@
  * weights only; the intermediate activation h entering w2 is bf16 (the a16
  * format of the expert linears) unless round_h is 0; the hash layers weight
  * the 6 table experts by their renormalised sqrt-softplus scores, no bias.
+ *
+ * Down experts in 3-bit blocks (or_forward_w2q3): page
+ * "Geometric-AI/DeepSeek-V4-Flash-0731-ROCmFP3-MIX", introduction and section
+ * "What 'adaptive' means here", gives 14 bytes per 32 weights for both its
+ * formats, one code book for every block (uniform) or a small table per
+ * expert (adaptive), and nothing finer. Readings: 12 bytes of 3-bit codes and
+ * a 2-byte IEEE binary16 scale d per 32 consecutive weights along the input
+ * dimension; weight = d * level[code]; the uniform code book is level[c] =
+ * c - 4 (a scale-only block, like the "_0" formats the name recalls); an
+ * adaptive table is 8 fp32 levels per expert; the code bits sit where
+ * or_q3_code reads them (a layout of this library's own).
  */
 #include <math.h>
 #include <omp.h>
@@ -102,6 +113,45 @@ double or_round_bf16(double v) {
  * `scale_bits` bits. */
 int64_t or_block_bytes(int bits, int group, int scale_bits) {
   return ((int64_t)bits * group + scale_bits) / 8;
+}
+
+/* IEEE 754 binary16: bit 15 sign, bits 14..10 exponent (bias 15), bits 9..0
+ * fraction; exponent 0 is subnormal (fraction * 2^-24), 31 is Inf/NaN. */
+double or_fp16_value(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
+  double mag;
+  if (e == 31) mag = f ? NAN : INFINITY;
+  else if (e == 0) mag = ldexp((double)f, -24);
+  else mag = ldexp(1.0 + f / 1024.0, e - 15);
+  return s ? -mag : mag;
+}
+
+/* The 3-bit code of weight i (0..31) of a 12-byte block b. Weights
+ * 0..23 have all three bits in one byte: weight i in byte 4*(i/8) + i%4,
+ * bits 0..2 if i%8 < 4, else bits 3..5. Weights 24..31 use the two top bits
+ * of three bytes: weight 24 + j has bits 0..1 in bits 6..7 of byte j and
+ * bit 2 in bit 6 of byte 8 + j; weight 28 + j has bits 0..1 in bits 6..7 of
+ * byte 4 + j and bit 2 in bit 7 of byte 8 + j. */
+int or_q3_code(const uint8_t* b, int i) {
+  if (i < 24) {
+    int byte = 4 * (i / 8) + i % 4;
+    int shift = (i % 8 < 4) ? 0 : 3;
+    return (b[byte] >> shift) & 7;
+  }
+  int j = (i - 24) % 4;
+  if (i < 28) return ((b[j] >> 6) & 3) | (((b[8 + j] >> 6) & 1) << 2);
+  return ((b[4 + j] >> 6) & 3) | (((b[8 + j] >> 7) & 1) << 2);
+}
+
+/* Level of code c: the expert's table, or c - 4 for the uniform code book. */
+double or_q3_level(const float* levels, int c) { return levels ? (double)levels[c] : (double)(c - 4); }
+
+/* Weight (n, k) of a 3-bit matrix with K inputs: codes [N][K/32][12],
+ * scales [N][K/32] binary16 bits, levels [8] or NULL (uniform). */
+double or_q3_weight(const uint8_t* codes, const uint16_t* scales, const float* levels, int64_t K, int64_t n,
+                    int64_t k) {
+  const uint8_t* blk = codes + (n * (K / 32) + k / 32) * 12;
+  return or_fp16_value(scales[n * (K / 32) + k / 32]) * or_q3_level(levels, or_q3_code(blk, (int)(k % 32)));
 }
 
 /* ---- elementwise pieces -------------------------------------------------- */
@@ -248,8 +298,8 @@ int or_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets, int32_
  * The inner loops run over whole 32-weight groups so that the group's
  * exponent is decoded once per group. */
 static void routed_expert(int H, int I, const double* xd, const uint8_t* c13, const uint8_t* s13,
-                          const uint8_t* c2, const uint8_t* s2, double limit, int round_h,
-                          double* hbuf, double* y) {
+                          const uint8_t* c2, const uint8_t* s2, const uint16_t* s2q3, int w2q3,
+                          const float* levels, double limit, int round_h, double* hbuf, double* y) {
 #pragma omp parallel for schedule(static)
   for (int i = 0; i < I; ++i) {
     double g = 0.0, u = 0.0;
@@ -267,6 +317,19 @@ static void routed_expert(int H, int I, const double* xd, const uint8_t* c13, co
     }
     double h = or_swiglu(g, u, limit);
     hbuf[i] = round_h ? or_round_bf16(h) : h;
+  }
+  if (w2q3) { /* down projection in 3-bit blocks: d * level[code] */
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < H; ++n) {
+      double acc = 0.0;
+      for (int i0 = 0; i0 < I; i0 += 32) {
+        double d = or_fp16_value(s2q3[(int64_t)n * (I / 32) + i0 / 32]);
+        const uint8_t* blk = c2 + ((int64_t)n * (I / 32) + i0 / 32) * 12;
+        for (int i = i0; i < i0 + 32; ++i) acc += d * or_q3_level(levels, or_q3_code(blk, i - i0)) * hbuf[i];
+      }
+      y[n] = acc;
+    }
+    return;
   }
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < H; ++n) {
@@ -314,6 +377,10 @@ typedef struct {
   const uint8_t *w13c, *w13s, *w2c, *w2s;
   double limit;
   int round_h;
+  /* w2 in 3-bit blocks: w2c [E][H][I/32][12], w2s16 [E][H][I/32], w2lv [E][8] or NULL */
+  int w2q3;
+  const uint16_t* w2s16;
+  const float* w2lv;
 } routed_args;
 
 /* out[n] = sum_j w_j * y_j[n] for one token, slots in order j = 0..k-1. */
@@ -330,9 +397,14 @@ static int routed_token(const routed_args* a, const double* xd, const int32_t* i
   for (int n = 0; n < H; ++n) out[n] = 0.0;
   for (int j = 0; j < a->k; ++j) {
     int e = ids[j];
-    routed_expert(H, I, xd, a->w13c + (int64_t)e * 2 * I * (H / 2), a->w13s + (int64_t)e * 2 * I * (H / 32),
-                  a->w2c + (int64_t)e * H * (I / 2), a->w2s + (int64_t)e * H * (I / 32), a->limit,
-                  a->round_h, hbuf, y);
+    if (a->w2q3)
+      routed_expert(H, I, xd, a->w13c + (int64_t)e * 2 * I * (H / 2), a->w13s + (int64_t)e * 2 * I * (H / 32),
+                    a->w2c + (int64_t)e * H * (I / 32) * 12, NULL, a->w2s16 + (int64_t)e * H * (I / 32), 1,
+                    a->w2lv ? a->w2lv + (int64_t)e * 8 : NULL, a->limit, a->round_h, hbuf, y);
+    else
+      routed_expert(H, I, xd, a->w13c + (int64_t)e * 2 * I * (H / 2), a->w13s + (int64_t)e * 2 * I * (H / 32),
+                    a->w2c + (int64_t)e * H * (I / 2), a->w2s + (int64_t)e * H * (I / 32), NULL, 0, NULL,
+                    a->limit, a->round_h, hbuf, y);
     for (int n = 0; n < H; ++n) out[n] += w[j] * y[n];
   }
   free(hbuf);
@@ -351,7 +423,7 @@ int or_expert_ffn(int T, int H, int E, int k, int I, const uint16_t* x, const in
   if (T < 0 || H <= 0 || H % 32 || I <= 0 || I % 32 || E <= 0 || k <= 0) return OR_EINVAL;
   for (int64_t i = 0; i < (int64_t)T * k; ++i)
     if (ids[i] < 0 || ids[i] >= E) return OR_EINVAL;
-  routed_args a = {H, E, k, I, w13c, w13s, w2c, w2s, limit, round_h};
+  routed_args a = {H, E, k, I, w13c, w13s, w2c, w2s, limit, round_h, 0, NULL, NULL};
   double* xd = (double*)malloc(sizeof(double) * (size_t)H);
   if (!xd) return OR_EINVAL;
   int rc = OR_OK;
@@ -391,12 +463,13 @@ int or_shared_ffn(int T, int H, int I, const uint16_t* x, const int8_t* q13, con
  * (weights are still the renormalised scores of those experts).
  * Per-row outputs: ids [n_rows][k], w [n_rows][k], gap [n_rows] (learned
  * router only; +inf for hash), next [n_rows], out [n_rows][H]. */
-int or_forward(int T, int H, int E, int k, int I, const uint16_t* x, const float* gate_w,
-               const float* bias, const float* offset, const int32_t* tids, const int32_t* tid2eid,
-               int V, const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
-               const int8_t* q13, const float* s13, const int8_t* q2, const float* s2, double scale,
-               double limit, int round_h, const int32_t* rows, int n_rows, const int32_t* force_ids,
-               int32_t* ids, double* w, double* gap, int32_t* next, double* out) {
+static int forward_impl(const routed_args* ra, int T, const uint16_t* x, const float* gate_w,
+                        const float* bias, const float* offset, const int32_t* tids, const int32_t* tid2eid,
+                        int V, const int8_t* q13, const float* s13, const int8_t* q2, const float* s2,
+                        double scale, const int32_t* rows, int n_rows, const int32_t* force_ids, int32_t* ids,
+                        double* w, double* gap, int32_t* next, double* out) {
+  const int H = ra->H, E = ra->E, k = ra->k, I = ra->I, round_h = ra->round_h;
+  const double limit = ra->limit;
   if (T < 0 || H <= 0 || H % 32 || I <= 0 || I % 32 || E <= 0 || E > 4096 || k <= 0 || k > E ||
       k > 64)
     return OR_EINVAL;
@@ -406,7 +479,7 @@ int or_forward(int T, int H, int E, int k, int I, const uint16_t* x, const float
     if (t < 0 || t >= T) return OR_EINVAL;
     if (tids && (tids[t] < 0 || tids[t] >= V)) return OR_EINVAL;
   }
-  routed_args a = {H, E, k, I, w13c, w13s, w2c, w2s, limit, round_h};
+  const routed_args a = *ra;
   double* xd = (double*)malloc(sizeof(double) * (size_t)H);
   double* z = (double*)malloc(sizeof(double) * (size_t)H);
   double* hbuf = (double*)malloc(sizeof(double) * (size_t)I);
@@ -443,6 +516,32 @@ int or_forward(int T, int H, int E, int k, int I, const uint16_t* x, const float
   free(z);
   free(hbuf);
   return rc;
+}
+
+int or_forward(int T, int H, int E, int k, int I, const uint16_t* x, const float* gate_w,
+               const float* bias, const float* offset, const int32_t* tids, const int32_t* tid2eid,
+               int V, const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+               const int8_t* q13, const float* s13, const int8_t* q2, const float* s2, double scale,
+               double limit, int round_h, const int32_t* rows, int n_rows, const int32_t* force_ids,
+               int32_t* ids, double* w, double* gap, int32_t* next, double* out) {
+  routed_args a = {H, E, k, I, w13c, w13s, w2c, w2s, limit, round_h, 0, NULL, NULL};
+  return forward_impl(&a, T, x, gate_w, bias, offset, tids, tid2eid, V, q13, s13, q2, s2, scale, rows, n_rows,
+                      force_ids, ids, w, gap, next, out);
+}
+
+/* or_forward with the routed experts' down projection (w2) in 3-bit blocks:
+ * w2c [E][H][I/32][12] codes, w2s [E][H][I/32] binary16 scales, w2_levels
+ * [E][8] fp32 (one table per expert) or NULL for the uniform code book. */
+int or_forward_w2q3(int T, int H, int E, int k, int I, const uint16_t* x, const float* gate_w,
+                    const float* bias, const float* offset, const int32_t* tids, const int32_t* tid2eid,
+                    int V, const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint16_t* w2s,
+                    const float* w2_levels, const int8_t* q13, const float* s13, const int8_t* q2,
+                    const float* s2, double scale, double limit, int round_h, const int32_t* rows, int n_rows,
+                    const int32_t* force_ids, int32_t* ids, double* w, double* gap, int32_t* next,
+                    double* out) {
+  routed_args a = {H, E, k, I, w13c, w13s, w2c, NULL, limit, round_h, 1, w2s, w2_levels};
+  return forward_impl(&a, T, x, gate_w, bias, offset, tids, tid2eid, V, q13, s13, q2, s2, scale, rows, n_rows,
+                      force_ids, ids, w, gap, next, out);
 }
 
 /* ---- int8 per-channel linear layers ("w8a16") --------------------------- */

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # Counter streams: one per tensor kind, so each tensor is regenerable alone.
 S_W13, S_W2, S_SH_W13, S_SH_W2, S_GATE, S_BIAS, S_OFFSET, S_TOKENS, S_TIDS, S_TID2EID = range(1, 11)
-S_STACK_PERM = 11  # per-layer expert order of a layer stack
+S_STACK_PERM = 11
+S_W2Q3, S_Q3TAB = 12, 13  # routed w2 in 3-bit blocks, their per-expert tables  # per-layer expert order of a layer stack
 
 _lib = None
 
@@ -62,6 +63,9 @@ def lib():
         L.synth_mxfp4_normal.argtypes = [u64, u64, u64, dbl, i64, i64, vp, vp]
         L.synth_quant_int8.argtypes = [vp, i64, i64, vp, vp]
         L.synth_int8_normal.argtypes = [u64, u64, u64, dbl, i64, i64, vp, vp]
+        L.synth_quant_q3.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        L.synth_q3_normal.argtypes = [u64, u64, u64, dbl, i64, i64, vp, i64, vp, vp]
+        L.synth_q3_tables.argtypes = [u64, u64, u64, i64, vp]
         L.synth_zipf_ids.argtypes = [u64, u64, u64, dbl, i64, i64, vp]
         L.synth_zipf_ids.restype = ctypes.c_int
         L.synth_tid2eid.argtypes = [u64, u64, u64, i64, i32, i32, vp]
@@ -131,6 +135,47 @@ def int8_normal(seed, stream, sub, rows, K, sigma):
     s = np.empty(rows, np.float32)
     lib().synth_int8_normal(seed, stream, sub, sigma, rows, K, _p(q), _p(s))
     return q, s
+
+
+def _q3_tables_arg(tables, rows, rows_per_table):
+    if tables is None:
+        return None, 1
+    tables = np.ascontiguousarray(tables, np.float32).reshape(-1, 8)
+    if rows_per_table is None:
+        rows_per_table = rows // tables.shape[0]
+    if rows_per_table <= 0 or (rows - 1) // rows_per_table >= tables.shape[0]:
+        raise ValueError("tables do not cover the rows")
+    return tables, rows_per_table
+
+
+def quant_q3(w: np.ndarray, tables=None, rows_per_table=None):
+    """Encode fp32 ``w`` [rows, K] as 3-bit blocks: (codes uint8 [rows, K/32*12],
+    scales uint16 [rows, K/32] binary16 bits). ``tables`` [n, 8] (row r uses
+    table r // rows_per_table) or None for the uniform code book c - 4."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, K = w.shape
+    assert K % 32 == 0
+    t, rpt = _q3_tables_arg(tables, rows, rows_per_table)
+    codes = np.empty((rows, K // 32 * 12), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint16)
+    lib().synth_quant_q3(_p(w), rows, K, None if t is None else _p(t), rpt, _p(codes), _p(scales))
+    return codes, scales
+
+
+def q3_normal(seed, stream, sub, rows, K, sigma, tables=None, rows_per_table=None):
+    t, rpt = _q3_tables_arg(tables, rows, rows_per_table)
+    codes = np.empty((rows, K // 32 * 12), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint16)
+    lib().synth_q3_normal(seed, stream, sub, sigma, rows, K, None if t is None else _p(t), rpt, _p(codes),
+                          _p(scales))
+    return codes, scales
+
+
+def q3_tables(seed, stream, sub, n) -> np.ndarray:
+    """n code books of 8 ascending fp32 levels."""
+    out = np.empty((n, 8), np.float32)
+    lib().synth_q3_tables(seed, stream, sub, n, _p(out))
+    return out
 
 
 def zipf_ids(seed, stream, sub, n, V, s=1.1) -> np.ndarray:
@@ -226,6 +271,22 @@ def make_layer(wl: Workload) -> Layer:
     off = normal_f32(s, S_OFFSET, 0, E, wl.offset_sigma) if wl.offset_sigma > 0 else None
     t2e = tid2eid(s, S_TID2EID, 0, wl.V, E, k) if wl.hash_layer else None
     return Layer(wl, gate, bias, off, w13c, w13s, w2c, w2s, sh13, sh13s, sh2, sh2s, t2e)
+
+
+def make_w2q3(wl: Workload, tables: bool):
+    """The routed experts' w2 in 3-bit blocks, N(0, weight_sigma^2) like the
+    MXFP4 w2: (codes uint8 [E, H, I/32*12], scales uint16 [E, H, I/32]
+    binary16 bits, levels fp32 [E, 8] or None for the uniform code book).
+    Expert e is sub-sequence e; tables from stream S_Q3TAB."""
+    E, H, I = wl.E, wl.H, wl.I
+    lv = q3_tables(wl.seed, S_Q3TAB, 0, E) if tables else None
+    codes = np.empty((E, H, I // 32 * 12), np.uint8)
+    scales = np.empty((E, H, I // 32), np.uint16)
+    L = lib()
+    for e in range(E):
+        L.synth_q3_normal(wl.seed, S_W2Q3, e, wl.weight_sigma, H, I, None if lv is None else _p(lv[e]), H,
+                          _p(codes[e]), _p(scales[e]))
+    return codes, scales, lv
 
 
 def make_tokens(wl: Workload, rep: int = 0, T: int | None = None) -> np.ndarray:

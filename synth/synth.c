@@ -24,6 +24,18 @@
  *  - int8: symmetric, one fp32 scale per output row, s = max|w| / 127,
  *    q = round-half-even(w / s) in [-127, 127]; all-zero rows get s = 1.
  *  - bf16: round to nearest even from fp32.
+ *  - 3-bit blocks (14 bytes per 32 weights; the byte count is the one page
+ *    "Geometric-AI/DeepSeek-V4-Flash-0731-ROCmFP3-MIX" gives for its
+ *    uniform and adaptive down-expert formats; the bit layout is this
+ *    library's own): per 32 consecutive weights along K, an IEEE binary16
+ *    scale d = max|w| / max|level| (rounded to nearest even) and 3-bit codes
+ *    c = the level nearest w / d (ties to the lower code), packed in 12
+ *    bytes b[0..11]: byte j + 4q (j < 4, q < 3) holds the code of weight
+ *    8q + j in bits 0..2 and of weight 8q + 4 + j in bits 3..5; weight 24 + j
+ *    takes bits 6..7 of byte j as its code bits 0..1 and bit 6 of byte 8 + j
+ *    as its bit 2; weight 28 + j takes bits 6..7 of byte 4 + j and bit 7 of
+ *    byte 8 + j. Levels: 8 per table; no table means c - 4 (the uniform
+ *    code book).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -217,6 +229,131 @@ void synth_mxfp4_normal(uint64_t seed, uint64_t stream, uint64_t sub, double sig
       encode_mxfp4_row(buf, K, codes + r * (K / 2), scales + r * (K / 32));
     }
     free(buf);
+  }
+}
+
+/* ---- 3-bit block encoder (input preparation only) ----------------------- */
+
+/* fp32 -> IEEE binary16 bits, round to nearest even, saturating at 65504
+ * (finite inputs only). */
+static uint16_t f32_to_f16_rne(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (a >= 65504.0) return (uint16_t)(sign | 0x7BFF);
+  int e;
+  frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+  int E = e - 1; /* a in [2^E, 2^(E+1)) */
+  if (E < -14) { /* subnormal: multiples of 2^-24 */
+    double q = nearbyint(ldexp(a, 24));
+    if (q >= 1024.0) return (uint16_t)(sign | 0x0400);
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  double q = nearbyint(ldexp(a, 10 - E)); /* 1024 .. 2048 */
+  if (q >= 2048.0) {
+    q = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return (uint16_t)(sign | 0x7BFF);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)q - 1024));
+}
+
+static double f16_bits_to_double(uint16_t h) {
+  int s = h >> 15, E = (h >> 10) & 31, m = h & 1023;
+  double v = E == 0 ? ldexp((double)m, -24) : ldexp(1024.0 + m, E - 25);
+  return s ? -v : v;
+}
+
+static const float kQ3Uniform[8] = {-4.f, -3.f, -2.f, -1.f, 0.f, 1.f, 2.f, 3.f};
+
+static void q3_put_code(uint8_t* b, int i, int c) {
+  int j = i & 3;
+  if (i < 24) {
+    int q = i >> 3, hi = (i >> 2) & 1;
+    b[4 * q + j] |= (uint8_t)(c << (hi ? 3 : 0));
+  } else if (i < 28) {
+    b[j] |= (uint8_t)((c & 3) << 6);
+    b[8 + j] |= (uint8_t)(((c >> 2) & 1) << 6);
+  } else {
+    b[4 + j] |= (uint8_t)((c & 3) << 6);
+    b[8 + j] |= (uint8_t)(((c >> 2) & 1) << 7);
+  }
+}
+
+static void encode_q3_row(const float* w, int64_t K, const float* lv, uint8_t* codes, uint16_t* scales) {
+  double lmax = 0.0;
+  for (int c = 0; c < 8; ++c)
+    if (fabs((double)lv[c]) > lmax) lmax = fabs((double)lv[c]);
+  for (int64_t g = 0; g < K / 32; ++g) {
+    const float* wg = w + g * 32;
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j)
+      if (fabs((double)wg[j]) > amax) amax = fabs((double)wg[j]);
+    uint16_t dh = (amax > 0.0 && lmax > 0.0) ? f32_to_f16_rne(amax / lmax) : 0;
+    scales[g] = dh;
+    double d = f16_bits_to_double(dh);
+    uint8_t* b = codes + g * 12;
+    memset(b, 0, 12);
+    for (int i = 0; i < 32; ++i) {
+      int best = 0;
+      double be = INFINITY;
+      for (int c = 0; c < 8; ++c) {
+        double err = fabs((double)wg[i] - d * (double)lv[c]);
+        if (err < be) {
+          be = err;
+          best = c;
+        }
+      }
+      q3_put_code(b, i, best);
+    }
+  }
+}
+
+/* rows x K fp32 weights -> codes [rows][K/32 * 12], scales [rows][K/32]
+ * (binary16 bits). tables [n][8] levels, row r using table r / rows_per_table,
+ * or NULL for the uniform code book. */
+void synth_quant_q3(const float* w, int64_t rows, int64_t K, const float* tables, int64_t rows_per_table,
+                    uint8_t* codes, uint16_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    encode_q3_row(w + r * K, K, tables ? tables + (r / rows_per_table) * 8 : kQ3Uniform, codes + r * (K / 32) * 12,
+                  scales + r * (K / 32));
+}
+
+/* Gaussian rows N(0, sigma^2) (element (r, k) = number r*K + k of the
+ * sequence) encoded as 3-bit blocks. */
+void synth_q3_normal(uint64_t seed, uint64_t stream, uint64_t sub, double sigma, int64_t rows, int64_t K,
+                     const float* tables, int64_t rows_per_table, uint8_t* codes, uint16_t* scales) {
+  uint64_t key = seq_key(seed, stream, sub);
+#pragma omp parallel
+  {
+    float* buf = (float*)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      fill_normal(key, (uint64_t)(r * K), K, 0.0, sigma, buf);
+      encode_q3_row(buf, K, tables ? tables + (r / rows_per_table) * 8 : kQ3Uniform, codes + r * (K / 32) * 12,
+                    scales + r * (K / 32));
+    }
+    free(buf);
+  }
+}
+
+/* n per-expert code books of 8 ascending levels: the normal quantiles at
+ * (c + 1/2) / 8, each times (1 + 0.15 u) with u uniform in (-1, 1), sorted. */
+void synth_q3_tables(uint64_t seed, uint64_t stream, uint64_t sub, int64_t n, float* out) {
+  static const double base[8] = {-1.5341205443525463, -0.8871465590189700, -0.4887764111146695,
+                                 -0.1573106846101707, 0.1573106846101707,  0.4887764111146695,
+                                 0.8871465590189700,  1.5341205443525463};
+  uint64_t key = seq_key(seed, stream, sub);
+  for (int64_t e = 0; e < n; ++e) {
+    float* t = out + e * 8;
+    for (int c = 0; c < 8; ++c) t[c] = (float)(base[c] * (1.0 + 0.15 * (2.0 * ctr_unif(key, (uint64_t)(e * 8 + c)) - 1.0)));
+    for (int a = 1; a < 8; ++a)
+      for (int b = a; b > 0 && t[b - 1] > t[b]; --b) {
+        float x = t[b];
+        t[b] = t[b - 1];
+        t[b - 1] = x;
+      }
   }
 }
 

@@ -579,10 +579,179 @@ def check_linear_w8a16():
             assert np.array_equal(np.delete(got2, np.s_[N:2 * N], axis=1), np.delete(got, np.s_[N:2 * N], axis=1))
 
 
+# ------------------------------------------------------------------ 3-bit down experts
+
+def golden_fp16() -> list[tuple[int, float]]:
+    out = []
+    with open(os.path.join(GOLDEN, "fp16_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            b, v = line.split()
+            out.append((int(b, 16), float(v)))
+    return out
+
+
+def golden_q3_blocks() -> list[tuple[np.ndarray, list[int]]]:
+    out = []
+    with open(os.path.join(GOLDEN, "q3_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            left, right = line.split("|")
+            b = np.array([int(t, 16) for t in left.split()], np.uint8)
+            codes = [0] * 32
+            for item in right.split():
+                i, c = item.split("=")
+                codes[int(i)] = int(c)
+            out.append((b, codes))
+    return out
+
+
+def check_fp16_values():
+    """binary16 scales: the golden IEEE values, and every one of the 65536
+    patterns against numpy's float16."""
+    for bits, v in golden_fp16():
+        got = oracle.fp16_value(bits)
+        if math.isnan(v):
+            assert math.isnan(got), hex(bits)
+        else:
+            assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), (hex(bits), got, v)
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    lib = oracle.lib()
+    for b in range(0, 65536, 7):  # a spread of patterns; the golden list covers the special ones
+        got = lib.or_fp16_value(b)
+        want = allv[b]
+        assert (math.isnan(got) and math.isnan(want)) or got == want, (hex(b), got, want)
+
+
+def check_q3_codes():
+    """The code of every weight of the hand-worked golden blocks."""
+    blocks = golden_q3_blocks()
+    assert len(blocks) >= 8
+    for b, codes in blocks:
+        assert [oracle.q3_code(b, i) for i in range(32)] == codes, b
+
+
+def check_q3_values():
+    """Golden blocks decoded with a binary16 scale, uniform (c - 4) and with a
+    table of levels: value = scale x level[code]."""
+    lv = np.array([-1.5, -1.0, -0.5, -0.25, 0.25, 0.5, 1.0, 1.5], np.float32)
+    blocks = golden_q3_blocks()
+    codes = np.stack([b for b, _ in blocks])                       # [n, 12]: row r = block r
+    sc_bits = np.array([0x3800, 0xC000, 0x0001, 0x3555] * 4, np.uint16)[: len(blocks)]
+    scale = sc_bits.view(np.float16).astype(np.float64)
+    uni = oracle.q3_decode(codes, sc_bits[:, None])
+    tab = oracle.q3_decode(codes, sc_bits[:, None], lv)
+    for r, (_, c) in enumerate(blocks):
+        c = np.array(c)
+        assert np.array_equal(uni[r], scale[r] * (c - 4.0)), r
+        assert np.array_equal(tab[r], scale[r] * lv.astype(np.float64)[c]), r
+
+
+def check_q3_roundtrip():
+    """Weights encoded by the input generator (an encoder written separately)
+    decode to the level nearest each weight: |w - decoded| is the distance
+    to the nearest of scale x level, for the uniform book and for tables,
+    over several rows and blocks (the block and row of each scale)."""
+    rng = _rng(14)
+    K = 128
+    w = (rng.standard_normal((6, K)) * 0.02).astype(np.float32)
+    w[2, 40] = 0.5  # a block with an outlier
+    tabs = synth.q3_tables(3, 13, 0, 3)
+    for tables in (None, tabs):
+        codes, scales = synth.quant_q3(w, tables=tables, rows_per_table=2)
+        dec = oracle.q3_decode(codes, scales) if tables is None else np.concatenate(
+            [oracle.q3_decode(codes[2 * e:2 * e + 2], scales[2 * e:2 * e + 2], tables[e]) for e in range(3)])
+        d = np.repeat(scales.view(np.float16).astype(np.float64), 32, axis=1)
+        for r in range(6):
+            lv = np.arange(8.0) - 4 if tables is None else tables[r // 2].astype(np.float64)
+            cand = d[r][:, None] * lv[None, :]                        # [K, 8]
+            best = np.abs(w[r].astype(np.float64)[:, None] - cand).min(axis=1)
+            err = np.abs(w[r].astype(np.float64) - dec[r])
+            assert np.allclose(err, best, rtol=0, atol=1e-12), r
+        assert np.abs(dec - w).max() < 0.5 * np.abs(w).max()
+
+
+def _q3_equal_to_mxfp4(rng, E, H, I):
+    """w2 weights that both formats hold exactly: 2^x * (c - 4) with c in
+    0..7 and a -4 in every block (so both encoders take the scale 2^x)."""
+    c = rng.integers(0, 8, size=(E * H, I))
+    c[:, ::32] = 0
+    x = rng.integers(-9, -5, size=(E * H, I // 32))
+    w = (np.repeat(np.ldexp(1.0, x), 32, axis=1) * (c - 4.0)).astype(np.float32)
+    qc, qs = synth.quant_q3(w)
+    mc, ms = synth.quant_mxfp4(w)
+    return (qc.reshape(E, H, -1), qs.reshape(E, H, -1), mc.reshape(E, H, I // 2), ms.reshape(E, H, I // 32), w)
+
+
+def check_forward_w2q3_equals_mxfp4():
+    """With the uniform code book and power-of-two scales the 3-bit w2 holds
+    the same numbers as an MXFP4 w2; the two forwards must agree to the bit
+    (same experts, same sums in the same order), for learned and hash
+    routing, on a subset of rows."""
+    rng = _rng(15)
+    wl = synth.Workload("q3eq", T=12, H=64, E=8, k=3, I=64, V=30, seed=4)
+    L = synth.make_layer(wl)
+    qc, qs, mc, ms, w = _q3_equal_to_mxfp4(rng, wl.E, wl.H, wl.I)
+    assert np.array_equal(oracle.q3_decode(qc[1], qs[1]), w[wl.H:2 * wl.H].astype(np.float64))
+    Lm = synth.Layer(wl, L.gate_w, L.bias, L.logit_offset, L.w13_codes, L.w13_scales, mc, ms, L.sh_w13,
+                     L.sh_w13_scale, L.sh_w2, L.sh_w2_scale, synth.tid2eid(1, 9, 0, wl.V, wl.E, wl.k))
+    x = synth.make_tokens(wl, rep=2)
+    rows = np.array([5, 0, 11, 3], np.int32)
+    a = oracle.forward(Lm, x, rows=rows)
+    b = oracle.forward_w2q3(Lm, qc, qs, None, x, rows=rows)
+    assert len(set(a["ids"].ravel().tolist())) > 3
+    assert np.array_equal(a["ids"], b["ids"]) and np.array_equal(a["out"], b["out"])
+    tids = rng.integers(0, wl.V, size=wl.T).astype(np.int32)
+    a = oracle.forward(Lm, x, token_ids=tids, rows=rows)
+    b = oracle.forward_w2q3(Lm, qc, qs, None, x, token_ids=tids, rows=rows)
+    assert np.array_equal(a["out"], b["out"])
+
+
+def check_forward_w2q3_tables():
+    """Per-expert tables: the layer against numpy's composition with each
+    expert's w2 decoded in numpy from the encoder's inputs (the level nearest
+    w / scale in that expert's own table, times the binary16 scale)."""
+    rng = _rng(16)
+    wl = synth.Workload("q3tab", T=8, H=64, E=6, k=3, I=64, V=30, seed=5)
+    L = synth.make_layer(wl)
+    E, H, I = wl.E, wl.H, wl.I
+    tabs = synth.q3_tables(2, 13, 1, E)
+    w = (rng.standard_normal((E * H, I)) * 0.05).astype(np.float32)
+    qc, qs = synth.quant_q3(w, tables=tabs, rows_per_table=H)
+    d = np.repeat(qs.view(np.float16).astype(np.float64), 32, axis=1)
+    W2 = np.empty((E * H, I))
+    for r in range(E * H):
+        cand = d[r][:, None] * tabs[r // H].astype(np.float64)[None, :]
+        W2[r] = cand[np.arange(I), np.abs(w[r].astype(np.float64)[:, None] - cand).argmin(axis=1)]
+    W2 = W2.reshape(E, H, I)
+    x = synth.make_tokens(wl, rep=1)
+    rows = np.array([1, 6, 3], np.int32)
+    r = oracle.forward_w2q3(L, qc.reshape(E, H, -1), qs.reshape(E, H, -1), tabs, x, rows=rows, round_h=False)
+    xd = bf16_to_f64(x[rows])
+    S13 = L.sh_w13.astype(np.float64) * L.sh_w13_scale.astype(np.float64)[:, None]
+    S2 = L.sh_w2.astype(np.float64) * L.sh_w2_scale.astype(np.float64)[:, None]
+    for i in range(len(rows)):
+        out = np.zeros(H)
+        for j, e in enumerate(r["ids"][i]):
+            W13 = decode_mxfp4_table(L.w13_codes[e], L.w13_scales[e])
+            h = np_swiglu(W13[:I] @ xd[i], W13[I:] @ xd[i])
+            out += r["w"][i, j] * (W2[e] @ h)
+        out += np_swiglu(S13[:I] @ xd[i], S13[I:] @ xd[i]) @ S2.T
+        assert np.allclose(r["out"][i], out, rtol=1e-12, atol=1e-12 * np.abs(out).max()), i
+    # the forward's experts and weights are those of the MXFP4 layer
+    ref = oracle.forward(L, x, rows=rows, round_h=False)
+    assert np.array_equal(ref["ids"], r["ids"]) and np.array_equal(ref["w"], r["w"])
+
+
 ALL_CHECKS = [
     check_e2m1_codes, check_e8m0_bytes, check_mxfp4_layout, check_block_bytes, check_bf16_values,
     check_softplus_score, check_swiglu, check_topk_exhaustive, check_topk_random, check_fp32_decision,
     check_noaux_bias, check_weights_sum, check_hash_route, check_permute, check_expert_ffn,
     check_shared_ffn, check_linearity, check_special_case_dense, check_forward_tiny,
-    check_forward_forced_ids, check_forward_hash, check_linear_w8a16,
+    check_forward_forced_ids, check_forward_hash, check_linear_w8a16, check_fp16_values, check_q3_codes,
+    check_q3_values, check_q3_roundtrip, check_forward_w2q3_equals_mxfp4, check_forward_w2q3_tables,
 ]

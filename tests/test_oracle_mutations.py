@@ -84,6 +84,25 @@ MUTATIONS = [
      "const uint16_t* xt = x + (int64_t)t * groups * K;"),
     ("linear_weight_group", "const int8_t* row = q + ((int64_t)g * N + n) * K;",
      "const int8_t* row = q + (int64_t)n * K;"),
+    ("fp16_exponent_bias", "else mag = ldexp(1.0 + f / 1024.0, e - 15);",
+     "else mag = ldexp(1.0 + f / 1024.0, e - 16);"),
+    ("fp16_subnormal", "else if (e == 0) mag = ldexp((double)f, -24);",
+     "else if (e == 0) mag = ldexp((double)f, -25);"),
+    ("q3_code_half_shift", "int shift = (i % 8 < 4) ? 0 : 3;", "int shift = (i % 8 < 4) ? 3 : 0;"),
+    ("q3_code_byte", "int byte = 4 * (i / 8) + i % 4;", "int byte = 4 * (i / 8) + (i % 8) / 2;"),
+    ("q3_top_codes_swapped", "if (i < 28) return ((b[j] >> 6) & 3)",
+     "if (i >= 28) return ((b[j] >> 6) & 3)"),
+    ("q3_high_bit", "if (i < 28) return ((b[j] >> 6) & 3) | (((b[8 + j] >> 6) & 1) << 2);",
+     "if (i < 28) return ((b[j] >> 6) & 3) | (((b[8 + j] >> 7) & 1) << 2);"),
+    ("q3_uniform_offset", "return levels ? (double)levels[c] : (double)(c - 4);",
+     "return levels ? (double)levels[c] : (double)(c - 3);"),
+    ("q3_table_not_per_expert", "a->w2lv ? a->w2lv + (int64_t)e * 8 : NULL", "a->w2lv ? a->w2lv : NULL"),
+    ("q3_scale_of_block", "double d = or_fp16_value(s2q3[(int64_t)n * (I / 32) + i0 / 32]);",
+     "double d = or_fp16_value(s2q3[(int64_t)n * (I / 32) + (i0 / 32) / 2 * 2]);"),
+    ("q3_expert_stride", "a->w2c + (int64_t)e * H * (I / 32) * 12, NULL",
+     "a->w2c + (int64_t)e * H * (I / 2), NULL"),
+    ("q3_weight_row_stride", "const uint8_t* blk = codes + (n * (K / 32) + k / 32) * 12;",
+     "const uint8_t* blk = codes + (n * (K / 32) + k / 32) * 12 + (n > 0 ? 12 : 0);"),
     ("linear_scale_row", "out[((int64_t)t * groups + g) * N + n] = (double)s[(int64_t)g * N + n] * acc;",
      "out[((int64_t)t * groups + g) * N + n] = (double)s[n] * acc;"),
 ]
