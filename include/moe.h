@@ -189,6 +189,38 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
                 const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
                 float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward with the routed experts' down projection (w2) in 3-bit
+ * blocks: 14 bytes per 32 weights, one code book for every block (uniform)
+ * or a small table per expert (adaptive); page
+ * "Geometric-AI/DeepSeek-V4-Flash-0731-ROCmFP3-MIX", introduction and
+ * section "What 'adaptive' means here". The pages fix the byte count only;
+ * the field layout is this library's own:
+ *   w2_codes  [E][H][I/32][12] u8: per 32 consecutive weights along I, 12
+ *             bytes b[0..11] of 3-bit codes. Byte j + 4q (j < 4, q < 3)
+ *             holds the code of weight 8q + j in bits 0..2 and of weight
+ *             8q + 4 + j in bits 3..5; weight 24 + j has its code bits 0..1
+ *             in bits 6..7 of byte j and bit 2 in bit 6 of byte 8 + j;
+ *             weight 28 + j has bits 0..1 in bits 6..7 of byte 4 + j and bit
+ *             2 in bit 7 of byte 8 + j.
+ *   w2_scales [E][H][I/32] u16: IEEE binary16 scale d of each block.
+ *   w2_levels [E][8] f32: expert e's levels, or NULL for the uniform code
+ *             book level[c] = c - 4.
+ *   weight = d * level[code]. The kernels round each decoded weight to bf16
+ *   (nearest even) before the bf16 MFMA; every other argument is as in
+ *   moe_forward. Supported: T <= 64 with H and I multiples of 1024 (one
+ *   streaming launch for both stages), T > 64 with H a multiple of 256 (the
+ *   grouped GEMMs); else MOE_EUNSUPPORTED. w2_codes need 4-byte alignment
+ *   of each block (its 16-byte pointer alignment suffices), w2_levels
+ *   16-byte alignment. */
+int moe_forward_w2q3(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w,
+                     const float* bias, const float* logit_offset, const int32_t* token_ids,
+                     const int32_t* tid2eid, int32_t V, const uint8_t* w13_codes,
+                     const uint8_t* w13_scales, const uint8_t* w2_codes, const uint16_t* w2_scales,
+                     const float* w2_levels, const int8_t* sh_w13, const float* sh_w13_scale,
+                     const int8_t* sh_w2, const float* sh_w2_scale, void* out, int32_t out_is_fp32,
+                     int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* The model's other int8 linear layers ("w8a16": int8, symmetric, one fp32
  * scale per output channel, 16-bit activations; page "deepseek-v4-mxfp4-int8
  * config.json", quantization_config, config group linears_w8a16, targets

@@ -85,6 +85,8 @@ _SIGNATURES = {
                              _VP, _VP, _VP, _I32, _VP, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                      _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
+    "moe_forward_w2q3": ([_CFGP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                          _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
 }
 
 
@@ -362,6 +364,50 @@ def forward(cfg: MoeConfig, x, layer: DeviceLayer, token_ids=None, out_fp32=Fals
         _ptr(layer.w13_scales), _ptr(layer.w2_codes), _ptr(layer.w2_scales), _ptr(layer.sh_w13),
         _ptr(layer.sh_w13_scale), _ptr(layer.sh_w2), _ptr(layer.sh_w2_scale), _ptr(out), int(out_fp32),
         _ptr(ids), _ptr(w), _ptr(buf), nb, _stream(dev)), "moe_forward")
+    if return_routing:
+        return out, (ids, w)
+    return out
+
+
+def forward_w2q3(cfg: MoeConfig, x, layer: DeviceLayer, w2_codes, w2_scales, w2_levels=None, token_ids=None,
+                 out_fp32=False, return_routing=False, ws=None, out=None):
+    """``forward`` with the routed experts' w2 in 3-bit blocks (moe_forward_w2q3):
+    w2_codes uint8 [E, H, I/32*12], w2_scales int16/uint16 [E, H, I/32]
+    (binary16 bits), w2_levels fp32 [E, 8] or None (the uniform code book).
+    ``layer``'s own w2 tensors are not used."""
+    T, H, E, k, I = x.shape[0], cfg.hidden_size, cfg.n_routed_experts, cfg.top_k, cfg.moe_intermediate
+    dev = x.device
+    _need(x, _BF16, (T, H), "x")
+    _need(layer.gate_w, torch.float32, (E, H), "gate_w")
+    _need(layer.w13_codes, torch.uint8, (E, 2 * I, H // 2), "w13_codes")
+    _need(layer.w13_scales, torch.uint8, (E, 2 * I, H // 32), "w13_scales")
+    _need(w2_codes, torch.uint8, (E, H, I // 32 * 12), "w2_codes")
+    _need(w2_scales, (torch.int16, torch.uint16), (E, H, I // 32), "w2_scales")
+    if w2_levels is not None:
+        _need(w2_levels, torch.float32, (E, 8), "w2_levels")
+    _need(layer.sh_w13, torch.int8, (2 * I, H), "sh_w13")
+    _need(layer.sh_w2, torch.int8, (H, I), "sh_w2")
+    V = 0
+    if token_ids is not None:
+        _need(token_ids, torch.int32, (T,), "token_ids")
+        if layer.tid2eid is None:
+            raise ValueError("hash layer needs layer.tid2eid")
+        V = layer.tid2eid.shape[0]
+    else:
+        _need(layer.bias, torch.float32, (E,), "bias")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=dev)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    buf, nb = _ws(cfg, T, dev, ws)
+    _check(lib().moe_forward_w2q3(
+        ctypes.byref(cfg), T, _ptr(x), _ptr(layer.gate_w), _ptr(layer.bias), _ptr(layer.logit_offset),
+        _ptr(token_ids), _ptr(layer.tid2eid if token_ids is not None else None), V, _ptr(layer.w13_codes),
+        _ptr(layer.w13_scales), _ptr(w2_codes), _ptr(w2_scales), _ptr(w2_levels), _ptr(layer.sh_w13),
+        _ptr(layer.sh_w13_scale), _ptr(layer.sh_w2), _ptr(layer.sh_w2_scale), _ptr(out), int(out_fp32),
+        _ptr(ids), _ptr(w), _ptr(buf), nb, _stream(dev)), "moe_forward_w2q3")
     if return_routing:
         return out, (ids, w)
     return out

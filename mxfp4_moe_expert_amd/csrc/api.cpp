@@ -493,6 +493,35 @@ RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const floa
 // Hash layers take the same schedules, with the token's table row in place
 // of the top-k, except the three-launch tiny schedule (its routed w13 blocks
 // redo the top-k themselves): there they take the decode schedule.
+// Routed w2 in 3-bit blocks runs in the fused streaming launch (T <= 64; both
+// stages' K multiples of 1024) or the grouped GEMM (T > 64; H a multiple of 256).
+bool w2q3_supported(const moe_config& c, int T) {
+  if (T <= kSmallT) return c.hidden_size % 1024 == 0 && c.moe_intermediate % 1024 == 0;
+  return use_gemm(c, T);
+}
+
+// The routed experts' w2: MXFP4 (codes + E8M0 bytes) or 3-bit blocks (codes
+// + binary16 scales + optional per-expert levels).
+struct W2Weights {
+  int fmt;  // kFmtMx or kFmtQ3
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* table;
+};
+
+// Points a routed w2 pass (streaming or GEMM) at 3-bit blocks: codes
+// [E][H][I/32][12], binary16 scales [E][H][I/32], levels [E][8] or null.
+template <class Args>
+void set_w2q3(const moe_config& c, const W2Weights& w, Args& a) {
+  const long long H = c.hidden_size, I = c.moe_intermediate;
+  a.fmt = kFmtQ3;
+  a.wq = w.codes;
+  a.wsc = w.scales;
+  a.table = w.table;
+  a.q_expert_stride = H * (I / 32) * 12;
+  a.s_expert_stride = H * (I / 32) * 2;
+}
+
 int schedule(const moe_config& c, int T, bool hash) {
   if (T * (c.top_k + 1) <= 16) {
     if (layer_small_supported(c.hidden_size, c.moe_intermediate, c.n_routed_experts, T, c.top_k))
@@ -816,17 +845,20 @@ int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash) {
   return schedule(*cfg, T, hash != 0);
 }
 
-int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w, const float* bias,
-                const float* logit_offset, const int32_t* token_ids, const int32_t* tid2eid, int32_t V,
-                const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
-                const uint8_t* w2_scales, const int8_t* sh_w13, const float* sh_w13_scale,
-                const int8_t* sh_w2, const float* sh_w2_scale, void* out, int32_t out_is_fp32,
-                int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+static int forward_impl(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w,
+                        const float* bias, const float* logit_offset, const int32_t* token_ids,
+                        const int32_t* tid2eid, int32_t V, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                        const W2Weights& W2, const int8_t* sh_w13, const float* sh_w13_scale, const int8_t* sh_w2,
+                        const float* sh_w2_scale, void* out, int32_t out_is_fp32, int32_t* topk_ids_out,
+                        float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const uint8_t* w2_codes = W2.codes;
+  const uint8_t* w2_scales = W2.scales;
+  const bool q3 = W2.fmt == kFmtQ3;
   if (!cfg) return MOE_EINVAL;
   if (!cfg_ok(cfg) || T > kMaxT) return MOE_EUNSUPPORTED;
   if (T < 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
+  if (q3 && !w2q3_supported(*cfg, T)) return MOE_EUNSUPPORTED;
   const bool hash = token_ids != nullptr;
   if (!x || !gate_w || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !sh_w13 || !sh_w13_scale ||
       !sh_w2 || !sh_w2_scale || !out)
@@ -853,9 +885,10 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   const SkinnyArgs s13w = shared_w13_args(*cfg, T, x, sh_w13, sh_w13_scale, hs, &sh13w_blocks, false);
   const SkinnyArgs s2 = shared_w2_args(*cfg, T, sh_w2, sh_w2_scale, hs, zbuf, &sh2_blocks);
   const SkinnyArgs r13 = routed_w13_args(*cfg, T, x, p, w13_codes, w13_scales, hbuf);
-  const SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
+  SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
+  if (q3) set_w2q3(*cfg, W2, r2);
   const int r13_blocks = p.max_tiles * r13.n_rowblocks, r2_blocks = p.max_tiles * r2.n_rowblocks;
-  const int sched = schedule(*cfg, T, hash);
+  const int sched = q3 ? (T <= kSmallT ? MOE_SCHED_DECODE : MOE_SCHED_LARGE) : schedule(*cfg, T, hash);
   const bool tiny = sched == MOE_SCHED_TINY;
   const bool decode = sched == MOE_SCHED_DECODE;
 
@@ -999,13 +1032,14 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
       GemmArgs h13 = gemm_shared_w13(*cfg, T, x, sh_w13, sh_w13_scale, hs);
       uint16_t* ybf = reinterpret_cast<uint16_t*>(ybuf);  // the slot outputs in bf16 here
       GemmArgs g2 = gemm_routed_w2(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybf);
+      if (q3) set_w2q3(*cfg, W2, g2);
       GemmArgs h2 = gemm_shared_w2_combine(*cfg, T, sh_w2, sh_w2_scale, hs, ybf, out, out_is_fp32 ? 1 : 0);
       g13.queue = gemm_queue(workspace, L, kQRoutedW13);
       h13.queue = gemm_queue(workspace, L, kQSharedW13);
       g2.queue = gemm_queue(workspace, L, kQRoutedW2);
       h2.queue = gemm_queue(workspace, L, kQSharedW2);
       const int sh_tiles = (T + kGemmTokens - 1) / kGemmTokens;
-      if (L.mx) {
+      if (L.mx && !q3) {
         rc = status(routed_gemms_mx(*cfg, T, x, p, w, w13_codes, w13_scales, w2_codes, w2_scales, workspace, L, ybf,
                                     st));
         if (rc) return rc;
@@ -1029,6 +1063,33 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
   }
   CombineArgs cb{T, cfg->hidden_size, cfg->top_k, ybuf, zbuf, out, out_is_fp32 ? 1 : 0, 0};
   return status(timed(MOE_KERNEL_COMBINE, st, [&] { return launch_combine(cb, st); }));
+}
+
+int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w, const float* bias,
+                const float* logit_offset, const int32_t* token_ids, const int32_t* tid2eid, int32_t V,
+                const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
+                const uint8_t* w2_scales, const int8_t* sh_w13, const float* sh_w13_scale,
+                const int8_t* sh_w2, const float* sh_w2_scale, void* out, int32_t out_is_fp32,
+                int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  const W2Weights W2{kFmtMx, w2_codes, w2_scales, nullptr};
+  return forward_impl(cfg, T, x, gate_w, bias, logit_offset, token_ids, tid2eid, V, w13_codes, w13_scales, W2,
+                      sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, out, out_is_fp32, topk_ids_out, topk_w_out,
+                      workspace, workspace_bytes, stream);
+}
+
+int moe_forward_w2q3(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w, const float* bias,
+                     const float* logit_offset, const int32_t* token_ids, const int32_t* tid2eid, int32_t V,
+                     const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
+                     const uint16_t* w2_scales, const float* w2_levels, const int8_t* sh_w13,
+                     const float* sh_w13_scale, const int8_t* sh_w2, const float* sh_w2_scale, void* out,
+                     int32_t out_is_fp32, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (w2_levels && !aligned16(w2_levels)) return MOE_EINVAL;
+  const W2Weights W2{kFmtQ3, w2_codes, reinterpret_cast<const uint8_t*>(w2_scales), w2_levels};
+  return forward_impl(cfg, T, x, gate_w, bias, logit_offset, token_ids, tid2eid, V, w13_codes, w13_scales, W2,
+                      sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, out, out_is_fp32, topk_ids_out, topk_w_out,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

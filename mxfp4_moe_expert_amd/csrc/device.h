@@ -63,6 +63,83 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// 3-bit down-expert blocks: 32 weights along K in 12 code bytes (three
+// dwords D0, D1, D2) and a binary16 scale d; weight = d * level[code], with
+// 8 levels per table (the uniform book is code - 4). Code bits: byte j of
+// dword q (j < 4, q < 3) holds the code of weight 8q + j in bits 0..2 and of
+// weight 8q + 4 + j in bits 3..5; weight 24 + j has its bits 0..1 in bits
+// 6..7 of D0's byte j and bit 2 in bit 6 of D2's byte j; weight 28 + j the
+// same from D1's byte j and bit 7 of D2's byte j. The layout lets a mask
+// turn four codes into the byte selectors of one v_perm_b32.
+//
+// A lane's scaled code book for one block: level[c] * d rounded to bf16
+// (nearest even), split into byte planes so that one perm looks up the low
+// bytes of four weights and one the high bytes.
+struct Q3Book {
+  uint32_t lo0, lo1, hi0, hi1;  // lo0: low bytes of entries 0..3, lo1: of 4..7; hi*: high bytes
+};
+
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+__device__ __forceinline__ Q3Book q3_book(const float (&lv)[8], float d) {
+  const uint32_t p0 = bf16x2_rne(lv[0] * d, lv[1] * d), p1 = bf16x2_rne(lv[2] * d, lv[3] * d);
+  const uint32_t p2 = bf16x2_rne(lv[4] * d, lv[5] * d), p3 = bf16x2_rne(lv[6] * d, lv[7] * d);
+  Q3Book b;
+  b.lo0 = __builtin_amdgcn_perm(p1, p0, 0x06040200u);  // bytes 0, 2 of p0, then of p1
+  b.hi0 = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+  b.lo1 = __builtin_amdgcn_perm(p3, p2, 0x06040200u);
+  b.hi1 = __builtin_amdgcn_perm(p3, p2, 0x07050301u);
+  return b;
+}
+
+// Four codes (selector bytes 0..7) -> four bf16 of the book, as two dwords.
+__device__ __forceinline__ uint2 q3_look4(const Q3Book& b, uint32_t sel) {
+  const uint32_t lo = __builtin_amdgcn_perm(b.lo1, b.lo0, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(b.hi1, b.hi0, sel);
+  return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
+// Weights 8kk .. 8kk+7 of a block as bf16, in order.
+__device__ __forceinline__ bf16x8_t q3_frag(uint32_t d0, uint32_t d1, uint32_t d2, int kk, const Q3Book& b) {
+  uint32_t sa, sb;
+  if (kk == 0) {
+    sa = d0 & 0x07070707u;
+    sb = (d0 >> 3) & 0x07070707u;
+  } else if (kk == 1) {
+    sa = d1 & 0x07070707u;
+    sb = (d1 >> 3) & 0x07070707u;
+  } else if (kk == 2) {
+    sa = d2 & 0x07070707u;
+    sb = (d2 >> 3) & 0x07070707u;
+  } else {
+    sa = ((d0 >> 6) & 0x03030303u) | ((d2 >> 4) & 0x04040404u);
+    sb = ((d1 >> 6) & 0x03030303u) | ((d2 >> 5) & 0x04040404u);
+  }
+  const uint2 x = q3_look4(b, sa), y = q3_look4(b, sb);
+  const uint4 u = make_uint4(x.x, x.y, y.x, y.y);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// The 8 levels of a table (expert e's row of `table`), or the uniform book
+// when table is null. e is uniform across the wave.
+__device__ __forceinline__ void q3_levels(const float* table, int e, float (&lv)[8]) {
+  if (table) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lv[c] = table[(size_t)e * 8 + c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lv[c] = (float)(c - 4);
+  }
+}
+
 // D[16x16] += A[16x32] * B[32x16], bf16 in, fp32 accumulate.
 // Lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16] and
 // D[4*(l/16) .. +4][l%16] (checked on gfx950).

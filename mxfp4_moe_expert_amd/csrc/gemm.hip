@@ -58,40 +58,56 @@ constexpr int kRB = 2;              // 16-row weight blocks per wave
 // thread's quarter of one token row: pieces kk = 0 .. kKK-1 of quarter g).
 template <int FMT>
 struct GemmCfg {
-  static constexpr int kBK = FMT == kFmtMx ? 128 : 64;
+  static constexpr int kBK = FMT != kFmtI8 ? 128 : 64;
   static constexpr int kKK = kBK / 32;
   static constexpr int kStage = kBM * kBK * 2;
   static constexpr int kAVec = kBK / 32;
   static_assert(kAVec == kKK, "a thread's pieces are the k-steps of one quarter");
 };
 
-// A lane's 16 weight bytes for one row block and stage, converted to bf16
-// eight K-values at a time.
+// A lane's weight bytes for one row block and stage, converted to bf16
+// eight K-values at a time (MXFP4: scaled FP4 convert; 3-bit: look-ups in
+// the block's scaled code book; int8: exact).
 template <int FMT>
-__device__ __forceinline__ bf16x8_t gemm_conv(const u32x4_t& q, int kk, uint32_t sc) {
+__device__ __forceinline__ bf16x8_t gemm_conv(const u32x4_t& q, int kk, uint32_t sc, const Q3Book& book) {
   if constexpr (FMT == kFmtMx) {
     const uint32_t d = kk == 0 ? q.x : kk == 1 ? q.y : kk == 2 ? q.z : q.w;
     return fp4x8_to_bf16x8(d, e8m0_scale_operand(sc));
+  } else if constexpr (FMT == kFmtQ3) {
+    return q3_frag(q.x, q.y, q.z, kk, book);
   } else {
     return i8x8_to_bf16x8(kk == 0 ? q.x : q.z, kk == 0 ? q.y : q.w);
   }
 }
 
-// Weights of the wave's row blocks for stage st.
+// Weights of the wave's row blocks for stage st: 16 bytes per lane and row
+// block (MXFP4, int8) or one 12-byte 3-bit block.
+template <int FMT>
 __device__ __forceinline__ void gemm_load_w(const uint8_t* qe, const uint32_t (&qoff)[kRB], int st,
                                             u32x4_t (&w)[kRB]) {
 #pragma unroll
-  for (int b = 0; b < kRB; ++b) w[b] = *reinterpret_cast<const u32x4_t*>(qe + (qoff[b] + (uint32_t)st * 64));
+  for (int b = 0; b < kRB; ++b) {
+    if constexpr (FMT == kFmtQ3) {
+      const uint32_t* s = reinterpret_cast<const uint32_t*>(qe + (qoff[b] + (uint32_t)st * 48));
+      w[b] = (u32x4_t){s[0], s[1], s[2], 0u};
+    } else {
+      w[b] = *reinterpret_cast<const u32x4_t*>(qe + (qoff[b] + (uint32_t)st * 64));
+    }
+  }
 }
 
-// MXFP4: the E8M0 byte of the lane's 32 K-values of stage st in each row
-// block (byte 4 st + g of the row: those 32 values are exactly one group),
-// from the block's scales in LDS.
+// The scale of the lane's 32 K-values of stage st in each row block (block
+// 4 st + g of the row: those 32 values are exactly one group), from the
+// block's scales in LDS: an E8M0 byte (MXFP4) or binary16 bits (3-bit).
 template <int FMT>
 __device__ __forceinline__ void gemm_scales(const unsigned char* lds_s, const uint32_t (&soff)[kRB], int st,
                                             uint32_t (&sc)[kRB]) {
 #pragma unroll
-  for (int b = 0; b < kRB; ++b) sc[b] = FMT == kFmtMx ? lds_s[soff[b] + (uint32_t)st * 4] : 0u;
+  for (int b = 0; b < kRB; ++b) {
+    if constexpr (FMT == kFmtMx) sc[b] = lds_s[soff[b] + (uint32_t)st * 4];
+    else if constexpr (FMT == kFmtQ3) sc[b] = *reinterpret_cast<const uint16_t*>(lds_s + soff[b] + (uint32_t)st * 8);
+    else sc[b] = 0u;
+  }
 }
 
 
@@ -124,10 +140,15 @@ struct GemmA {
 template <int FMT, int MB>
 __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x4_t (&w)[kRB],
                                              const unsigned char* lds_s, const uint32_t (&soff)[kRB], int st,
-                                             const unsigned char* abase) {
+                                             const unsigned char* abase, const float (&lv)[8]) {
   constexpr int kKK = GemmCfg<FMT>::kKK;
   uint32_t sc[kRB];
   gemm_scales<FMT>(lds_s, soff, st, sc);
+  Q3Book book[kRB] = {};
+  if constexpr (FMT == kFmtQ3) {
+#pragma unroll
+    for (int b = 0; b < kRB; ++b) book[b] = q3_book(lv, f16_bits_to_f32(sc[b]));
+  }
   // int8 weights are unpacked here, in their stage: without the empty asm
   // the compiler starts unpacking them right after their load, a stage
   // ahead, which waits for that load and holds the unpacked bytes meanwhile
@@ -151,7 +172,7 @@ __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t wa[kRB];
 #pragma unroll
-    for (int b = 0; b < kRB; ++b) wa[b] = gemm_conv<FMT>(wv[b], kk, sc[b]);
+    for (int b = 0; b < kRB; ++b) wa[b] = gemm_conv<FMT>(wv[b], kk, sc[b], book[b]);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -166,7 +187,8 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
                                           const uint16_t* asrc, u32x4_t* adst0, u32x4_t* adst1,
                                           const unsigned char* abase0, const unsigned char* abase1, int nst,
                                           int ncols, int pos0, int nt, int wn, int g, int r,
-                                          const StoreScales& store_scales, const int (&slot_r)[kMB]) {
+                                          const StoreScales& store_scales, const int (&slot_r)[kMB],
+                                          const float (&lv)[8]) {
   f32x4_t acc[kRB][MB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b)
@@ -181,7 +203,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
   u32x4_t w0[kRB], w1[kRB];
   GemmA<FMT> av0, av1;
   const int last = nst - 1;
-  gemm_load_w(qe, qoff, 0, w0);
+  gemm_load_w<FMT>(qe, qoff, 0, w0);
   av0.load(asrc, 0);
   store_scales();  // the block's scales, requested before these first loads
   // routed w2: the routing weights of the lane's columns (their slots came
@@ -193,22 +215,22 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
   av0.store(adst0);
   av1.load(asrc, min(1, last));
   av0.load(asrc, min(2, last));
-  gemm_load_w(qe, qoff, min(1, last), w1);
+  gemm_load_w<FMT>(qe, qoff, min(1, last), w1);
   for (int st = 0; st + 1 < nst; st += 2) {
     __syncthreads();
     av1.store(adst1);  // stage st+1
     av1.load(asrc, min(st + 3, last));
-    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, st, abase0);
-    gemm_load_w(qe, qoff, min(st + 2, last), w0);
+    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, st, abase0, lv);
+    gemm_load_w<FMT>(qe, qoff, min(st + 2, last), w0);
     __syncthreads();
     av0.store(adst0);  // stage st+2
     av0.load(asrc, min(st + 4, last));
-    gemm_compute<FMT, MB>(acc, w1, lds_s, soff, st + 1, abase1);
-    gemm_load_w(qe, qoff, min(st + 3, last), w1);
+    gemm_compute<FMT, MB>(acc, w1, lds_s, soff, st + 1, abase1, lv);
+    gemm_load_w<FMT>(qe, qoff, min(st + 3, last), w1);
   }
   if (nst & 1) {  // the last stage (buffer 0, w0)
     __syncthreads();
-    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, last, abase0);
+    gemm_compute<FMT, MB>(acc, w0, lds_s, soff, last, abase0, lv);
   }
 
   // epilogue: lane holds acc[b][m][i] = D[row 4g+i of block b][token r of block m]
@@ -277,7 +299,8 @@ template <int FMT, int MODE>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr int kBK = GemmCfg<FMT>::kBK, kKK = GemmCfg<FMT>::kKK;
   __shared__ __align__(16) unsigned char lds_a[2][GemmCfg<FMT>::kStage];
-  extern __shared__ __align__(16) unsigned char lds_s[];  // MXFP4: [256 local rows][K/32 + 4] E8M0 bytes
+  // MXFP4: [256 local rows][K/32 + 4] E8M0 bytes; 3-bit: [256][K/16 + 4] bytes of binary16 scales
+  extern __shared__ __align__(16) unsigned char lds_s[];
   __shared__ int grabbed;
 
   // Persistent: at most the blocks that fit at once, each walking tiles.
@@ -297,8 +320,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 
   const int K = p.K;
   const int nst = K / kBK;
-  const int srow = K / 32 + 4;  // padded LDS row of scales
-  const int rowlen = K / 32, npieces = FMT == kFmtMx ? 2 * 128 * rowlen / 16 : 0;
+  const int rowlen = FMT == kFmtQ3 ? K / 16 : K / 32;  // scale bytes per weight row
+  const int srow = rowlen + 4;                          // padded LDS row of scales
+  const int npieces = FMT != kFmtI8 ? 2 * 128 * rowlen / 16 : 0;
   const int hpieces = npieces > 1 ? npieces / 2 : 1;  // pieces per run of 128 rows
   constexpr int kScalePieces = 4;
 
@@ -342,16 +366,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
     // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
     const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
+    float lv[8] = {};  // 3-bit: the expert's levels
+    if constexpr (FMT == kFmtQ3) q3_levels(p.table, e, lv);
     uint32_t qoff[kRB], soff[kRB];
 #pragma unroll
     for (int b = 0; b < kRB; ++b) {
       int wrow;
       if (MODE == kGemmW13) wrow = (b == 0 ? 0 : p.half) + nt * (kBN / 2) + wn * 16 + r;
       else wrow = nt * kBN + wn * 32 + b * 16 + r;
-      qoff[b] = (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
+      qoff[b] = FMT == kFmtQ3 ? (uint32_t)wrow * (K / 32 * 12) + g * 12
+                              : (uint32_t)wrow * (FMT == kFmtMx ? K / 2 : K) + g * 16;
       // local row: gate rows (w13) or the first 128 rows (w2) at 0 .., the rest at 128 ..
       const int lrow = MODE == kGemmW13 ? (b == 0 ? 0 : 128) + wn * 16 + r : wn * 32 + b * 16 + r;
-      soff[b] = (uint32_t)lrow * srow + g;
+      soff[b] = (uint32_t)lrow * srow + g * (FMT == kFmtQ3 ? 2 : 1);
     }
     // the tile's scales: two runs of 128 rows (w13: gate rows, up rows; w2:
     // the tile's 256 rows), K/32 bytes per row, in 16-byte pieces. Up to
@@ -383,13 +410,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       slot_r[m] = MODE == kGemmW2 ? p.sorted_slots[pos0 + (tok < ncols ? tok : 0)] : 0;
     }
     uint4 scv[kScalePieces];
-    if (FMT == kFmtMx) {
+    if (FMT != kFmtI8) {
 #pragma unroll
       for (int j = 0; j < kScalePieces; ++j) scv[j] = *piece_src(min(tid + j * kGemmThreads, npieces - 1));
     }
     const int arow = wave * 16 + r;
     auto store_scales = [&]() __attribute__((always_inline)) {
-      if (FMT == kFmtMx) {
+      if (FMT != kFmtI8) {
 #pragma unroll
         for (int j = 0; j < kScalePieces; ++j) {
           const int i = tid + j * kGemmThreads;
@@ -418,19 +445,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     switch ((ncols + 31) >> 5) {
       case 1:
         gemm_main<FMT, MODE, 2>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                wn, g, r, store_scales, slot_r);
+                                wn, g, r, store_scales, slot_r, lv);
         break;
       case 2:
         gemm_main<FMT, MODE, 4>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                wn, g, r, store_scales, slot_r);
+                                wn, g, r, store_scales, slot_r, lv);
         break;
       case 3:
         gemm_main<FMT, MODE, 6>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0, nt,
-                                wn, g, r, store_scales, slot_r);
+                                wn, g, r, store_scales, slot_r, lv);
         break;
       default:
         gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0,
-                                  nt, wn, g, r, store_scales, slot_r);
+                                  nt, wn, g, r, store_scales, slot_r, lv);
     }
     if (tid == 0) grabbed = lo + 2 * nx + grab;
     __syncthreads();  // every wave is done with this tile's LDS; the grab is visible
@@ -451,7 +478,7 @@ static hipError_t launch_gemm_t(const GemmArgs& p, int tiles, hipStream_t st) {
   const long long nblk = (long long)tiles * p.n_ntiles;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  const size_t dyn = FMT == kFmtMx ? (size_t)2 * 128 * (p.K / 32 + 4) : 0;
+  const size_t dyn = FMT != kFmtI8 ? (size_t)2 * 128 * (p.K / (FMT == kFmtQ3 ? 16 : 32) + 4) : 0;
   if (dyn + 2 * GemmCfg<FMT>::kStage > 160 * 1024) return hipErrorInvalidValue;
   static size_t raised = 0;  // dynamic LDS limit set so far for this kernel
   if (dyn > raised) {
@@ -480,6 +507,10 @@ hipError_t launch_gemm(const GemmArgs& p, int tiles, hipStream_t st) {
   if (p.fmt == kFmtMx) {
     if (p.mode == kGemmW13) return launch_gemm_t<kFmtMx, kGemmW13>(p, tiles, st);
     return launch_gemm_t<kFmtMx, kGemmW2>(p, tiles, st);
+  }
+  if (p.fmt == kFmtQ3) {  // routed w2 only
+    if (p.mode != kGemmW2) return hipErrorInvalidValue;
+    return launch_gemm_t<kFmtQ3, kGemmW2>(p, tiles, st);
   }
   if (p.mode == kGemmW13) return launch_gemm_t<kFmtI8, kGemmW13>(p, tiles, st);
   return launch_gemm_t<kFmtI8, kGemmW2Combine>(p, tiles, st);

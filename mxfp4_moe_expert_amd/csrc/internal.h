@@ -40,7 +40,9 @@ struct Perm {
 // passes clamp or mask the others).
 constexpr int kRecInts = 52;
 
-enum { kFmtMx = 0, kFmtI8 = 1 };  // routed MXFP4 / shared int8 weights
+// routed MXFP4 / shared int8 / routed w2 in 3-bit blocks (12 code bytes +
+// a binary16 scale per 32 weights, 8 levels per expert table)
+enum { kFmtMx = 0, kFmtI8 = 1, kFmtQ3 = 2 };
 enum { kW13 = 0, kW2 = 1 };        // expert stage
 
 struct RouterArgs {
@@ -78,8 +80,10 @@ struct HashArgs {
 // w13, 16 gate rows and the 16 matching up rows) against one tile of at most
 // 16 activation columns; K split over the 8 waves of the block.
 struct SkinnyArgs {
-  const uint8_t* wq;          // MXFP4 codes [E][N][K/2] or int8 [N][K]
-  const uint8_t* wsc;         // MXFP4 scales [E][N][K/32] (null for int8)
+  const uint8_t* wq;          // MXFP4 codes [E][N][K/2], 3-bit codes [E][N][K/32][12] or int8 [N][K]
+  const uint8_t* wsc;         // MXFP4 E8M0 [E][N][K/32], 3-bit binary16 [E][N][K/32] (null for int8)
+  const float* table;         // 3-bit: levels [E][8], null for the uniform book
+  int fmt;                    // kFmtQ3 for a routed w2 pass in 3-bit blocks (else unused)
   const float* row_scale;     // int8 per-row scales [N] (null for MXFP4)
   long long q_expert_stride;  // bytes between experts of wq
   long long s_expert_stride;  // bytes between experts of wsc
@@ -137,11 +141,12 @@ struct W2CombineArgs {
 // weight rows.
 enum { kGemmW13 = 0, kGemmW2 = 1, kGemmW2Combine = 2 };
 struct GemmArgs {
-  int fmt;                    // 0 MXFP4 (routed), 1 int8 (shared)
+  int fmt;                    // kFmtMx (routed), kFmtI8 (shared), kFmtQ3 (routed w2 only)
   int mode;                   // kGemmW13: SwiGLU -> hout; kGemmW2: x slot weight -> yout[slot];
                               // kGemmW2Combine: shared w2 + sum of the slots' ybuf -> out
   const uint8_t* wq;
   const uint8_t* wsc;
+  const float* table;         // 3-bit: levels [E][8], null for the uniform book
   const float* row_scale;     // int8 per-row scales
   long long q_expert_stride, s_expert_stride;
   int K, half;

@@ -55,25 +55,40 @@ constexpr int kUnitRows = 256;  // weight rows per unit
 
 template <int FMT>
 struct StreamStage {
-  uint4 q[FMT == kFmtMx ? 1 : 2];
+  uint4 q[FMT == kFmtI8 ? 2 : 1];
 };
 
 template <int FMT>
 __device__ __forceinline__ void stream_load(const uint8_t* q, int st, StreamStage<FMT>& d) {
   if constexpr (FMT == kFmtMx) {
     d.q[0] = *reinterpret_cast<const uint4*>(q + (size_t)st * 64);
+  } else if constexpr (FMT == kFmtQ3) {  // one 32-weight block: 12 bytes
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(q + (size_t)st * 48);
+    d.q[0] = make_uint4(s[0], s[1], s[2], 0u);
   } else {
     d.q[0] = *reinterpret_cast<const uint4*>(q + (size_t)st * 128);
     d.q[1] = *reinterpret_cast<const uint4*>(q + (size_t)st * 128 + 64);
   }
 }
 
-// scale: the E8M0 byte of the lane's group (MXFP4), unused for int8
+// Per row block and stage, what turns the lane's codes into bf16: the E8M0
+// scale operand (MXFP4), the scaled code book (3-bit), nothing (int8).
 template <int FMT>
-__device__ __forceinline__ bf16x8_t stream_frag(const StreamStage<FMT>& d, int kk, uint32_t scale) {
+struct StreamDec {
+  float sc;
+};
+template <>
+struct StreamDec<kFmtQ3> {
+  Q3Book book;
+};
+
+template <int FMT>
+__device__ __forceinline__ bf16x8_t stream_frag(const StreamStage<FMT>& d, int kk, const StreamDec<FMT>& dec) {
   if constexpr (FMT == kFmtMx) {
     const uint32_t w = kk == 0 ? d.q[0].x : kk == 1 ? d.q[0].y : kk == 2 ? d.q[0].z : d.q[0].w;
-    return fp4x8_to_bf16x8(w, e8m0_scale_operand(scale));
+    return fp4x8_to_bf16x8(w, dec.sc);
+  } else if constexpr (FMT == kFmtQ3) {
+    return q3_frag(d.q[0].x, d.q[0].y, d.q[0].z, kk, dec.book);
   } else {
     const uint4 u = d.q[kk >> 1];
     return i8x8_to_bf16x8((kk & 1) ? u.z : u.x, (kk & 1) ? u.w : u.y);
@@ -107,10 +122,11 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K, S = K >> 7, n16 = K >> 3, row_bytes = 2 * K + 16;
   const int nrb = p.n_rowblocks;
-  const int srow = K / 32;  // scale bytes per row (a multiple of 4)
+  // scale bytes per row (a multiple of 4): one E8M0 byte or one binary16 per 32 weights
+  const int srow = FMT == kFmtQ3 ? K / 16 : K / 32;
   unsigned char* lds_sc = lds + (size_t)p.tile_n * row_bytes;  // [256 rows][srow]
   const bool sc16 = srow % 16 == 0;                            // rows of whole 16-byte pieces
-  const int nsc = FMT == kFmtMx ? kUnitRows * srow / (sc16 ? 16 : 4) : 0;
+  const int nsc = FMT != kFmtI8 ? kUnitRows * srow / (sc16 ? 16 : 4) : 0;
   // this lane's two block rows (of the unit's 256)
   const int brA = MODE == kW13 ? wave * 16 + r : wave * 32 + r;
   const int brB = MODE == kW13 ? 128 + wave * 16 + r : wave * 32 + 16 + r;
@@ -121,7 +137,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   // shared tiles (consecutive tokens) computed
   auto rec_of = [&](int i) -> int {
     const int tile = local(i) / nrb;
-    if constexpr (FMT == kFmtMx) {
+    if constexpr (FMT != kFmtI8) {
       return p.tile_rec[(size_t)tile * kRecInts + min(lane, kRecInts - 1)];
     } else {
       const int pos0 = tile * p.tile_n, ncols = min(p.tile_n, p.T - pos0);
@@ -144,6 +160,8 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   };
   auto wptr = [&](const SUnit& x, int br) -> const uint8_t* {
     if (FMT == kFmtMx) return p.wq + (long long)x.e * p.q_expert_stride + (size_t)grow(x, br) * (K / 2) + g * 16;
+    if (FMT == kFmtQ3)
+      return p.wq + (long long)x.e * p.q_expert_stride + (size_t)grow(x, br) * (K / 32 * 12) + g * 12;
     return p.wq + (size_t)grow(x, br) * K + g * 16;
   };
   auto sc_src = [&](const SUnit& x, int i, int piece) {  // piece i of the unit's scales
@@ -199,7 +217,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   u32x4_t sv[NS], av[NA];
   float es[8] = {};
   auto load_ops = [&](const SUnit& x) __attribute__((always_inline)) {
-    if constexpr (FMT == kFmtMx) {
+    if constexpr (FMT != kFmtI8) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         // rows of dword pieces are loaded at the boundary; meanwhile a
@@ -224,7 +242,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     asm volatile("" ::: "memory");
   };
   auto store_ops = [&](const SUnit& x) __attribute__((always_inline)) {
-    if constexpr (FMT == kFmtMx) {
+    if constexpr (FMT != kFmtI8) {
       if (sc16) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -250,12 +268,14 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   // MXFP4 stages come in pairs whose loads are issued back to back: the two
   // 64-byte halves of each 128-byte line of a row (one int8 stage reads a
   // whole line in two adjacent loads already)
-  constexpr int P = (FMT == kFmtMx && D % 2 == 0) ? 2 : 1;
+  constexpr int P = (FMT != kFmtI8 && D % 2 == 0) ? 2 : 1;
 
   // first unit: its record, its first D stages, its operands; the next
   // unit's record
   SUnit cur = unit_of(idx[0], rec_of(idx[0]));
   int rec_nxt = rec_of(idx[1]);
+  float lv[8] = {};  // 3-bit: the current unit's expert's levels
+  if constexpr (FMT == kFmtQ3) q3_levels(p.table, cur.e, lv);
   const uint8_t* qA = wptr(cur, brA);
   const uint8_t* qB = wptr(cur, brB);
   StreamStage<FMT> wA[D], wB[D];
@@ -280,22 +300,29 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   for (;;) {
     f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     const bool live = r < cur.ncols;
-    const unsigned char* bcol = lds + (live ? r : 0) * row_bytes + g * (FMT == kFmtMx ? 64 : 32);
-    const unsigned char* scA = lds_sc + (size_t)brA * srow + g;  // group 4 st + g of each row
-    const unsigned char* scB = lds_sc + (size_t)brB * srow + g;
+    const unsigned char* bcol = lds + (live ? r : 0) * row_bytes + g * (FMT != kFmtI8 ? 64 : 32);
+    // the scale of block 4 st + g of each row (MXFP4: a byte, 3-bit: a binary16)
+    const unsigned char* scA = lds_sc + (size_t)brA * srow + g * (FMT == kFmtQ3 ? 2 : 1);
+    const unsigned char* scB = lds_sc + (size_t)brB * srow + g * (FMT == kFmtQ3 ? 2 : 1);
     // byte offset in the column of fragment kk (the lane's K-values of it)
-    auto kbyte = [](int kk) { return FMT == kFmtMx ? kk * 16 : (kk >> 1) * 128 + (kk & 1) * 16; };
+    auto kbyte = [](int kk) { return FMT != kFmtI8 ? kk * 16 : (kk >> 1) * 128 + (kk & 1) * 16; };
+    auto dec_of = [&](const unsigned char* sc, int st) __attribute__((always_inline)) {
+      StreamDec<FMT> d{};
+      if constexpr (FMT == kFmtMx) d.sc = e8m0_scale_operand(sc[st * 4]);
+      if constexpr (FMT == kFmtQ3)
+        d.book = q3_book(lv, f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc + st * 8)));
+      return d;
+    };
     auto stage = [&](int i, int st) __attribute__((always_inline)) {
       bf16x8_t b[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         b[kk] = live ? *reinterpret_cast<const bf16x8_t*>(bcol + st * 256 + kbyte(kk)) : zero8;
-      const uint32_t scaleA = FMT == kFmtMx ? scA[st * 4] : 0u;
-      const uint32_t scaleB = FMT == kFmtMx ? scB[st * 4] : 0u;
+      const StreamDec<FMT> decA = dec_of(scA, st), decB = dec_of(scB, st);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        accA = mfma_16x16x32(stream_frag<FMT>(wA[i], kk, scaleA), b[kk], accA);
-        accB = mfma_16x16x32(stream_frag<FMT>(wB[i], kk, scaleB), b[kk], accB);
+        accA = mfma_16x16x32(stream_frag<FMT>(wA[i], kk, decA), b[kk], accA);
+        accB = mfma_16x16x32(stream_frag<FMT>(wB[i], kk, decB), b[kk], accB);
       }
     };
     // Main loop: consume stages st0 .. st0+D-1, request st0+D .. st0+2D-1.
@@ -318,6 +345,8 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     // it, the next grab, then its first stages
     const bool more = in_range(idx[1]);
     const SUnit nxt = unit_of(more ? idx[1] : idx[0], more ? rec_nxt : cur.rec);
+    float lv_nxt[8] = {};
+    if constexpr (FMT == kFmtQ3) q3_levels(p.table, nxt.e, lv_nxt);
     const uint8_t* nA = more ? wptr(nxt, brA) : qA;
     const uint8_t* nB = more ? wptr(nxt, brB) : qB;
     const int nst = more ? 0 : S - D;
@@ -348,7 +377,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     // epilogue: lane (r, g) holds rows 4g .. 4g+3 of each row block, column r
     int slot = 0;
     float wv = 0.0f;
-    if (FMT == kFmtMx && MODE == kW2) {  // every lane takes part in the shuffles
+    if (FMT != kFmtI8 && MODE == kW2) {  // every lane takes part in the shuffles
       slot = __shfl(cur.rec, 20 + r);
       wv = __int_as_float(__shfl(cur.rec, 36 + r));
     }
@@ -380,7 +409,7 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
         float* dst;
         float4 ya, yb;
         if (!cur_ok) wv = __builtin_nanf("");  // the wait for this unit's h expired
-        if (FMT == kFmtMx) {
+        if (FMT != kFmtI8) {
           ya = make_float4(accA[0] * wv, accA[1] * wv, accA[2] * wv, accA[3] * wv);
           yb = make_float4(accB[0] * wv, accB[1] * wv, accB[2] * wv, accB[3] * wv);
           dst = p.yout + (size_t)slot * p.yout_ld;
@@ -412,6 +441,10 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     if (!more) break;
     cur = nxt;
     cur_ok = nxt_ok;
+    if constexpr (FMT == kFmtQ3) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) lv[c] = lv_nxt[c];
+    }
     rec_nxt = rec_after;
     poll_nxt = poll_after;
     qA = nA;
@@ -455,7 +488,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(SkinnyArgs a, int has
 // last w13 units and the w2 units start without a launch in between; a w2
 // unit waits (rarely) for its tile's w13 units through done_r (routed tiles)
 // and done_s (shared tiles), which the tile builders zero.
-template <int DA, int DB>
+// Q3: the routed w2 pass reads 3-bit blocks; a unit's binary16 scales (256
+// rows x K/16 bytes) are 4 pieces per thread at K = 2048.
+template <int DA, int DB, bool Q3>
 __global__ __launch_bounds__(kStreamThreads) void k_stream_fused(SkinnyArgs a13, SkinnyArgs b13, SkinnyArgs a2,
                                                                  SkinnyArgs b2, int* queue, int* done_r,
                                                                  int* done_s) {
@@ -477,7 +512,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fused(SkinnyArgs a13,
   if (idx[0] >= e1 && idx[0] < e2)
     stream_loop<kFmtI8, kW2, DB, 1, 4, true>(b2, e1, e2, queue, idx, lds, sh, done_s, b13.n_rowblocks);
   if (idx[0] >= e2 && idx[0] < e3)
-    stream_loop<kFmtMx, kW2, DA, 2, 3, true>(a2, e2, e3, queue, idx, lds, sh, done_r, a13.n_rowblocks);
+    stream_loop<Q3 ? kFmtQ3 : kFmtMx, kW2, DA, Q3 ? 4 : 2, 3, true>(a2, e2, e3, queue, idx, lds, sh, done_r,
+                                                                   a13.n_rowblocks);
 }
 
 // Blocks of kernel k with lds bytes that the current device holds at once
@@ -548,7 +584,8 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
 
 static size_t stream_lds(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks) {
   size_t lds = 0;
-  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / 32);
+  if (a_blocks > 0)
+    lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / (a.fmt == kFmtQ3 ? 16 : 32));
   if (b_blocks > 0) {
     const size_t lb = (size_t)b.tile_n * (2 * (size_t)b.K + 16);
     lds = lb > lds ? lb : lds;
@@ -569,10 +606,12 @@ hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, con
     return hipErrorInvalidValue;
   const long long nblk = (long long)a_blocks13 + b_blocks13 + a_blocks2 + b_blocks2;
   if (nblk > 0x3fffffffLL) return hipErrorInvalidValue;
+  const bool q3 = a2.fmt == kFmtQ3;
+  if (a13.fmt == kFmtQ3) return hipErrorInvalidValue;  // 3-bit blocks are a w2 format
   size_t lds = stream_lds(a13, a_blocks13, b13, b_blocks13);
   const size_t l2 = stream_lds(a2, a_blocks2, b2, b_blocks2);
   lds = l2 > lds ? l2 : lds;
-  auto kern = &k_stream_fused<kDA, kDB>;
+  auto kern = q3 ? &k_stream_fused<kDA, kDB, true> : &k_stream_fused<kDA, kDB, false>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -593,6 +632,7 @@ hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, con
 // largest that divides it of 4 and 1.
 hipError_t launch_stream(int mode, const SkinnyArgs& a, int a_blocks, const SkinnyArgs* b, int b_blocks, int* queue,
                          hipStream_t st) {
+  if (a_blocks > 0 && a.fmt == kFmtQ3) return hipErrorInvalidValue;  // 3-bit w2 runs in the fused launch only
   SkinnyArgs bb{};
   if (b) bb = *b; else b_blocks = 0;
   const int K = a_blocks > 0 ? a.K : bb.K;

@@ -68,16 +68,18 @@ def assert_outputs_close(gpu, ref, what=""):
     return e
 
 
-def reference_rows(layer, x, rows, token_ids=None, routing=None):
+def reference_rows(layer, x, rows, token_ids=None, routing=None, fwd=None):
     """Oracle outputs for ``rows``; rows whose GPU selection was a near-tie swap
-    are recomputed by the oracle with its own one-swap alternative."""
-    r = oracle.forward(layer, x, token_ids=token_ids, rows=np.asarray(rows, np.int32))
+    are recomputed by the oracle with its own one-swap alternative. ``fwd``
+    replaces ``oracle.forward`` (same keyword arguments)."""
+    fwd = fwd or oracle.forward
+    r = fwd(layer, x, token_ids=token_ids, rows=np.asarray(rows, np.int32))
     out = r["out"]
     if routing is not None:
         for i, t in enumerate(rows):
             if int(t) in routing["alt_rows"]:
                 alt = routing["alt_rows"][int(t)][None, :]
-                r2 = oracle.forward(layer, x, rows=np.array([t], np.int32), force_ids=alt)
+                r2 = fwd(layer, x, rows=np.array([t], np.int32), force_ids=alt)
                 out[i] = r2["out"][0]
     return r, out
 

@@ -94,6 +94,30 @@ def test_invalid_arguments_are_rejected_before_launch():
                          None, None, p, 100, None) == mx.MOE_EWORKSPACE
 
 
+def test_w2q3_host_checks():
+    """moe_forward_w2q3: shapes without a 3-bit path are refused, and the
+    usual pointer checks apply, before anything is launched."""
+    L = mx.lib()
+    p = ctypes.c_void_p(0x100000)
+    q = ctypes.c_void_p(0x100004)
+    small = _cfg(hidden_size=512, moe_intermediate=256, n_routed_experts=16)
+    cfg = _cfg()
+    for c, T, want in ((small, 4, mx.MOE_EUNSUPPORTED), (cfg, 70000, mx.MOE_EUNSUPPORTED)):
+        nb = L.moe_workspace_size(ctypes.byref(c), min(T, 64))
+        assert L.moe_forward_w2q3(ctypes.byref(c), T, p, p, p, None, None, None, 0, p, p, p, p, None, p, p, p, p,
+                                  p, 0, None, None, p, nb, None) == want
+    nb = L.moe_workspace_size(ctypes.byref(cfg), 4)
+    # misaligned levels, null codes, too small a workspace
+    assert L.moe_forward_w2q3(ctypes.byref(cfg), 4, p, p, p, None, None, None, 0, p, p, p, p, q, p, p, p, p, p, 0,
+                              None, None, p, nb, None) == mx.MOE_EINVAL
+    assert L.moe_forward_w2q3(ctypes.byref(cfg), 4, p, p, p, None, None, None, 0, p, p, None, p, None, p, p, p, p,
+                              p, 0, None, None, p, nb, None) == mx.MOE_EINVAL
+    assert L.moe_forward_w2q3(ctypes.byref(cfg), 4, p, p, p, None, None, None, 0, p, p, p, p, None, p, p, p, p, p,
+                              0, None, None, p, 100, None) == mx.MOE_EWORKSPACE
+    assert L.moe_forward_w2q3(ctypes.byref(cfg), 0, None, None, None, None, None, None, 0, None, None, None, None,
+                              None, None, None, None, None, None, 0, None, None, None, 0, None) == mx.MOE_OK
+
+
 def test_empty_batch_is_a_no_op():
     L = mx.lib()
     cfg = _cfg()

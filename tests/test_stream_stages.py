@@ -108,4 +108,4 @@ def test_kernel_source_matches_model():
     assert "const int nst = more ? 0 : S - D;" in src
     assert "return K % 128 == 0 && S >= D && S % D == 0;" in src
     assert "constexpr int kDA = 8, kDB = 4;" in src
-    assert "constexpr int P = (FMT == kFmtMx && D % 2 == 0) ? 2 : 1;" in src
+    assert "constexpr int P = (FMT != kFmtI8 && D % 2 == 0) ? 2 : 1;" in src
