@@ -41,6 +41,9 @@ DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), b
     "prefill_t8192": (20, 3, 1, "routed_w13", "mfma"),
     "hash_t4096": (20, 3, 1, "routed_w13", "mfma"),
     "stack43_t1": (100, 5, 1, "routed_w13", "hbm"),
+    "w2q3_t1": (1000, 50, 12, "routed_w13", "hbm"),
+    "w2q3_t64": (200, 20, 12, "routed_w13", "hbm"),
+    "w2q3_t8192": (20, 3, 1, "routed_w2", "mfma"),
 }
 # The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
 # names it, what it does there, and which algorithmic work it is priced on.
@@ -48,7 +51,7 @@ DOMINANT = {
     "decode_t1": ("moe::k_layer_small<4, 2, 1, 6>",
                   "the whole layer in one launch of one block per CU: router, shared int8 w13, top-6, routed "
                   "MXFP4 w13 + clamped SwiGLU, routed MXFP4 + shared int8 w2 and the weighted combine", "layer"),
-    "decode_t64": ("moe::k_stream_fused<8, 4>",
+    "decode_t64": ("moe::k_stream_fused<8, 4, false>",
                    "both expert stages in one launch: routed MXFP4 + shared int8 w13 with the clamped SwiGLU, "
                    "then routed MXFP4 (x routing weight) + shared int8 w2", "experts"),
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
@@ -56,6 +59,16 @@ DOMINANT = {
     "stack43_t1": ("moe::k_layer_small<4, 2, 1, 6>",
                    "one layer of the 43-layer stack in one launch (three hash-routed layers, then learned-router "
                    "layers), each layer reading the previous layer's output", "layer"),
+    "w2q3_t1": ("moe::k_stream_fused<8, 4, true>",
+                "both expert stages in one launch, the routed w2 in 3-bit blocks (14 B per 32 weights, "
+                "per-expert tables): routed MXFP4 + shared int8 w13 with the clamped SwiGLU, then routed 3-bit "
+                "(x routing weight) + shared int8 w2", "experts"),
+    "w2q3_t64": ("moe::k_stream_fused<8, 4, true>",
+                 "both expert stages in one launch, the routed w2 in 3-bit blocks (14 B per 32 weights, "
+                 "per-expert tables)", "experts"),
+    "w2q3_t8192": ("moe::k_gemm<2, 1>",
+                   "routed w2 in 3-bit blocks (per-expert tables): grouped GEMM on bf16 MFMA, x routing weight",
+                   "w2"),
 }
 # with --prefill-mfma block-scaled (moe_set_option MOE_OPTION_PREFILL_BLOCK_SCALED)
 DOMINANT_MX = ("moe::k_gemm_mx<0>",
@@ -132,7 +145,7 @@ class Hip:
         self.L.hipEventDestroy(ev)
 
 
-def algorithmic(wl, ids_np):
+def algorithmic(wl, ids_np, w2q3=False):
     """Per-step algorithmic work of the layer and of the routed w13 kernel.
 
     Bytes: every distinct routed expert's MXFP4 codes + scales (w13 and w2),
@@ -141,7 +154,8 @@ def algorithmic(wl, ids_np):
     expert GEMMs (routed slots and shared expert), router separately."""
     H, I, E, k = wl.H, wl.I, wl.E, wl.k
     w13_exp = 2 * I * (H // 2) + 2 * I * (H // 32)
-    w2_exp = H * (I // 2) + H * (I // 32)
+    # routed w2: MXFP4 (16 B of codes + 1 B E8M0 per 32) or 3-bit blocks (12 B + 2 B per 32)
+    w2_exp = H * (I // 32) * 14 if w2q3 else H * (I // 2) + H * (I // 32)
     shared = 2 * I * H + 2 * I * 4 + H * I + H * 4
     router = E * H * 4 + E * 4
     T = ids_np.shape[1]
@@ -154,8 +168,11 @@ def algorithmic(wl, ids_np):
     experts_bytes = (Dm * (w13_exp + w2_exp) + shared + (slots + T) * H * 2 + 2 * (slots + T) * I * 2
                      + (slots + T) * H * 4)
     flops_w13 = 2.0 * slots * H * 2 * I
+    flops_w2 = 2.0 * slots * I * H
+    w2_bytes = Dm * w2_exp + slots * I * 2 + slots * H * 2  # weights + h in + weighted y out (bf16)
     flops = 2.0 * slots * (H * 2 * I + I * H) + 2.0 * T * (H * 2 * I + I * H)
     return dict(distinct_experts=Dm, layer_bytes=layer_bytes, w13_bytes=w13_bytes, w13_flops=flops_w13,
+                w2_bytes=w2_bytes, w2_flops=flops_w2,
                 experts_bytes=experts_bytes,
                 layer_flops=flops, router_flops=2.0 * T * E * H)
 
@@ -372,7 +389,7 @@ def summarize(workload, outdir, commands):
     print(json.dumps(rec))
 
 
-def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids):
+def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids, fwd=None):
     """The CPU-oracle leg of one workload: time the oracle, as it stands, on a
     bounded sample of the workload's batches (whole batches at T <= 64,
     sampled rows above), and grade the GPU's first batch against it: routing
@@ -382,6 +399,7 @@ def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids):
 
     import oracle
 
+    fwd = fwd or oracle.forward
     threads = oracle.lib().or_num_threads()
     T = batches[0].shape[0]
     rows = None if T <= 64 else np.unique(np.linspace(0, T - 1, 16).astype(np.int32))
@@ -390,7 +408,7 @@ def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids):
     while True:
         xb = batches[i % len(batches)]
         tb = None if tids is None else tids[i % len(tids)]
-        r = oracle.forward(layer, xb, token_ids=tb, rows=rows)
+        r = fwd(layer, xb, token_ids=tb, rows=rows)
         if i == 0:
             first = r
         done_tokens += T if rows is None else len(rows)
@@ -413,7 +431,7 @@ def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids):
         for j, t in enumerate(sel):
             if set(gpu_ids[t].tolist()) != set(first["ids"][j].tolist()):
                 swapped += 1
-                r2 = oracle.forward(layer, batches[0], rows=np.array([t], np.int32), force_ids=gpu_ids[t][None, :])
+                r2 = fwd(layer, batches[0], rows=np.array([t], np.int32), force_ids=gpu_ids[t][None, :])
                 ref[j] = r2["out"][0]
         # every token of the batch whose set differs (near-ties only, at the bar)
         differ = [t for t in range(T) if set(gpu_ids[t].tolist()) != set(oi[t].tolist())]
@@ -469,6 +487,19 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
     dev = base_copies[0].gate_w.device
     cfg = mx.config_of(wl)
     layer, copies = workload_variant(base_host, base_copies[:C], wl)
+    # the routed w2 in 3-bit blocks (per-expert tables): host once, C device copies
+    q3 = name.startswith("w2q3_")
+    q3_host = q3_dev = None
+    if q3:
+        if "w2q3" not in _Q3:
+            t = time.perf_counter()
+            _Q3["w2q3"] = synth.make_w2q3(synth.WORKLOADS["decode_t1"], True)
+            print(f"[bench] 3-bit w2 generated in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
+        q3_host = _Q3["w2q3"]
+        c0 = torch.from_numpy(q3_host[0]).to(dev)
+        s0 = torch.from_numpy(q3_host[1].view(np.int16)).to(dev)
+        l0 = torch.from_numpy(q3_host[2]).to(dev)
+        q3_dev = [(c0, s0, l0)] + [(c0.clone(), s0.clone(), l0.clone()) for _ in range(C - 1)]
     sched = mx.forward_schedule(cfg, T, hash_layer=wl.hash_layer)
     nb = min(K + W, max(2, (1 << 27) // (T * H)))
     batches = [synth.make_tokens(wl, rep=r) for r in range(nb)]
@@ -488,16 +519,18 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
         xb = x_dev[s % nb]
         tb = None if t_dev is None else t_dev[s % nb]
         P = mx._ptr
+        w2 = (P(D.w2_codes), P(D.w2_scales)) if not q3 else tuple(P(t) for t in q3_dev[s % C])
         return (ctypes.byref(cfg), T, P(xb), P(D.gate_w), P(D.bias), P(D.logit_offset), P(tb),
                 P(D.tid2eid if tb is not None else None), 0 if D.tid2eid is None else D.tid2eid.shape[0],
-                P(D.w13_codes), P(D.w13_scales), P(D.w2_codes), P(D.w2_scales), P(D.sh_w13), P(D.sh_w13_scale),
+                P(D.w13_codes), P(D.w13_scales), *w2, P(D.sh_w13), P(D.sh_w13_scale),
                 P(D.sh_w2), P(D.sh_w2_scale), P(out), 0, P(ids_all[s % K]), P(w_all[s % K]), P(buf), buf.numel(),
                 ctypes.c_void_p(st))
 
     argv = [call_args(s, stream.cuda_stream) for s in range(max(K, W))]
+    entry = L.moe_forward_w2q3 if q3 else L.moe_forward
 
     def step(s):
-        rc = L.moe_forward(*argv[s])
+        rc = entry(*argv[s])
         if rc != 0:
             raise mx.MoEError(rc, "moe_forward")
 
@@ -533,7 +566,7 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
                 gr = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(gr, stream=cs):
                     for s in range(g0, min(K, g0 + G)):
-                        rc = L.moe_forward(*argv_g[s])
+                        rc = entry(*argv_g[s])
                         if rc != 0:
                             raise mx.MoEError(rc, "moe_forward (capture)")
                 graphs.append(gr)
@@ -551,7 +584,7 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
     total_ms = graph_ms if graph_ms is not None else eager_ms
     ms_step = total_ms / K
     ids_np = ids_all.cpu().numpy()
-    alg = algorithmic(wl, ids_np)
+    alg = algorithmic(wl, ids_np, w2q3=q3)
     # The dominant kernel's average duration: in the single-launch schedule
     # the kernel is the whole step, so it is the timed region over K steps
     # (the event pair around each eager launch adds its own recording time);
@@ -608,15 +641,27 @@ def run_workload(args, name, base_host, base_copies, K, W, C, cpu_budget):
                   "graph_ms_per_step": None if graph_ms is None else round(graph_ms / K, 5)},
     }
     if cpu_budget > 0:
-        o32 = mx.forward(cfg, x_dev[0], copies[0], token_ids=None if t_dev is None else t_dev[0], out_fp32=True,
-                         ws=ws)
-        ids0 = mx.forward(cfg, x_dev[0], copies[0], token_ids=None if t_dev is None else t_dev[0],
-                          return_routing=True, ws=ws)[1][0]
+        import oracle
+
+        tb0 = None if t_dev is None else t_dev[0]
+        if q3:
+            o32 = mx.forward_w2q3(cfg, x_dev[0], copies[0], *q3_dev[0], token_ids=tb0, out_fp32=True, ws=ws)
+            ids0 = mx.forward_w2q3(cfg, x_dev[0], copies[0], *q3_dev[0], token_ids=tb0, return_routing=True,
+                                   ws=ws)[1][0]
+            c2, s2, l2 = q3_host
+            fwd = lambda lay, xb, **kw: oracle.forward_w2q3(lay, c2, s2, l2, xb, **kw)  # noqa: E731
+        else:
+            o32 = mx.forward(cfg, x_dev[0], copies[0], token_ids=tb0, out_fp32=True, ws=ws)
+            ids0 = mx.forward(cfg, x_dev[0], copies[0], token_ids=tb0, return_routing=True, ws=ws)[1][0]
+            fwd = None
         torch.cuda.synchronize(dev)
-        cb, check = cpu_leg(layer, batches, tids, cpu_budget, o32.cpu().double().numpy(), ids0.cpu().numpy())
+        cb, check = cpu_leg(layer, batches, tids, cpu_budget, o32.cpu().double().numpy(), ids0.cpu().numpy(),
+                            fwd=fwd)
         rec["cpu_baseline"] = cb
         rec["parity"] = check
-    del x_dev, t_dev, out, ids_all, w_all, ws, buf
+    if q3:
+        rec["w2_format"] = "3-bit blocks: 12 B codes + binary16 scale per 32 weights, per-expert tables of 8 levels"
+    del x_dev, t_dev, out, ids_all, w_all, ws, buf, q3_dev
     torch.cuda.empty_cache()
     return rec
 
@@ -839,7 +884,8 @@ def run_linears(reps=40, copies=4):
     return res
 
 
-ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096", "stack43_t1"]
+ORDER = ["decode_t1", "decode_t64", "prefill_t8192", "hash_t4096", "w2q3_t1", "w2q3_t64", "stack43_t1"]
+_Q3 = {}  # the 3-bit w2 of the base layer (host), generated once
 
 
 def main():

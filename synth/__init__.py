@@ -229,6 +229,10 @@ WORKLOADS = {
     "prefill_t8192": Workload("prefill_t8192", T=8192, offset_sigma=0.5),
     # full-shape hash-routed layer, 4096 Zipf tokens
     "hash_t4096": Workload("hash_t4096", T=4096, hash_layer=True),
+    # the same layers with the routed w2 in 3-bit blocks (per-expert tables)
+    "w2q3_t1": Workload("w2q3_t1", T=1),
+    "w2q3_t64": Workload("w2q3_t64", T=64, bias_sigma=0.05),
+    "w2q3_t8192": Workload("w2q3_t8192", T=8192, offset_sigma=0.5),
     # one token through the 43-layer stack (3 hash-routed layers, then learned-router layers)
     "stack43_t1": Workload("stack43_t1", T=1),
 }
