@@ -48,7 +48,7 @@ DEFAULTS = {  # workload: steps, warmup, copies, dominant kernel (event slot), b
 # The kernel that runs in the routed-w13 slot of each schedule, as rocprofv3
 # names it, what it does there, and which algorithmic work it is priced on.
 DOMINANT = {
-    "decode_t1": ("moe::k_layer_small<4, 2, 1, 6>",
+    "decode_t1": ("moe::k_layer_small<4, 2, 1, 6, false>",
                   "the whole layer in one launch of one block per CU: router, shared int8 w13, top-6, routed "
                   "MXFP4 w13 + clamped SwiGLU, routed MXFP4 + shared int8 w2 and the weighted combine", "layer"),
     "decode_t64": ("moe::k_stream_fused<8, 4, false>",
@@ -56,13 +56,12 @@ DOMINANT = {
                    "then routed MXFP4 (x routing weight) + shared int8 w2", "experts"),
     "prefill_t8192": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
     "hash_t4096": ("moe::k_gemm<0, 0>", "routed w13: MXFP4 grouped GEMM on bf16 MFMA + clamped SwiGLU", "w13"),
-    "stack43_t1": ("moe::k_layer_small<4, 2, 1, 6>",
+    "stack43_t1": ("moe::k_layer_small<4, 2, 1, 6, false>",
                    "one layer of the 43-layer stack in one launch (three hash-routed layers, then learned-router "
                    "layers), each layer reading the previous layer's output", "layer"),
-    "w2q3_t1": ("moe::k_stream_fused<8, 4, true>",
-                "both expert stages in one launch, the routed w2 in 3-bit blocks (14 B per 32 weights, "
-                "per-expert tables): routed MXFP4 + shared int8 w13 with the clamped SwiGLU, then routed 3-bit "
-                "(x routing weight) + shared int8 w2", "experts"),
+    "w2q3_t1": ("moe::k_layer_small<4, 2, 1, 6, true>",
+                "the whole layer in one launch of one block per CU, the routed w2 in 3-bit blocks (14 B per 32 "
+                "weights, per-expert tables)", "layer"),
     "w2q3_t64": ("moe::k_stream_fused<8, 4, true>",
                  "both expert stages in one launch, the routed w2 in 3-bit blocks (14 B per 32 weights, "
                  "per-expert tables)", "experts"),

@@ -207,9 +207,10 @@ int moe_forward(const moe_config* cfg, int32_t T, const uint16_t* x, const float
  *             book level[c] = c - 4.
  *   weight = d * level[code]. The kernels round each decoded weight to bf16
  *   (nearest even) before the bf16 MFMA; every other argument is as in
- *   moe_forward. Supported: T <= 64 with H and I multiples of 1024 (one
- *   streaming launch for both stages), T > 64 with H a multiple of 256 (the
- *   grouped GEMMs); else MOE_EUNSUPPORTED. w2_codes need 4-byte alignment
+ *   moe_forward. Supported: T <= 64 with H and I multiples of 1024 (the
+ *   single-launch layer where moe_forward takes it, else one streaming
+ *   launch for both stages), T > 64 with H a multiple of 256 (the grouped
+ *   GEMMs); else MOE_EUNSUPPORTED. w2_codes need 4-byte alignment
  *   of each block (its 16-byte pointer alignment suffices), w2_levels
  *   16-byte alignment. */
 int moe_forward_w2q3(const moe_config* cfg, int32_t T, const uint16_t* x, const float* gate_w,

@@ -888,7 +888,13 @@ static int forward_impl(const moe_config* cfg, int32_t T, const uint16_t* x, con
   SkinnyArgs r2 = routed_w2_args(*cfg, T, p, w, w2_codes, w2_scales, hbuf, ybuf);
   if (q3) set_w2q3(*cfg, W2, r2);
   const int r13_blocks = p.max_tiles * r13.n_rowblocks, r2_blocks = p.max_tiles * r2.n_rowblocks;
-  const int sched = q3 ? (T <= kSmallT ? MOE_SCHED_DECODE : MOE_SCHED_LARGE) : schedule(*cfg, T, hash);
+  int sched = schedule(*cfg, T, hash);
+  if (q3) {  // the 3-bit w2 runs in the single launch, the fused streaming launch or the GEMM
+    if (sched == MOE_SCHED_SINGLE &&
+        !layer_small_supported(cfg->hidden_size, cfg->moe_intermediate, cfg->n_routed_experts, T, cfg->top_k, true))
+      sched = MOE_SCHED_DECODE;
+    if (sched == MOE_SCHED_TINY) sched = MOE_SCHED_DECODE;
+  }
   const bool tiny = sched == MOE_SCHED_TINY;
   const bool decode = sched == MOE_SCHED_DECODE;
 
@@ -910,6 +916,8 @@ static int forward_impl(const moe_config* cfg, int32_t T, const uint16_t* x, con
     la.w13s = w13_scales;
     la.w2c = w2_codes;
     la.w2s = w2_scales;
+    la.w2tab = W2.table;
+    la.w2q3 = q3 ? 1 : 0;
     la.sh13 = sh_w13;
     la.sh13s = sh_w13_scale;
     la.sh2 = sh_w2;

@@ -74,7 +74,8 @@ struct LayerShape {
   static constexpr size_t off_ycol = off_red2 + (size_t)kLayerWaves * 64 * 16;
   static constexpr size_t off_rred = off_ycol + 16 * 16 * 4;
   static constexpr size_t off_sel = off_rred + (size_t)kLayerWaves * TT * 4;
-  static constexpr size_t lds_bytes = off_sel + 16 * 4 + 16 * 4 + 16;
+  static constexpr size_t off_lv = off_sel + 16 * 4 + 16 * 4 + 16;  // 3-bit w2: 8 levels per slot
+  static constexpr size_t lds_bytes = off_lv + 16 * 8 * 4;
   static_assert(NCOL <= kXferCols && TT <= kXferTokens && I <= kXferMaxI, "hand-off buffers too small");
   static_assert(NCOL <= 16, "one 16-column MFMA tile holds every slot and the shared columns");
   static_assert(XPT == 4 || XPT == 8, "H / 512 elements per thread");
@@ -132,6 +133,18 @@ __device__ __forceinline__ void i816_mfma(const uint4& q, const unsigned char* b
   acc = mfma_16x16x32(i8x8_to_bf16x8(q.z, q.w), b1, acc);
 }
 
+// One 3-bit block (32 elements of one row: 12 code bytes in q.x .. q.z and
+// the binary16 scale h16) against 64 bytes of bf16 B at bsrc: 4 MFMAs.
+__device__ __forceinline__ void q3_16_mfma(const uint4& q, uint32_t h16, const float (&lv)[8],
+                                           const unsigned char* bsrc, f32x4_t& acc) {
+  const Q3Book bk = q3_book(lv, f16_bits_to_f32(h16));
+  bf16x8_t b[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const bf16x8_t*>(bsrc + m * 16);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc = mfma_16x16x32(q3_frag(q.x, q.y, q.z, m, bk), b[m], acc);
+}
+
 // Indices and LDS carve-up of a block.
 template <int NH, int NI, int TT, int KK>
 struct LayerBlock {
@@ -147,6 +160,7 @@ struct LayerBlock {
   int32_t* sid;         // [16]
   float* sw;            // [16]
   int* flag;            // [4]: 0 router hand-off failed, 1 h hand-off failed
+  float* lv;            // [16 slots][8] levels of each slot's expert (3-bit w2)
   __device__ __forceinline__ LayerBlock(const LayerArgs& a, unsigned char* lds) {
     b = blockIdx.x;
     tid = threadIdx.x;
@@ -170,6 +184,7 @@ struct LayerBlock {
     sid = reinterpret_cast<int32_t*>(lds + S::off_sel);
     sw = reinterpret_cast<float*>(sid + 16);
     flag = reinterpret_cast<int*>(sw + 16);
+    lv = reinterpret_cast<float*>(lds + S::off_lv);
   }
 };
 
@@ -311,8 +326,9 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
   return acc_sh;
 }
 
-// Steps 5-9.
-template <int NH, int NI, int TT, int KK>
+// Steps 5-9. Q3: the routed w2 in 3-bit blocks (a.w2c codes [E][H][I/32][12],
+// a.w2s binary16 scales [E][H][I/32], a.w2tab levels [E][8] or null).
+template <int NH, int NI, int TT, int KK, bool Q3>
 __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<NH, NI, TT, KK>& L, const Xfer& X,
                                            uint32_t ep, f32x4_t acc_sh, const uint4 (&qs2)[2 * NI]) {
   using S = LayerShape<NH, NI, TT, KK>;
@@ -321,6 +337,14 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   const int b = L.b, tid = L.tid, w = L.w, lane = L.lane, r = L.r, g = L.g, NB = L.NB;
   const int gb = L.gb, ob = L.ob, row13 = L.row13, n2 = L.n2;
   const bool ok_route = L.flag[0] == 0;
+  if (Q3 && tid < NS * 8) {  // the levels of each slot's expert, read from LDS before each use
+    const int u = tid >> 3, c = tid & 7;
+    L.lv[tid] = a.w2tab ? a.w2tab[(size_t)L.sid[u] * 8 + c] : (float)(c - 4);
+  }
+  auto slot_levels = [&](int u, float (&lv)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lv[c] = L.lv[u * 8 + c];
+  };
 
   // preloaded for wave 0's reduction and the combine
   float shs[4] = {0.f, 0.f, 0.f, 0.f};  // shared w13 scales: gate rows 8gb+2p, +1; up rows
@@ -355,11 +379,23 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   uint32_t s2[NS][N2];
   auto issue2 = [&](int u) __attribute__((always_inline)) {
     const long long e = L.sid[u];
-    const uint8_t* sb = a.w2s + e * ((long long)H * (I / 32)) + (size_t)n2 * (I / 32) + w * (I / 256);
-    load_scale_words<N2>(sb, s2[u]);
-    const uint8_t* qb = a.w2c + e * ((long long)H * (I / 2)) + (size_t)n2 * (I / 2) + w * (I / 16) + g * 16;
+    if constexpr (Q3) {  // piece i: block w*(I/256) + 4i + g of row n2 (12 bytes) and its scale
+      const long long row = e * H + n2;
+      const uint8_t* qb = a.w2c + row * (I / 32) * 12 + (size_t)(w * (I / 256) + g) * 12;
+      const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w2s) + row * (I / 32) + w * (I / 256) + g;
 #pragma unroll
-    for (int i = 0; i < N2; ++i) q2[u][i] = *reinterpret_cast<const uint4*>(qb + i * 64);
+      for (int i = 0; i < N2; ++i) {
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(qb + i * 48);
+        q2[u][i] = make_uint4(c[0], c[1], c[2], 0u);
+        s2[u][i] = sb[4 * i];
+      }
+    } else {
+      const uint8_t* sb = a.w2s + e * ((long long)H * (I / 32)) + (size_t)n2 * (I / 32) + w * (I / 256);
+      load_scale_words<N2>(sb, s2[u]);
+      const uint8_t* qb = a.w2c + e * ((long long)H * (I / 2)) + (size_t)n2 * (I / 2) + w * (I / 16) + g * 16;
+#pragma unroll
+      for (int i = 0; i < N2; ++i) q2[u][i] = *reinterpret_cast<const uint4*>(qb + i * 64);
+    }
   };
 #pragma unroll
   for (int j = 0; j < P && j < NS; ++j) issue13(j);
@@ -431,12 +467,23 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   for (int u = 0; u < kPre; ++u)
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
-      const float sc = e8m0_scale_operand((s2[u][i] >> (8 * g)) & 0xff);
-      const uint32_t d[4] = {q2[u][i].x, q2[u][i].y, q2[u][i].z, q2[u][i].w};
+      if constexpr (Q3) {
+        float lv[8];
+        slot_levels(u, lv);
+        const Q3Book bk = q3_book(lv, f16_bits_to_f32(s2[u][i]));
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        c2[u][i][m] = fp4x8_to_bf16x8(d[m], sc);
-        asm volatile("" : "+v"(c2[u][i][m]));
+        for (int m = 0; m < 4; ++m) {
+          c2[u][i][m] = q3_frag(q2[u][i].x, q2[u][i].y, q2[u][i].z, m, bk);
+          asm volatile("" : "+v"(c2[u][i][m]));
+        }
+      } else {
+        const float sc = e8m0_scale_operand((s2[u][i] >> (8 * g)) & 0xff);
+        const uint32_t d[4] = {q2[u][i].x, q2[u][i].y, q2[u][i].z, q2[u][i].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          c2[u][i][m] = fp4x8_to_bf16x8(d[m], sc);
+          asm volatile("" : "+v"(c2[u][i][m]));
+        }
       }
     }
 
@@ -502,7 +549,13 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
           acc2[(u * N2 + i) & 3] = mfma_16x16x32(c2[u][i][m], *reinterpret_cast<const bf16x8_t*>(bsrc + i * 256 + m * 16),
                                                  acc2[(u * N2 + i) & 3]);
       } else {
-        mx16_mfma(q2[u][i], (s2[u][i] >> (8 * g)) & 0xff, bsrc + i * 256, acc2[(u * N2 + i) & 3]);
+        if constexpr (Q3) {
+          float lv[8];
+          slot_levels(u, lv);
+          q3_16_mfma(q2[u][i], s2[u][i], lv, bsrc + i * 256, acc2[(u * N2 + i) & 3]);
+        } else {
+          mx16_mfma(q2[u][i], (s2[u][i] >> (8 * g)) & 0xff, bsrc + i * 256, acc2[(u * N2 + i) & 3]);
+        }
       }
     }
   }
@@ -567,7 +620,7 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
   }
 }
 
-template <int NH, int NI, int TT, int KK>
+template <int NH, int NI, int TT, int KK, bool Q3>
 __global__ __launch_bounds__(kLayerThreads) void k_layer_small(LayerArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const LayerBlock<NH, NI, TT, KK> L(a, lds);
@@ -575,7 +628,7 @@ __global__ __launch_bounds__(kLayerThreads) void k_layer_small(LayerArgs a) {
   const Xfer X(a.xfer, ep & 1);
   uint4 qs2[2 * NI];
   const f32x4_t acc_sh = layer_head(a, L, X, qs2);
-  layer_tail(a, L, X, ep, acc_sh, qs2);
+  layer_tail<NH, NI, TT, KK, Q3>(a, L, X, ep, acc_sh, qs2);
 }
 
 namespace {
@@ -586,15 +639,17 @@ using LayerKernel = void (*)(LayerArgs);
 // a CU (the design is one block per CU; two on one CU would leave another
 // idle).
 template <int NH, int NI, int TT, int KK>
-LayerKernel pick(size_t* lds) {
+LayerKernel pick(size_t* lds, bool q3) {
   *lds = std::max(LayerShape<NH, NI, TT, KK>::lds_bytes, (size_t)81 * 1024);
-  return &k_layer_small<NH, NI, TT, KK>;
+  return q3 ? &k_layer_small<NH, NI, TT, KK, true> : &k_layer_small<NH, NI, TT, KK, false>;
 }
 
-LayerKernel layer_kernel(int H, int I, int T, int k, size_t* lds) {
+LayerKernel layer_kernel(int H, int I, int T, int k, size_t* lds, bool q3) {
   if (k != 6) return nullptr;
-  if (H == 4096 && I == 2048) return T == 1 ? pick<4, 2, 1, 6>(lds) : T == 2 ? pick<4, 2, 2, 6>(lds) : nullptr;
-  if (H == 2048 && I == 1024) return T == 1 ? pick<2, 1, 1, 6>(lds) : T == 2 ? pick<2, 1, 2, 6>(lds) : nullptr;
+  if (H == 4096 && I == 2048)
+    return T == 1 ? pick<4, 2, 1, 6>(lds, q3) : T == 2 ? pick<4, 2, 2, 6>(lds, q3) : nullptr;
+  if (H == 2048 && I == 1024)
+    return T == 1 ? pick<2, 1, 1, 6>(lds, q3) : T == 2 ? pick<2, 1, 2, 6>(lds, q3) : nullptr;
   return nullptr;
 }
 
@@ -630,9 +685,9 @@ int layer_grid(int H, int I, int E) { return std::max(E, std::max(I / 8, H / 16)
 
 }  // namespace
 
-bool layer_small_supported(int H, int I, int E, int T, int k) {
+bool layer_small_supported(int H, int I, int E, int T, int k, bool w2q3) {
   size_t lds = 0;
-  LayerKernel kern = layer_kernel(H, I, T, k, &lds);
+  LayerKernel kern = layer_kernel(H, I, T, k, &lds, w2q3);
   if (!kern || E < k || E > 256) return false;
   const int grid = layer_grid(H, I, E);
   return grid <= kXferBlocks && resident_blocks(kern, lds) >= grid;
@@ -640,7 +695,7 @@ bool layer_small_supported(int H, int I, int E, int T, int k) {
 
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st) {
   size_t lds = 0;
-  LayerKernel kern = layer_kernel(a.H, a.I, a.T, a.k, &lds);
+  LayerKernel kern = layer_kernel(a.H, a.I, a.T, a.k, &lds, a.w2q3 != 0);
   if (!kern) return hipErrorInvalidValue;
   const int grid = layer_grid(a.H, a.I, a.E);
   if (grid > kXferBlocks || resident_blocks(kern, lds) < grid) return hipErrorInvalidValue;

@@ -304,8 +304,10 @@ struct LayerArgs {
   const float* logit_offset;   // [E] or null
   const uint8_t* w13c;         // [E][2I][H/2]
   const uint8_t* w13s;         // [E][2I][H/32]
-  const uint8_t* w2c;          // [E][H][I/2]
-  const uint8_t* w2s;          // [E][H][I/32]
+  const uint8_t* w2c;          // [E][H][I/2] (3-bit: [E][H][I/32][12])
+  const uint8_t* w2s;          // [E][H][I/32] (3-bit: binary16 [E][H][I/32])
+  const float* w2tab;          // 3-bit: levels [E][8], null for the uniform book
+  int w2q3;                    // routed w2 in 3-bit blocks
   const int8_t* sh13;          // [2I][H]
   const float* sh13s;          // [2I]
   const int8_t* sh2;           // [H][I]
@@ -322,7 +324,7 @@ struct LayerArgs {
 };
 // Whether the single-launch layer has a kernel for this shape whose whole
 // grid the current device holds at once.
-bool layer_small_supported(int H, int I, int E, int T, int k);
+bool layer_small_supported(int H, int I, int E, int T, int k, bool w2q3 = false);
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

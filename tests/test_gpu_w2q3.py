@@ -6,8 +6,9 @@ every block (uniform) or a table per expert (adaptive), page
 code bytes, a binary16 scale). Against the oracle's or_forward_w2q3 at the
 usual bar (the kernels round each decoded weight, scale x level, to bf16:
 at most 2^-9 relative per weight, far inside rel L2 5e-3):
-  * decode sizes (one streaming launch), T = 1, 2, 5, 17, 64, learned and
-    hash routing, uniform and tables, every row;
+  * decode sizes, T = 1, 2 (the single-launch layer), 5, 17, 64 (one
+    streaming launch), learned and hash routing, uniform and tables, every
+    row;
   * the grouped GEMM, T = 65, 300 and 1000 (several tiles per expert and
     ragged last tiles), every row;
   * the full-shape layer at T = 1, 64 (sampled rows) and 8192 (32
@@ -94,7 +95,7 @@ def test_w2q3_gemm(T, tables):
     _run(MID, tables, T, 420 + T)
 
 
-@pytest.mark.parametrize("T", [1, 17, 300])
+@pytest.mark.parametrize("T", [1, 2, 17, 300])
 def test_w2q3_hash(T):
     _run(MIDH, True, T, 440 + T, hash_layer=True)
 
@@ -127,11 +128,11 @@ def test_w2q3_equals_mxfp4_when_exact():
     D = mx.DeviceLayer.from_host(L, DEV)
     dq = (torch.from_numpy(qc.reshape(E, H, -1)).to(DEV), torch.from_numpy(qs.view(np.int16).reshape(E, H, -1)).to(DEV))
     cfg = mx.config_of(wl)
-    for T in (3, 64, 200):
+    for T in (1, 2, 3, 64, 200):
         print(f"[w2q3 == mxfp4 T={T}]", flush=True)
         x = mx.bf16_from_numpy(synth.make_tokens(wl, rep=470 + T, T=T), DEV)
         a = mx.forward_w2q3(cfg, x, D, *dq, None, out_fp32=True)
-        # the MXFP4 layer in the same schedule family (T >= 3: streaming or GEMM)
+        # the MXFP4 layer in the same schedule (single launch, streaming launch or GEMM)
         b = mx.forward(cfg, x, D, out_fp32=True)
         torch.cuda.synchronize()
         assert torch.equal(a, b), T
