@@ -851,7 +851,7 @@ def run_linears(reps=40, copies=4):
     stream = torch.cuda.current_stream(dev)
     res = {}
     for i, (name, (K, N, G)) in enumerate(LINEARS.items()):
-        q, sc = synth.int8_normal(0, 12, i, G * N, K, 0.02)
+        q, sc = synth.int8_normal(0, synth.S_LINEAR, i, G * N, K, 0.02)
         qs = [torch.from_numpy(q).to(dev) for _ in range(copies)]
         ss = [torch.from_numpy(sc).to(dev) for _ in range(copies)]
         wbytes = G * N * K + G * N * 4

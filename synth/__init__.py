@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 # Counter streams: one per tensor kind, so each tensor is regenerable alone.
 S_W13, S_W2, S_SH_W13, S_SH_W2, S_GATE, S_BIAS, S_OFFSET, S_TOKENS, S_TIDS, S_TID2EID = range(1, 11)
 S_STACK_PERM = 11
-S_W2Q3, S_Q3TAB = 12, 13  # routed w2 in 3-bit blocks, their per-expert tables  # per-layer expert order of a layer stack
+S_W2Q3, S_Q3TAB = 12, 13  # routed w2 in 3-bit blocks, their per-expert tables
+S_LINEAR = 14  # int8 attention projections (sub-sequence: the projection)  # per-layer expert order of a layer stack
 
 _lib = None
 

@@ -40,7 +40,7 @@ def _weights(name):
     if name not in _W:
         K, N, G = SHAPES[name]
         sub = list(SHAPES).index(name)
-        q, s = synth.int8_normal(0, 12, sub, G * N, K, 0.02)
+        q, s = synth.int8_normal(0, synth.S_LINEAR, sub, G * N, K, 0.02)
         _W[name] = (q, s, torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV))
     return _W[name]
 
