@@ -840,8 +840,9 @@ LINEARS = {"fused_wqa_wkv": (4096, 1536, 1), "wq_b": (1024, 32768, 1), "wo_a": (
 def run_linears(reps=40, copies=4):
     """moe_linear_w8a16 on each projection at T = 1, 64 (bound by the int8
     weights' bytes) and 8192 (bf16 MFMA), weights rotated through `copies`
-    copies (together beyond the last-level cache), events around each call
-    on the launch stream; the mean per call."""
+    copies (together beyond the last-level cache): `reps` calls captured in
+    one HIP graph, replayed between events on the launch stream (so that the
+    host's call overhead is not timed); the mean per call."""
     import torch
 
     import mxfp4_moe_expert_amd as mx
@@ -862,14 +863,23 @@ def run_linears(reps=40, copies=4):
             n = reps if T <= 64 else 10
             for r in range(3):
                 mx.linear_w8a16(x, qs[r % copies], ss[r % copies], groups=G, out=out)
+            torch.cuda.synchronize(dev)
+            cs = torch.cuda.Stream(dev)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cs):
+                with torch.cuda.graph(gr, stream=cs):
+                    for r in range(n):
+                        mx.linear_w8a16(x, qs[r % copies], ss[r % copies], groups=G, out=out)
+            torch.cuda.synchronize(dev)
+            gr.replay()  # warm replay
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize(dev)
             e0.record(stream)
-            for r in range(n):
-                mx.linear_w8a16(x, qs[r % copies], ss[r % copies], groups=G, out=out)
+            gr.replay()
             e1.record(stream)
             torch.cuda.synchronize(dev)
             us = e0.elapsed_time(e1) * 1e3 / n
+            del gr
             if T <= 64:
                 b = wbytes + T * G * (K + N) * 2
                 res[name][f"T{T}"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),

@@ -226,8 +226,7 @@ int moe_forward_w2q3(const moe_config* cfg, int32_t T, const uint16_t* x, const 
  * scale per output channel, 16-bit activations; page "deepseek-v4-mxfp4-int8
  * config.json", quantization_config, config group linears_w8a16, targets
  * attn.fused_wqa_wkv, attn.wq_b, attn.wo_a, attn.wo_b, attn.indexer.wq_b,
- * attn.indexer.compressor.wkv), on the same kernels as the shared expert's
- * w2: y = x W^T with W[n][k] = scale[n] * q[n][k].
+ * attn.indexer.compressor.wkv): y = x W^T with W[n][k] = scale[n] * q[n][k].
  *   groups > 1: a grouped (block-diagonal) projection such as wo_a
  *   (o_groups): group g maps input features [g K, (g+1) K) to output
  *   features [g N, (g+1) N) with its own rows q[g N .. g N + N) and scales.
@@ -235,8 +234,13 @@ int moe_forward_w2q3(const moe_config* cfg, int32_t T, const uint16_t* x, const 
  *   q     [groups N][K] int8;  scale [groups N] f32
  *   out   [T][groups N] bf16 (out_is_fp32 = 0) or f32
  *   workspace: moe_linear_workspace_size(T, K, N, groups) bytes, 256-byte
- *   aligned, zero-filled before its first use (its counters are left at zero
- *   by every call); calls sharing one must be ordered on one stream.
+ *   aligned, zero-filled before its first use (its counters, bytes 0 .. 36
+ *   and 256 .. 262399, are left at zero by every call; at T <= 64 the rest
+ *   holds partial sums, written before they are read); calls sharing one
+ *   must be ordered on one stream.
+ *   T <= 64: one launch that splits K over blocks of 64 rows (the last block
+ *   of each row block adds the slices in order: deterministic); T > 64: the
+ *   shared expert's grouped GEMM, one launch per group.
  * Supported: K a multiple of 128, N of 256 (each at most 65536), groups at
  * most 64, 0 <= T <= 65536. Errors as for moe_forward. */
 size_t moe_linear_workspace_size(int32_t T, int32_t K, int32_t N, int32_t groups);

@@ -759,13 +759,24 @@ int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_w
   return MOE_OK;
 }
 
+// the split-K linear's arrival words: one per 64 rows of the largest
+// projection (64 groups x 65536 rows), from byte 256
+constexpr size_t kLinearPartOffset = 256 + (size_t)64 * 65536 / 64 * 4;
+
 size_t moe_linear_workspace_size(int32_t T, int32_t K, int32_t N, int32_t groups) {
   if (T < 0 || T > kMaxT || K <= 0 || N <= 0 || groups <= 0 || K % 128 || N % 256 || K > 65536 || N > 65536 ||
       groups > 64)
     return 0;
-  // counters (the GEMM's tile queue, the streaming pass's unit counter), then the streaming pass's
-  // fp32 outputs
-  return 256 + align256((size_t)(T <= kSmallT ? T : 0) * groups * N * 4);
+  // counters (the GEMM's tile queue), then at decode sizes the split-K pass's
+  // arrival words and its fp32 partial sums [split][T][groups*N]. The
+  // arrival words sit at a fixed place, sized for the largest projection,
+  // so that no call's partial sums land where another shape's words are
+  // (the words must be zero before a launch; each call leaves its own zero).
+  if (T == 0 || T > kSmallT) return 256;
+  const int ks = linear_dec_ks(T, K, N, groups);
+  if (ks == 0) return 0;
+  const size_t rows = (size_t)groups * N;
+  return kLinearPartOffset + align256((size_t)(K / ks) * T * rows * 4);
 }
 
 int moe_linear_w8a16(int32_t T, int32_t K, int32_t N, int32_t groups, const uint16_t* x, const int8_t* q,
@@ -776,7 +787,8 @@ int moe_linear_w8a16(int32_t T, int32_t K, int32_t N, int32_t groups, const uint
   if (need == 0) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !q || !scale || !out || !workspace) return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255))
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
     return MOE_EINVAL;
   if (workspace_bytes < need) return MOE_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -807,35 +819,22 @@ int moe_linear_w8a16(int32_t T, int32_t K, int32_t N, int32_t groups, const uint
     }
     return MOE_OK;
   }
-  // batched decode: the streaming int8 pass (fp32 rows), then one cast of all groups' outputs
-  float* y = at<float>(workspace, 256);
-  for (int g = 0; g < groups; ++g) {
-    SkinnyArgs b;
-    memset(&b, 0, sizeof(b));
-    b.T = T;
-    b.routed = 0;
-    b.flags = device_flags();
-    b.wq = reinterpret_cast<const uint8_t*>(q + (size_t)g * N * K);
-    b.row_scale = scale + (size_t)g * N;
-    b.K = K;
-    b.half = 0;
-    b.rows = N;
-    b.n_rowblocks = N / 256;
-    b.tile_n = shared_stream_tile(T, K);
-    b.n_tiles_grid = (T + b.tile_n - 1) / b.tile_n;
-    b.act = x + (size_t)g * K;
-    b.act_ld = ldx;
-    b.yout = y + (size_t)g * N;
-    b.yout_ld = ldo;
-    SkinnyArgs none;
-    memset(&none, 0, sizeof(none));
-    int rc = status(launch_fill_zero(counters + kQueueInts, 4, st));  // the pass's unit counter
-    if (rc) return rc;
-    rc = status(launch_stream(kW2, none, 0, &b, b.n_tiles_grid * b.n_rowblocks, counters + kQueueInts, st));
-    if (rc) return rc;
-  }
-  CombineArgs cb{T, ldo, 0, nullptr, y, out, out_is_fp32 ? 1 : 0, 0};
-  return status(launch_combine(cb, st));
+  // decode sizes: every group in one split-K launch
+  LinearDecArgs a;
+  a.T = T;
+  a.K = K;
+  a.N = N;
+  a.G = groups;
+  a.ks = linear_dec_ks(T, K, N, groups);
+  a.split = K / a.ks;
+  a.x = x;
+  a.q = q;
+  a.scale = scale;
+  a.out = out;
+  a.out_is_fp32 = out_is_fp32 ? 1 : 0;
+  a.count = at<int32_t>(workspace, 256);
+  a.part = at<float>(workspace, kLinearPartOffset);
+  return status(launch_linear_dec(a, st));
 }
 
 int moe_forward_schedule(const moe_config* cfg, int32_t T, int32_t hash) {

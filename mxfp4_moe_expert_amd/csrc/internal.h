@@ -325,6 +325,24 @@ struct LayerArgs {
 // Whether the single-launch layer has a kernel for this shape whose whole
 // grid the current device holds at once.
 bool layer_small_supported(int H, int I, int E, int T, int k, bool w2q3 = false);
+
+// int8 per-channel linear at decode sizes (linear.hip): x [T][G*K] bf16,
+// q [G*N][K] int8, scale [G*N] -> out [T][G*N]; blocks of 64 rows x a K slice
+// of ks (linear_dec_ks), split = K / ks slices added by the last block of
+// each row block.
+struct LinearDecArgs {
+  int T, K, N, G;
+  int ks, split;
+  const uint16_t* x;
+  const int8_t* q;
+  const float* scale;
+  void* out;
+  int out_is_fp32;
+  float* part;  // [split][T][G*N] fp32 partial sums (split > 1)
+  int* count;   // [G*N/64] arrivals per row block: zero before the launch, left zero
+};
+int linear_dec_ks(int T, int K, int N, int G);  // 0: not supported
+hipError_t launch_linear_dec(const LinearDecArgs& a, hipStream_t st);
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
