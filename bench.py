@@ -351,7 +351,7 @@ def summarize(workload, outdir, commands):
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.2f}% |")
         tag = workload + ("_block_scaled" if PREFILL_MX[0] else "")
-    with open(os.path.join(ROOT, "profiles", f"moe_forward_{tag}_kernels.md"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", f"moe_forward_{tag}_kernels.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     try:
         rb, rn = _read_bytes(_find(outdir, "pmc_read", "counter_collection.csv"), kname)

@@ -87,6 +87,8 @@ typedef struct moe_config {
   int32_t moe_intermediate;     /* I: moe_intermediate_size, 2048 */
   float routed_scaling_factor;  /* 1.5 */
   float swiglu_limit;           /* 10.0 */
+  int32_t norm_topk_prob;       /* 1: the top-k scores are renormalised (the model's true);
+                                   0 is not supported (MOE_EUNSUPPORTED) */
 } moe_config;
 
 enum {

@@ -44,13 +44,14 @@ class MoeConfig(ctypes.Structure):
     """Mirror of ``moe_config`` (names of the checkpoint's config.json)."""
     _fields_ = [("hidden_size", ctypes.c_int32), ("n_routed_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("moe_intermediate", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
+                ("routed_scaling_factor", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
+                ("norm_topk_prob", ctypes.c_int32)]
 
 
 def config(hidden_size=4096, n_routed_experts=256, top_k=6, moe_intermediate=2048,
-           routed_scaling_factor=1.5, swiglu_limit=10.0) -> MoeConfig:
+           routed_scaling_factor=1.5, swiglu_limit=10.0, norm_topk_prob=1) -> MoeConfig:
     return MoeConfig(hidden_size, n_routed_experts, top_k, moe_intermediate, routed_scaling_factor,
-                     swiglu_limit)
+                     swiglu_limit, norm_topk_prob)
 
 
 def config_of(wl) -> MoeConfig:

@@ -32,6 +32,7 @@ bool cfg_ok(const moe_config* c) {
   if (k < 1 || k > kMaxTopK || E < k || E > kMaxExperts) return false;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
   if (!(c->swiglu_limit == c->swiglu_limit)) return false;
+  if (c->norm_topk_prob != 1) return false;  // the weights are always renormalised over the top-k
   return true;
 }
 

@@ -55,6 +55,8 @@ def test_workspace_size_host_logic():
     assert L.moe_workspace_size(ctypes.byref(cfg), -1) == 0
     assert L.moe_workspace_size(ctypes.byref(cfg), 65537) == 0
     assert L.moe_workspace_size(None, 1) == 0
+    # norm_topk_prob: only the model's renormalised weights are supported
+    assert L.moe_workspace_size(ctypes.byref(_cfg(norm_topk_prob=0)), 1) == 0
 
 
 def test_invalid_arguments_are_rejected_before_launch():
