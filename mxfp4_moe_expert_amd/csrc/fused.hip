@@ -498,21 +498,29 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     }
   }
 
-  // 7. every block's h slices: poll the columns into LDS
+  // 7. every block's h slices: poll the columns into LDS. A piece whose four
+  //    words are all in is kept and not read again (the polls of 256 blocks
+  //    compete with the w2 weight stream for the memory system)
   {
     constexpr int n16 = I / 8;
     constexpr int nact = NCOL * n16;
     constexpr int PER = (nact + kLayerThreads - 1) / kLayerThreads;
     u32x4_t v[PER];
+    bool got[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) got[i] = false;
     int spins = 0;
     while (true) {
       bool rdy = true;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int ii = min(tid + i * kLayerThreads, nact - 1);
-        const int c = ii / n16, o = ii - c * n16;
-        v[i] = load_agent_u32x4(X.h + c * (kXferMaxI / 2) + 4 * o);
-        rdy = rdy && v[i][0] != 0 && v[i][1] != 0 && v[i][2] != 0 && v[i][3] != 0;
+        if (!got[i]) {
+          const int ii = min(tid + i * kLayerThreads, nact - 1);
+          const int c = ii / n16, o = ii - c * n16;
+          v[i] = load_agent_u32x4(X.h + c * (kXferMaxI / 2) + 4 * o);
+          got[i] = v[i][0] != 0 && v[i][1] != 0 && v[i][2] != 0 && v[i][3] != 0;
+        }
+        rdy = rdy && got[i];
       }
       if (rdy) break;
       if (++spins >= kPollLimit) {
