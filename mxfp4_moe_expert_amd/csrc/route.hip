@@ -197,12 +197,28 @@ __global__ __launch_bounds__(kDecExperts * 64) void k_router_dec(RouterArgs a) {
       acc[t] = s;
     }
   }
-  float mine = 0.0f;
+  // transposed reduction of the 8 token partials over the wave: each
+  // exchange halves the values a lane holds (8 -> 4 -> 2 -> 1 at lane
+  // distances 32, 16, 8), then 4, 2, 1 finish one token per group of 8
+  // lanes (11 shuffles in place of 8 x 6)
+  const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
+  float b4[4], b2[2];
 #pragma unroll
-  for (int t = 0; t < kDecTokens; ++t) {
-    const float v = wave_sum(acc[t]);
-    mine = lane == t ? v : mine;
+  for (int i = 0; i < 4; ++i) {
+    const float keep = h32 ? acc[i + 4] : acc[i], send = h32 ? acc[i] : acc[i + 4];
+    b4[i] = keep + __shfl_xor(send, 32);
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = h16 ? b4[i + 2] : b4[i], send = h16 ? b4[i] : b4[i + 2];
+    b2[i] = keep + __shfl_xor(send, 16);
+  }
+  float b1 = (h8 ? b2[1] : b2[0]) + __shfl_xor(h8 ? b2[0] : b2[1], 8);
+  b1 += __shfl_xor(b1, 4);
+  b1 += __shfl_xor(b1, 2);
+  b1 += __shfl_xor(b1, 1);
+  // lane l holds token (l >> 3) & 7; lane q < 8 takes token q from lane 8q
+  const float mine = __shfl(b1, (lane & 7) * 8);
   if (e < a.E && lane < nt) store_score(a, t0 + lane, e, mine + (a.logit_offset ? a.logit_offset[e] : 0.0f));
 }
 
