@@ -140,14 +140,19 @@ struct GemmA {
 template <int FMT, int MB>
 __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x4_t (&w)[kRB],
                                              const unsigned char* lds_s, const uint32_t (&soff)[kRB], int st,
-                                             const unsigned char* abase, const float (&lv)[8]) {
+                                             const unsigned char* abase, const float* lv_lds) {
   constexpr int kKK = GemmCfg<FMT>::kKK;
   uint32_t sc[kRB];
   gemm_scales<FMT>(lds_s, soff, st, sc);
   Q3Book book[kRB] = {};
   if constexpr (FMT == kFmtQ3) {
+    {
+      float lv[8];  // the tile's expert's levels, from LDS (broadcast reads)
 #pragma unroll
-    for (int b = 0; b < kRB; ++b) book[b] = q3_book(lv, f16_bits_to_f32(sc[b]));
+      for (int c = 0; c < 8; ++c) lv[c] = lv_lds[c];
+#pragma unroll
+      for (int b = 0; b < kRB; ++b) book[b] = q3_book(lv, f16_bits_to_f32(sc[b]));
+    }
   }
   // int8 weights are unpacked here, in their stage: without the empty asm
   // the compiler starts unpacking them right after their load, a stage
@@ -188,7 +193,7 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
                                           const unsigned char* abase0, const unsigned char* abase1, int nst,
                                           int ncols, int pos0, int nt, int wn, int g, int r,
                                           const StoreScales& store_scales, const int (&slot_r)[kMB],
-                                          const float (&lv)[8]) {
+                                          const float* lv) {
   f32x4_t acc[kRB][MB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b)
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   // MXFP4: [256 local rows][K/32 + 4] E8M0 bytes; 3-bit: [256][K/16 + 4] bytes of binary16 scales
   extern __shared__ __align__(16) unsigned char lds_s[];
   __shared__ int grabbed;
+  __shared__ float lds_lv[8];
 
   // Persistent: at most the blocks that fit at once, each walking tiles.
   // XCD-aware order: XCD x (blocks b with b % 8 == x) owns a contiguous run
@@ -366,8 +372,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     // weight rows of the wave's 2 row blocks (w13: 16 gate rows and the
     // matching 16 up rows), as 32-bit offsets from the expert's (uniform) bases
     const uint8_t* qe = p.wq + (long long)e * p.q_expert_stride;
-    float lv[8] = {};  // 3-bit: the expert's levels
-    if constexpr (FMT == kFmtQ3) q3_levels(p.table, e, lv);
+    // 3-bit: the expert's levels to LDS (read after the K loop's first
+    // barrier; the previous tile's readers passed the barrier that ends it)
+    if constexpr (FMT == kFmtQ3) {
+      if (tid < 8) lds_lv[tid] = p.table ? p.table[(size_t)e * 8 + tid] : (float)(tid - 4);
+    }
+    const float* lv = lds_lv;
     uint32_t qoff[kRB], soff[kRB];
 #pragma unroll
     for (int b = 0; b < kRB; ++b) {

@@ -72,3 +72,26 @@ def test_linear_w8a16_arguments():
     q = torch.zeros(256, 128, dtype=torch.int8, device=DEV)
     sc = torch.ones(256, dtype=torch.float32, device=DEV)
     assert mx.linear_w8a16(x, q, sc).shape == (0, 256)
+
+
+def test_linear_w8a16_interleaved_and_repeatable():
+    """At decode sizes the split-K pass counts each row block's slices in
+    arrival words that every call leaves at zero: calls of different shapes
+    (split 16, 1 and 4 slices, grouped and plain) interleaved on one
+    workspace give the same bits as the same calls alone, twice over."""
+    cases = [("fused_wqa_wkv", 1), ("wq_b", 1), ("wo_a", 1), ("indexer_compressor_wkv", 5), ("wo_b", 33)]
+    xs, first = {}, {}
+    for name, T in cases:
+        K, N, G = SHAPES[name]
+        xs[name] = mx.bf16_from_numpy(
+            synth.normal_bf16(0, synth.S_TOKENS, 750 + T, T * G * K).reshape(T, G * K), DEV)
+    for rep in range(2):
+        for name, T in cases:
+            K, N, G = SHAPES[name]
+            _, _, qd, sd = _weights(name)
+            out = mx.linear_w8a16(xs[name], qd, sd, groups=G, out_fp32=True)
+            torch.cuda.synchronize()
+            if rep == 0:
+                first[name] = out.clone()
+            else:
+                assert torch.equal(out, first[name]), name
