@@ -53,6 +53,12 @@ namespace moe {
 constexpr int kStreamThreads = 512;
 constexpr int kUnitRows = 256;  // weight rows per unit
 
+// LDS row of a unit's scales: the row's E8M0 bytes (K/32) or binary16 scales
+// (K/16), padded by 16 bytes so that the 16 rows a wave's lanes read in one
+// instruction fall in different banks (unpadded, rows 64 or 128 bytes apart
+// shared two banks).
+__host__ __device__ inline int stream_scale_row(int K, bool q3) { return (q3 ? K / 16 : K / 32) + 16; }
+
 template <int FMT>
 struct StreamStage {
   uint4 q[FMT == kFmtI8 ? 2 : 1];
@@ -123,8 +129,14 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
   const int K = p.K, S = K >> 7, n16 = K >> 3, row_bytes = 2 * K + 16;
   const int nrb = p.n_rowblocks;
   // scale bytes per row (a multiple of 4): one E8M0 byte or one binary16 per 32 weights
-  const int srow = FMT == kFmtQ3 ? K / 16 : K / 32;
-  unsigned char* lds_sc = lds + (size_t)p.tile_n * row_bytes;  // [256 rows][srow]
+  const int srow = FMT == kFmtQ3 ? K / 16 : K / 32;          // scale bytes per weight row
+  const int srow_l = stream_scale_row(K, FMT == kFmtQ3);      // its padded LDS row
+  unsigned char* lds_sc = lds + (size_t)p.tile_n * row_bytes;  // [256 rows][srow_l]
+  // LDS place of piece i (of `piece` bytes) of the unit's scales
+  auto sc_dst = [&](int i, int piece) {
+    const int row = (i * piece) / srow;
+    return lds_sc + (size_t)row * srow_l + (i * piece - row * srow);
+  };
   const bool sc16 = srow % 16 == 0;                            // rows of whole 16-byte pieces
   const int nsc = FMT != kFmtI8 ? kUnitRows * srow / (sc16 ? 16 : 4) : 0;
   // this lane's two block rows (of the unit's 256)
@@ -247,13 +259,13 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const int i = tid + j * kStreamThreads;
-          if (i < nsc) *reinterpret_cast<u32x4_t*>(lds_sc + i * 16) = sv[j];
+          if (i < nsc) *reinterpret_cast<u32x4_t*>(sc_dst(i, 16)) = sv[j];
         }
         for (int i = tid + NS * kStreamThreads; i < nsc; i += kStreamThreads)
-          *reinterpret_cast<u32x4_t*>(lds_sc + i * 16) = *reinterpret_cast<const u32x4_t*>(sc_src(x, i, 16));
+          *reinterpret_cast<u32x4_t*>(sc_dst(i, 16)) = *reinterpret_cast<const u32x4_t*>(sc_src(x, i, 16));
       } else {
         for (int i = tid; i < nsc; i += kStreamThreads)
-          *reinterpret_cast<uint32_t*>(lds_sc + i * 4) = *reinterpret_cast<const uint32_t*>(sc_src(x, i, 4));
+          *reinterpret_cast<uint32_t*>(sc_dst(i, 4)) = *reinterpret_cast<const uint32_t*>(sc_src(x, i, 4));
       }
     }
     const int nact = x.ncols * n16;
@@ -302,8 +314,8 @@ __device__ __forceinline__ void stream_loop(const SkinnyArgs& p, int lo, int hi,
     const bool live = r < cur.ncols;
     const unsigned char* bcol = lds + (live ? r : 0) * row_bytes + g * (FMT != kFmtI8 ? 64 : 32);
     // the scale of block 4 st + g of each row (MXFP4: a byte, 3-bit: a binary16)
-    const unsigned char* scA = lds_sc + (size_t)brA * srow + g * (FMT == kFmtQ3 ? 2 : 1);
-    const unsigned char* scB = lds_sc + (size_t)brB * srow + g * (FMT == kFmtQ3 ? 2 : 1);
+    const unsigned char* scA = lds_sc + (size_t)brA * srow_l + g * (FMT == kFmtQ3 ? 2 : 1);
+    const unsigned char* scB = lds_sc + (size_t)brB * srow_l + g * (FMT == kFmtQ3 ? 2 : 1);
     // byte offset in the column of fragment kk (the lane's K-values of it)
     auto kbyte = [](int kk) { return FMT != kFmtI8 ? kk * 16 : (kk >> 1) * 128 + (kk & 1) * 16; };
     auto dec_of = [&](const unsigned char* sc, int st) __attribute__((always_inline)) {
@@ -563,7 +575,7 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
       (b_blocks > 0 && (b.tile_n > 16 || b.tile_n < 1)))
     return hipErrorInvalidValue;
   size_t lds = 0;
-  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / 32);
+  if (a_blocks > 0) lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)stream_scale_row(a.K, false);
   if (b_blocks > 0) {
     const size_t lb = (size_t)b.tile_n * (2 * (size_t)b.K + 16);
     lds = lb > lds ? lb : lds;
@@ -585,7 +597,7 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
 static size_t stream_lds(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks) {
   size_t lds = 0;
   if (a_blocks > 0)
-    lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)(a.K / (a.fmt == kFmtQ3 ? 16 : 32));
+    lds = (size_t)a.tile_n * (2 * (size_t)a.K + 16) + kUnitRows * (size_t)stream_scale_row(a.K, a.fmt == kFmtQ3);
   if (b_blocks > 0) {
     const size_t lb = (size_t)b.tile_n * (2 * (size_t)b.K + 16);
     lds = lb > lds ? lb : lds;
