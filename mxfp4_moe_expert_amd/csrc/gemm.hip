@@ -185,6 +185,70 @@ __device__ __forceinline__ void gemm_compute(f32x4_t (&acc)[kRB][MB], const u32x
   }
 }
 
+// Shared w2 + combine epilogue: out[t][n] = sum_j ybuf[t k + j][n] (slot
+// order) + s2[n] acc[n][t]. The matrix cores are idle here, and the k bf16
+// slot rows of a token dominate the tile's bytes (at k = 6, 393 KB against
+// the K loop's 0.5 MB of weights), so they are requested as a batch: all k
+// rows of both row blocks for a column block of 16 tokens, the next column
+// block's batch before the current one is added. At 8192 tokens this took
+// the launch from 339 to 268 us (the loop over the slots had kept one load
+// per wave in flight); three column blocks in flight measured no better.
+template <int MB>
+__device__ __forceinline__ void gemm_combine(const GemmArgs& p, const f32x4_t (&acc)[kRB][MB], int ncols, int pos0,
+                                             int nt, int wn, int g, int r) {
+  const int k = p.topk;
+  int n[kRB];
+  float s2[kRB][4];
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    n[b] = nt * kBN + wn * 32 + b * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s2[b][i] = p.row_scale[n[b] + i];
+  }
+  uint2 y[2][kRB][kMaxTopK];
+  auto fetch = [&](int m, uint2 (&d)[kRB][kMaxTopK]) __attribute__((always_inline)) {
+    const int tok = m * 16 + r;
+    const uint16_t* row = p.ybuf + (size_t)(pos0 + (tok < ncols ? tok : 0)) * k * p.out_ld;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) {
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) d[b][j] = *reinterpret_cast<const uint2*>(row + (size_t)j * p.out_ld + n[b]);
+      }
+  };
+  fetch(0, y[0]);
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m + 1 < MB) fetch(m + 1, y[(m + 1) & 1]);
+    const int tok = m * 16 + r;
+    if (tok >= ncols) continue;
+    const size_t orow = (size_t)(pos0 + tok) * p.out_ld;
+#pragma unroll
+    for (int b = 0; b < kRB; ++b) {
+      float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) {
+          const uint2 v = y[m & 1][b][j];
+          o[0] += bf16_to_f32(v.x & 0xffffu);
+          o[1] += bf16_to_f32(v.x >> 16);
+          o[2] += bf16_to_f32(v.y & 0xffffu);
+          o[3] += bf16_to_f32(v.y >> 16);
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] += s2[b][i] * acc[b][m][i];
+      if (p.out_is_fp32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + n[b]) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + n[b]) = pk;
+      }
+    }
+  }
+}
+
 // The K loop and epilogue of one block over its first MB*16 positions.
 template <int FMT, int MODE, int MB, class StoreScales>
 __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, const unsigned char* lds_s,
@@ -271,33 +335,9 @@ __device__ __forceinline__ void gemm_main(const GemmArgs& p, const uint8_t* qe, 
         pk.y = (uint32_t)f32_to_bf16(acc[b][m][2] * wv) | ((uint32_t)f32_to_bf16(acc[b][m][3] * wv) << 16);
         *reinterpret_cast<uint2*>(p.yout + (size_t)slot * p.yout_ld + n) = pk;
       }
-    } else {  // shared w2 + combine: out[t] = sum_j ybuf[t*k+j] + s2 * acc
-#pragma unroll
-      for (int b = 0; b < kRB; ++b) {
-        const int n = nt * kBN + wn * 32 + b * 16 + 4 * g;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < p.topk; ++j) {
-          const uint2 y = *reinterpret_cast<const uint2*>(p.ybuf + ((size_t)pos * p.topk + j) * p.out_ld + n);
-          o.x += bf16_to_f32(y.x & 0xffffu);
-          o.y += bf16_to_f32(y.x >> 16);
-          o.z += bf16_to_f32(y.y & 0xffffu);
-          o.w += bf16_to_f32(y.y >> 16);
-        }
-        o.x += p.row_scale[n] * acc[b][m][0];
-        o.y += p.row_scale[n + 1] * acc[b][m][1];
-        o.z += p.row_scale[n + 2] * acc[b][m][2];
-        o.w += p.row_scale[n + 3] * acc[b][m][3];
-        if (p.out_is_fp32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)pos * p.out_ld + n) = o;
-        } else {
-          uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16(o.x) | ((uint32_t)f32_to_bf16(o.y) << 16);
-          pk.y = (uint32_t)f32_to_bf16(o.z) | ((uint32_t)f32_to_bf16(o.w) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (size_t)pos * p.out_ld + n) = pk;
-        }
-      }
     }
   }
+  if constexpr (MODE == kGemmW2Combine) gemm_combine<MB>(p, acc, ncols, pos0, nt, wn, g, r);
 }
 
 template <int FMT, int MODE>
