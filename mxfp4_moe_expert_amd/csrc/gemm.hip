@@ -354,15 +354,51 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   // of the logical tiles (N tiles fastest), handed out in order: a block's
   // first two tiles are fixed, then it grabs from its XCD's counter, two
   // tiles ahead, so that while a tile computes the block already knows the
-  // next one and requests its record and gathered row ids.
+  // next one and requests its record and gathered row ids. Once its XCD's
+  // run is handed out, a block takes tiles from the run of the XCD with the
+  // most left (equal runs of tiles are not equal work: at prefill the last
+  // XCD finished 90-130 us after the median one).
   const int nblk = p.routed ? *p.n_tiles * p.n_ntiles : ((p.T + kBM - 1) / kBM) * p.n_ntiles;
   if (nblk <= 0) return;  // no tiles (a rejected permutation): the whole grid leaves, the queue untouched
+  const int kNone = nblk;  // no tile
+  constexpr bool kSteal = FMT != kFmtI8;  // the shared expert's tiles (int8) are all alike: no stealing
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, inx = blockIdx.x >> 3;
-  const int nx = (G - xcd + 7) >> 3;  // blocks on this XCD
   const int per = nblk >> 3, extra = nblk & 7;
-  const int lo = xcd * per + min(xcd, extra), hi = lo + per + (xcd < extra ? 1 : 0);
+  // XCD y's run [lo, hi) and its blocks; tiles past the first two per block go through its counter
+  auto run_of = [&](int y, int& ylo, int& yhi, int& yq0) __attribute__((always_inline)) {
+    ylo = y * per + min(y, extra);
+    yhi = ylo + per + (y < extra ? 1 : 0);
+    yq0 = ylo + 2 * ((G - y + 7) >> 3);
+  };
+  int lo, hi, q0;
+  run_of(xcd, lo, hi, q0);
+  const int nx = (G - xcd + 7) >> 3;  // blocks on this XCD
   int* const q = p.queue;  // [8] tiles handed out per XCD, [8] blocks done
+  // another XCD's tile (thread 0, once this XCD's run is handed out): the
+  // counters are read, the run with the most tiles left is chosen and one
+  // tile taken from it with its counter; kNone when no run has any left
+  auto steal = [&]() -> int {
+    for (int attempt = 0; attempt < 8; ++attempt) {
+      int best = -1, best_left = 0, bhi = 0, bq0 = 0;
+#pragma unroll 1
+      for (int y = 0; y < 8; ++y) {
+        int ylo, yhi, yq0;
+        run_of(y, ylo, yhi, yq0);
+        const int left = yhi - (yq0 + (int)load_agent(reinterpret_cast<const uint32_t*>(q + y)));
+        if (y != xcd && left > best_left && left >= 2) {
+          best = y;
+          best_left = left;
+          bhi = yhi;
+          bq0 = yq0;
+        }
+      }
+      if (best < 0) return kNone;
+      const int t = bq0 + atomicAdd(q + best, 1);
+      if (t < bhi) return t;
+    }
+    return kNone;
+  };
 
   const int K = p.K;
   const int nst = K / kBK;
@@ -389,10 +425,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     return p.act_row ? p.act_row[apos] : apos;
   };
 
-  int cur = lo + inx, nxt = lo + nx + inx;
+  int cur = lo + inx < hi ? lo + inx : kNone;
+  int nxt = lo + nx + inx < hi ? lo + nx + inx : kNone;
   int4 rec = record(cur);
   int atrow = act_row_of(rec, (threadIdx.x >> 6) * 16 + (threadIdx.x & 15));
-  while (cur < hi) {
+  while (cur < kNone) {
     // Per-lane values come from an opaque copy of the thread index, so that
     // they are recomputed per tile: hoisted out of the loop they stayed live
     // across it and spilled.
@@ -509,12 +546,27 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
         gemm_main<FMT, MODE, kMB>(p, qe, lds_s, qoff, soff, asrc, adst0, adst1, abase0, abase1, nst, ncols, pos0,
                                   nt, wn, g, r, store_scales, slot_r, lv);
     }
-    if (tid == 0) grabbed = lo + 2 * nx + grab;
+    if (tid == 0) {
+      int t = q0 + grab;
+      if (t >= hi) t = kSteal && p.routed ? steal() : kNone;
+      grabbed = t;
+    }
     __syncthreads();  // every wave is done with this tile's LDS; the grab is visible
-    cur = nxt;
-    nxt = __builtin_amdgcn_readfirstlane(grabbed);
-    rec = rec_n;
-    atrow = atrow_n;
+    const int got = __builtin_amdgcn_readfirstlane(grabbed);
+    if (kSteal && nxt == kNone) {
+      // no next tile was known (a run shorter than two tiles per block): a
+      // stolen tile is taken now, its record loaded here
+      cur = got;
+      if (cur < kNone) {
+        rec = record(cur);
+        atrow = act_row_of(rec, (threadIdx.x >> 6) * 16 + (threadIdx.x & 15));
+      }
+    } else {
+      cur = nxt;
+      nxt = got;
+      rec = rec_n;
+      atrow = atrow_n;
+    }
   }
   // the last block out sets the counters back to zero for the next launch
   if (threadIdx.x == 0 && atomicAdd(q + 8, 1) == G - 1) {
