@@ -283,8 +283,13 @@ typedef struct moe_layer_weights {
  *              output of layer l, l < n_layers - 1, is left in act[l % 2])
  *   workspace  as for moe_forward (moe_workspace_size(cfg, T) bytes), shared
  *              by the layers in turn
- * Each layer takes the schedule moe_forward takes for it. Errors as for
- * moe_forward; a failed layer stops the stack. */
+ * Where moe_forward would run the layers as single launches (T <= 2 at
+ * shapes that have one), up to 8 layers run in one launch, each layer's
+ * output rows handed to the next inside it (also written to act as above);
+ * the results are those of the layers called one by one, bit for bit, and
+ * every layer's arguments are checked before anything is launched.
+ * Otherwise each layer takes the schedule moe_forward takes for it and a
+ * failed layer stops the stack. Errors as for moe_forward. */
 int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_weights* layers, int32_t T,
                       const uint16_t* x, const int32_t* token_ids, uint16_t* act, void* out,
                       int32_t out_is_fp32, void* workspace, size_t workspace_bytes, void* stream);

@@ -460,6 +460,47 @@ hipError_t routed_gemms_mx(const moe_config& c, int T, const uint16_t* x, const 
   return timed(MOE_KERNEL_ROUTED_W2, st, [&] { return launch_gemm_mx(b, p.max_tiles, st); });
 }
 
+// The single-launch layer's arguments (MXFP4 w2; the caller sets the 3-bit
+// fields). Hash layers (tid2eid) take no selection bias or logit offset.
+LayerArgs single_layer_args(const moe_config& c, int T, const uint16_t* x, const float* gate_w, const float* bias,
+                            const float* logit_offset, const int32_t* token_ids, const int32_t* tid2eid, int V,
+                            const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                            const int8_t* sh13, const float* sh13s, const int8_t* sh2, const float* sh2s, void* out,
+                            int out_is_fp32, int32_t* ids, float* w, uint32_t* xfer) {
+  const bool hash = tid2eid != nullptr;
+  LayerArgs la;
+  memset(&la, 0, sizeof(la));
+  la.T = T;
+  la.H = c.hidden_size;
+  la.I = c.moe_intermediate;
+  la.E = c.n_routed_experts;
+  la.k = c.top_k;
+  la.scale = c.routed_scaling_factor;
+  la.limit = c.swiglu_limit;
+  la.x = x;
+  la.gate_w = gate_w;
+  la.bias = hash ? nullptr : bias;
+  la.logit_offset = hash ? nullptr : logit_offset;
+  la.w13c = w13c;
+  la.w13s = w13s;
+  la.w2c = w2c;
+  la.w2s = w2s;
+  la.sh13 = sh13;
+  la.sh13s = sh13s;
+  la.sh2 = sh2;
+  la.sh2s = sh2s;
+  la.out = out;
+  la.out_is_fp32 = out_is_fp32 ? 1 : 0;
+  la.ids_out = ids;
+  la.w_out = w;
+  la.xfer = xfer;
+  la.flags = device_flags();
+  la.token_ids = hash ? token_ids : nullptr;
+  la.tid2eid = tid2eid;
+  la.V = hash ? V : 0;
+  return la;
+}
+
 int check_ws(const moe_config& c, int T, const void* ws, size_t bytes) {
   if (!ws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EINVAL;
@@ -745,6 +786,49 @@ int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_w
   for (int l = 0; l < n_layers; ++l)
     if (layers[l].tid2eid && !token_ids) return MOE_EINVAL;
   const size_t plane = (size_t)T * cfg->hidden_size;
+  if (schedule(*cfg, T, false) == MOE_SCHED_SINGLE &&
+      layer_stack_supported(cfg->hidden_size, cfg->moe_intermediate, cfg->n_routed_experts, T, cfg->top_k)) {
+    // Every layer is one single-launch layer: up to kStackChunk of them per
+    // launch, each layer's output rows handed to the next inside the launch.
+    // Every layer's arguments are checked before anything is launched.
+    if (!aligned16(x) || !aligned16(out)) return MOE_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+      const moe_layer_weights& W = layers[l];
+      const bool hash = W.tid2eid != nullptr;
+      if (!W.gate_w || !W.w13_codes || !W.w13_scales || !W.w2_codes || !W.w2_scales || !W.sh_w13 ||
+          !W.sh_w13_scale || !W.sh_w2 || !W.sh_w2_scale || (hash && W.V <= 0) || (!hash && !W.bias))
+        return MOE_EINVAL;
+      if (!aligned16(W.gate_w) || !aligned16(W.w13_codes) || !aligned16(W.w13_scales) || !aligned16(W.w2_codes) ||
+          !aligned16(W.w2_scales) || !aligned16(W.sh_w13) || !aligned16(W.sh_w2))
+        return MOE_EINVAL;
+    }
+    int rc = check_ws(*cfg, T, workspace, workspace_bytes);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = layout(*cfg, T);
+    uint32_t* xfer = at<uint32_t>(workspace, L.xfer);
+    int32_t* ids = at<int32_t>(workspace, L.ids);
+    float* w = at<float>(workspace, L.w);
+    for (int c0 = 0; c0 < n_layers; c0 += kStackChunk) {
+      StackArgs sa;
+      memset(&sa, 0, sizeof(sa));
+      sa.n = std::min(kStackChunk, n_layers - c0);
+      for (int j = 0; j < sa.n; ++j) {
+        const int l = c0 + j;
+        const moe_layer_weights& W = layers[l];
+        const bool last = l == n_layers - 1;
+        const uint16_t* in = l == 0 ? x : act + (size_t)((l - 1) & 1) * plane;  // read by the launch's first layer
+        void* dst = last ? out : static_cast<void*>(act + (size_t)(l & 1) * plane);
+        sa.layer[j] = single_layer_args(*cfg, T, in, W.gate_w, W.bias, W.logit_offset, token_ids, W.tid2eid, W.V,
+                                        W.w13_codes, W.w13_scales, W.w2_codes, W.w2_scales, W.sh_w13,
+                                        W.sh_w13_scale, W.sh_w2, W.sh_w2_scale, dst, last ? out_is_fp32 : 0, ids, w,
+                                        xfer);
+      }
+      rc = status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_layer_stack(sa, st); }));
+      if (rc) return rc;
+    }
+    return MOE_OK;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer_weights& W = layers[l];
     const bool hash = W.tid2eid != nullptr;
@@ -900,41 +984,11 @@ static int forward_impl(const moe_config* cfg, int32_t T, const uint16_t* x, con
 
   if (sched == MOE_SCHED_SINGLE) {
     // the whole layer in one launch, one block per CU
-    LayerArgs la;
-    la.T = T;
-    la.H = cfg->hidden_size;
-    la.I = cfg->moe_intermediate;
-    la.E = cfg->n_routed_experts;
-    la.k = cfg->top_k;
-    la.scale = cfg->routed_scaling_factor;
-    la.limit = cfg->swiglu_limit;
-    la.x = x;
-    la.gate_w = gate_w;
-    la.bias = bias;
-    la.logit_offset = logit_offset;
-    la.w13c = w13_codes;
-    la.w13s = w13_scales;
-    la.w2c = w2_codes;
-    la.w2s = w2_scales;
+    LayerArgs la = single_layer_args(*cfg, T, x, gate_w, bias, logit_offset, token_ids, hash ? tid2eid : nullptr,
+                                     V, w13_codes, w13_scales, w2_codes, w2_scales, sh_w13, sh_w13_scale, sh_w2,
+                                     sh_w2_scale, out, out_is_fp32, ids, w, at<uint32_t>(workspace, L.xfer));
     la.w2tab = W2.table;
     la.w2q3 = q3 ? 1 : 0;
-    la.sh13 = sh_w13;
-    la.sh13s = sh_w13_scale;
-    la.sh2 = sh_w2;
-    la.sh2s = sh_w2_scale;
-    la.out = out;
-    la.out_is_fp32 = out_is_fp32 ? 1 : 0;
-    la.ids_out = ids;
-    la.w_out = w;
-    la.xfer = at<uint32_t>(workspace, L.xfer);
-    la.flags = p.flags;
-    la.token_ids = hash ? token_ids : nullptr;
-    la.tid2eid = hash ? tid2eid : nullptr;
-    la.V = hash ? V : 0;
-    if (hash) {
-      la.bias = nullptr;  // selection bias and logit offset do not apply to hash layers
-      la.logit_offset = nullptr;
-    }
     return status(timed(MOE_KERNEL_ROUTED_W13, st, [&] { return launch_layer_small(la, st); }));
   }
   if (tiny) {

@@ -81,19 +81,22 @@ struct LayerShape {
   static_assert(XPT == 4 || XPT == 8, "H / 512 elements per thread");
 };
 
-// The hand-off buffers of one call (parity p) and of the next (1 - p).
+// The hand-off buffers of one layer (parity p) and of the next (1 - p).
 struct Xfer {
-  uint32_t* epoch;                 // [kXferBlocks] calls made by each block
-  uint32_t *scores, *h;            // [2 tokens][256], [16 columns][1024 pairs]: this call
-  uint32_t *scores_next, *h_next;  // the other parity: zeroed for the next call
+  uint32_t* epoch;                         // [kXferBlocks] layers run by each block
+  uint32_t *scores, *h, *x;                // [2 tokens][256], [16 columns][1024 pairs], [2 tokens][2048 pairs]
+  uint32_t *scores_next, *h_next, *x_next;  // the other parity: zeroed for the next layer
   __device__ __forceinline__ Xfer(uint32_t* base, uint32_t p) {
     epoch = base;
     uint32_t* s0 = base + kXferBlocks;
     uint32_t* h0 = s0 + 2 * kXferScoreWords;
+    uint32_t* x0 = h0 + 2 * kXferHWords;
     scores = s0 + p * kXferScoreWords;
     scores_next = s0 + (1 - p) * kXferScoreWords;
     h = h0 + p * kXferHWords;
     h_next = h0 + (1 - p) * kXferHWords;
+    x = x0 + p * kXferXWords;
+    x_next = x0 + (1 - p) * kXferXWords;
   }
 };
 
@@ -161,9 +164,9 @@ struct LayerBlock {
   float* sw;            // [16]
   int* flag;            // [4]: 0 router hand-off failed, 1 h hand-off failed
   float* lv;            // [16 slots][8] levels of each slot's expert (3-bit w2)
-  __device__ __forceinline__ LayerBlock(const LayerArgs& a, unsigned char* lds) {
+  __device__ __forceinline__ LayerBlock(const LayerArgs& a, unsigned char* lds, int thread = threadIdx.x) {
     b = blockIdx.x;
-    tid = threadIdx.x;
+    tid = thread;
     w = tid >> 6;
     lane = tid & 63;
     r = lane & 15;
@@ -190,9 +193,12 @@ struct LayerBlock {
 
 // Steps 1-4, the same for every wave: router slice, shared w13, top-k.
 // Returns the wave's shared w13 partial; qs2 gets the shared w2 weights.
+// xin: the layer's input rows come from the previous layer of the same
+// launch through X.x (its blocks publish them as tagged bf16 pairs), not
+// from a.x.
 template <int NH, int NI, int TT, int KK>
 __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlock<NH, NI, TT, KK>& L,
-                                              const Xfer& X, uint4 (&qs2)[2 * NI]) {
+                                              const Xfer& X, uint4 (&qs2)[2 * NI], bool xin = false) {
   using S = LayerShape<NH, NI, TT, KK>;
   constexpr int H = S::H, I = S::I, XPT = S::XPT, N13I = 2 * NH, N2I = 2 * NI;
   const int b = L.b, tid = L.tid, w = L.w, lane = L.lane, r = L.r, g = L.g, E = L.E;
@@ -201,15 +207,17 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
   //    tid*XPT ..), the router row slice of expert b, the shared w13 weights
   //    of the wave's K range
   uint32_t xr[TT][XPT / 2];
+  if (!xin) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const uint16_t* src = a.x + (size_t)t * H + tid * XPT;
-    if constexpr (XPT == 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      xr[t][0] = v.x; xr[t][1] = v.y; xr[t][2] = v.z; xr[t][3] = v.w;
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      xr[t][0] = v.x; xr[t][1] = v.y;
+    for (int t = 0; t < TT; ++t) {
+      const uint16_t* src = a.x + (size_t)t * H + tid * XPT;
+      if constexpr (XPT == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        xr[t][0] = v.x; xr[t][1] = v.y; xr[t][2] = v.z; xr[t][3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        xr[t][0] = v.x; xr[t][1] = v.y;
+      }
     }
   }
   const int er = min(b, E - 1);
@@ -218,6 +226,45 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
 #pragma unroll
   for (int i = 0; i < XPT / 4; ++i)
     rw[i] = *reinterpret_cast<const float4*>(a.gate_w + (size_t)er * H + tid * XPT + 4 * i);
+  bool xbad = false;  // the previous layer's rows did not all arrive
+  if (xin) {  // poll this thread's words of every token's row until none is zero
+    bool got[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) got[t] = false;
+    int spins = 0;
+    while (true) {
+      bool rdy = true;
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (!got[t]) {
+          const uint32_t* src = X.x + (size_t)t * (kXferMaxH / 2) + tid * (XPT / 2);
+          if constexpr (XPT == 8) {
+            const u32x4_t v = load_agent_u32x4(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[t][i] = v[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xr[t][i] = load_agent(src + i);
+          }
+          bool all = true;
+#pragma unroll
+          for (int i = 0; i < XPT / 2; ++i) all = all && xr[t][i] != 0u;
+          got[t] = all;
+        }
+        rdy = rdy && got[t];
+      }
+      if (rdy) break;
+      if (++spins >= kPollLimit) {
+        xbad = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int i = 0; i < XPT / 2; ++i) xr[t][i] ^= kHTag;
+  }
   // every wave's x and router slices are requested before any wave's shared
   // expert weights (the logit needs all eight slices: with each wave
   // requesting its three kinds back to back, the last slices queued behind
@@ -259,6 +306,7 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
     if (lane == 0) L.rred[w * TT + t] = acc;
   }
   __syncthreads();
+  if (xbad) L.flag[1] = 1;  // the layer's output becomes NaN
   if (tid < TT && b < E) {
     float logit = 0.0f;
 #pragma unroll
@@ -328,9 +376,17 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
 
 // Steps 5-9. Q3: the routed w2 in 3-bit blocks (a.w2c codes [E][H][I/32][12],
 // a.w2s binary16 scales [E][H][I/32], a.w2tab levels [E][8] or null).
-template <int NH, int NI, int TT, int KK, bool Q3>
+// STACK: one of several layers in one launch. The next layer's hand-off
+// buffers are zeroed here, before the h slices are awaited, and every store
+// of that is complete before this block publishes its output rows (nothing
+// another block can see comes earlier: every block enters the next layer only
+// once it has all of this layer's rows, so none can read a stale word there);
+// the layer count is kept by the launch. publish: the output rows go to the
+// next layer through X.x_next (and to a.out, bf16).
+template <int NH, int NI, int TT, int KK, bool Q3, bool STACK = false>
 __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<NH, NI, TT, KK>& L, const Xfer& X,
-                                           uint32_t ep, f32x4_t acc_sh, const uint4 (&qs2)[2 * NI]) {
+                                           uint32_t ep, f32x4_t acc_sh, const uint4 (&qs2)[2 * NI],
+                                           bool publish = false) {
   using S = LayerShape<NH, NI, TT, KK>;
   constexpr int H = S::H, I = S::I, NS = S::NS, NCOL = S::NCOL, P = S::P, HROW = S::HROW;
   constexpr int N13 = NH, N2 = NI, N2I = 2 * NI;
@@ -356,6 +412,34 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     shs[3] = a.sh13s[I + 8 * gb + 2 * p4 + 1];
   }
   const float s2n = a.sh2s[16 * ob + (tid & 15)];
+  float s2p[2] = {0.f, 0.f};  // publish: the shared w2 scales of output rows 2q, 2q + 1 (thread (t, q))
+  if (STACK && publish) {
+    s2p[0] = a.sh2s[16 * ob + 2 * (tid & 7)];
+    s2p[1] = a.sh2s[16 * ob + 2 * (tid & 7) + 1];
+  }
+
+  // this block's slices of the next layer's (or call's) hand-off buffers:
+  // scores of experts b, b+NB, ..; h pieces b, b+NB, .. of all columns;
+  // (stack) its output pairs of every token
+  auto zero_next = [&]() __attribute__((always_inline)) {
+    constexpr int kPieces = kXferMaxI / 8;
+    for (int i = tid; i < kXferCols * ((kPieces + NB - 1) / NB); i += kLayerThreads) {
+      const int c = i % kXferCols, o = b + NB * (i / kXferCols);
+      if (o < kPieces) {
+        uint64_t* d = reinterpret_cast<uint64_t*>(X.h_next + c * (kXferMaxI / 2) + 4 * o);
+        __hip_atomic_store(d, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    for (int i = tid; i < kXferTokens * ((kXferBlocks + NB - 1) / NB); i += kLayerThreads) {
+      const int t = i % kXferTokens, e = b + NB * (i / kXferTokens);
+      if (e < kXferBlocks) store_agent(X.scores_next + t * kXferBlocks + e, 0u);
+    }
+    if (STACK && b < H / 16 && tid < kXferTokens * 4) {  // 8 words of each token's row
+      uint64_t* d = reinterpret_cast<uint64_t*>(X.x_next + (size_t)(tid >> 2) * (kXferMaxH / 2) + 8 * b + 2 * (tid & 3));
+      __hip_atomic_store(d, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   f32x4_t acc13[1 + NS];
   acc13[0] = acc_sh;
@@ -457,6 +541,7 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
 #pragma unroll
   for (int u = kEarly; u < NS; ++u) issue2(u);
   asm volatile("" ::: "memory");
+  if constexpr (STACK) zero_next();
 
   // the early routed w2 jobs' weights, converted to bf16 while the other
   // blocks' h slices are awaited (they arrived before the h publish; the
@@ -538,6 +623,9 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
       }
     }
   }
+  // stack: this thread's zeroing stores are complete (the w2 weights, needed
+  // next, are in too) before the barrier that precedes the output
+  if constexpr (STACK) __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));  // vmcnt(0)
   __syncthreads();
   const bool ok = ok_route && L.flag[1] == 0;
 
@@ -590,7 +678,28 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     L.ycol[rr * 16 + c] = s;
   }
   __syncthreads();
-  if (tid < TT * 16) {  // thread (t, rr): output row 16ob + rr of token t
+  if (STACK && publish) {
+    if (tid < TT * 8) {  // thread (t, q): output rows 16ob + 2q, + 1 of token t, as one tagged pair
+      const int t = tid >> 3, q = tid & 7;
+      float o2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rr = 2 * q + hh;
+        float o = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KK; ++j) o += L.sw[t * KK + j] * L.ycol[rr * 16 + t * KK + j];
+        o += s2p[hh] * L.ycol[rr * 16 + NS + t];
+        o2[hh] = o;
+      }
+      uint32_t packed = (uint32_t)f32_to_bf16(o2[0]) | ((uint32_t)f32_to_bf16(o2[1]) << 16);
+      if (!ok) packed = kNaNPair;  // a hand-off timed out: never a silent wrong value
+      if (!ok && tid == 0 && a.flags) atomicOr(a.flags, kFlagWaitExpired);
+      if (b < H / 16) {
+        store_agent(X.x_next + (size_t)t * (kXferMaxH / 2) + 8 * ob + q, packed ^ kHTag);
+        reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + (size_t)t * H + 16 * ob)[q] = packed;
+      }
+    }
+  } else if (tid < TT * 16) {  // thread (t, rr): output row 16ob + rr of token t
     const int t = tid >> 4, rr = tid & 15;
     const int n = 16 * ob + rr;
     float o = 0.0f;
@@ -605,26 +714,15 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     }
   }
 
-  // 9. for the next call: zero this block's slices of the other buffers
-  //    (scores of experts b, b+NB, ..; h pieces b, b+NB, .. of all columns)
-  //    and count the call for blocks b, b+NB, .. (so that smaller grids keep
+  // 9. for the next call: zero this block's slices of the other buffers and
+  //    count the call for blocks b, b+NB, .. (so that smaller grids keep
   //    every count in step)
-  constexpr int kPieces = kXferMaxI / 8;
-  for (int i = tid; i < kXferCols * ((kPieces + NB - 1) / NB); i += kLayerThreads) {
-    const int c = i % kXferCols, o = b + NB * (i / kXferCols);
-    if (o < kPieces) {
-      uint64_t* d = reinterpret_cast<uint64_t*>(X.h_next + c * (kXferMaxI / 2) + 4 * o);
-      __hip_atomic_store(d, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(d + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (!STACK) {
+    zero_next();
+    for (int i = tid; i < (kXferBlocks + NB - 1) / NB; i += kLayerThreads) {
+      const int bb = b + NB * i;
+      if (bb < kXferBlocks) store_agent(X.epoch + bb, ep + 1);
     }
-  }
-  for (int i = tid; i < kXferTokens * ((kXferBlocks + NB - 1) / NB); i += kLayerThreads) {
-    const int t = i % kXferTokens, e = b + NB * (i / kXferTokens);
-    if (e < kXferBlocks) store_agent(X.scores_next + t * kXferBlocks + e, 0u);
-  }
-  for (int i = tid; i < (kXferBlocks + NB - 1) / NB; i += kLayerThreads) {
-    const int bb = b + NB * i;
-    if (bb < kXferBlocks) store_agent(X.epoch + bb, ep + 1);
   }
 }
 
@@ -639,9 +737,42 @@ __global__ __launch_bounds__(kLayerThreads) void k_layer_small(LayerArgs a) {
   layer_tail<NH, NI, TT, KK, Q3>(a, L, X, ep, acc_sh, qs2);
 }
 
+// Layers run back to back in one launch (a stack at T <= 2): layer j of the
+// launch uses the hand-off buffers of parity (layers so far + j) & 1, takes
+// its input rows from the previous layer through them (the first from its
+// x) and publishes its output rows the same way (the last one only writes
+// its out).
+template <int NH, int NI, int TT, int KK>
+__global__ __launch_bounds__(kLayerThreads) void k_layer_stack(StackArgs sa) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const uint32_t* xfer = sa.layer[0].xfer;
+  const uint32_t ep = load_agent(xfer + blockIdx.x);  // this block's layers so far
+  const int n = sa.n;
+  for (int j = 0; j < n; ++j) {
+    const LayerArgs& a = sa.layer[j];
+    // per-lane values from an opaque copy of the thread index, recomputed per
+    // layer: hoisted out of the loop they stay live across it and spill
+    int thread;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(thread) : "v"((int)threadIdx.x));
+    const LayerBlock<NH, NI, TT, KK> L(a, lds, thread);
+    const Xfer X(a.xfer, (ep + j) & 1);
+    uint4 qs2[2 * NI];
+    const f32x4_t acc_sh = layer_head(a, L, X, qs2, j > 0);
+    layer_tail<NH, NI, TT, KK, false, true>(a, L, X, ep + j, acc_sh, qs2, j + 1 < n);
+    __syncthreads();  // the next layer reuses the LDS
+  }
+  // count the layers for blocks b, b+NB, .. (every count in step)
+  const Xfer X(sa.layer[0].xfer, 0);
+  for (int i = threadIdx.x; i < (kXferBlocks + (int)gridDim.x - 1) / (int)gridDim.x; i += kLayerThreads) {
+    const int bb = blockIdx.x + gridDim.x * i;
+    if (bb < kXferBlocks) store_agent(X.epoch + bb, ep + n);
+  }
+}
+
 namespace {
 
 using LayerKernel = void (*)(LayerArgs);
+using StackKernel = void (*)(StackArgs);
 
 // LDS asked for: at least 81 KB of the CU's 160 KB, so that one block holds
 // a CU (the design is one block per CU; two on one CU would leave another
@@ -663,20 +794,18 @@ LayerKernel layer_kernel(int H, int I, int T, int k, size_t* lds, bool q3) {
 
 // Blocks of kernel k that the current device holds at once (0 if unknown),
 // cached per device and kernel.
-int resident_blocks(LayerKernel k, size_t lds) {
-  constexpr int kDev = 16, kKern = 8;
-  static LayerKernel seen[kDev][kKern];
+int resident_blocks(const void* k, size_t lds) {
+  constexpr int kDev = 16, kKern = 16;
+  static const void* seen[kDev][kKern];
   static int count[kDev][kKern];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) return 0;
   for (int i = 0; i < kKern; ++i)
     if (seen[dev][i] == k) return count[dev][i];
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-          hipSuccess)
+  if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return 0;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), kLayerThreads, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kLayerThreads, lds) !=
           hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -691,6 +820,21 @@ int resident_blocks(LayerKernel k, size_t lds) {
 
 int layer_grid(int H, int I, int E) { return std::max(E, std::max(I / 8, H / 16)); }
 
+template <int NH, int NI, int TT, int KK>
+StackKernel pick_stack(size_t* lds) {
+  *lds = std::max(LayerShape<NH, NI, TT, KK>::lds_bytes, (size_t)81 * 1024);
+  return &k_layer_stack<NH, NI, TT, KK>;
+}
+
+StackKernel stack_kernel(int H, int I, int T, int k, size_t* lds) {
+  if (k != 6) return nullptr;
+  if (H == 4096 && I == 2048)
+    return T == 1 ? pick_stack<4, 2, 1, 6>(lds) : T == 2 ? pick_stack<4, 2, 2, 6>(lds) : nullptr;
+  if (H == 2048 && I == 1024)
+    return T == 1 ? pick_stack<2, 1, 1, 6>(lds) : T == 2 ? pick_stack<2, 1, 2, 6>(lds) : nullptr;
+  return nullptr;
+}
+
 }  // namespace
 
 bool layer_small_supported(int H, int I, int E, int T, int k, bool w2q3) {
@@ -698,7 +842,7 @@ bool layer_small_supported(int H, int I, int E, int T, int k, bool w2q3) {
   LayerKernel kern = layer_kernel(H, I, T, k, &lds, w2q3);
   if (!kern || E < k || E > 256) return false;
   const int grid = layer_grid(H, I, E);
-  return grid <= kXferBlocks && resident_blocks(kern, lds) >= grid;
+  return grid <= kXferBlocks && resident_blocks(reinterpret_cast<const void*>(kern), lds) >= grid;
 }
 
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st) {
@@ -706,8 +850,33 @@ hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st) {
   LayerKernel kern = layer_kernel(a.H, a.I, a.T, a.k, &lds, a.w2q3 != 0);
   if (!kern) return hipErrorInvalidValue;
   const int grid = layer_grid(a.H, a.I, a.E);
-  if (grid > kXferBlocks || resident_blocks(kern, lds) < grid) return hipErrorInvalidValue;
+  if (grid > kXferBlocks || resident_blocks(reinterpret_cast<const void*>(kern), lds) < grid) return hipErrorInvalidValue;
   kern<<<grid, kLayerThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+bool layer_stack_supported(int H, int I, int E, int T, int k) {
+  size_t lds = 0;
+  StackKernel kern = stack_kernel(H, I, T, k, &lds);
+  if (!kern || E < k || E > 256) return false;
+  const int grid = layer_grid(H, I, E);
+  return grid <= kXferBlocks && resident_blocks(reinterpret_cast<const void*>(kern), lds) >= grid;
+}
+
+hipError_t launch_layer_stack(const StackArgs& sa, hipStream_t st) {
+  if (sa.n < 1 || sa.n > kStackChunk) return hipErrorInvalidValue;
+  const LayerArgs& a = sa.layer[0];
+  for (int j = 1; j < sa.n; ++j)  // one shape and one hand-off region for every layer of the launch
+    if (sa.layer[j].T != a.T || sa.layer[j].H != a.H || sa.layer[j].I != a.I || sa.layer[j].E != a.E ||
+        sa.layer[j].k != a.k || sa.layer[j].xfer != a.xfer || sa.layer[j].w2q3)
+      return hipErrorInvalidValue;
+  size_t lds = 0;
+  StackKernel kern = stack_kernel(a.H, a.I, a.T, a.k, &lds);
+  if (!kern || a.w2q3) return hipErrorInvalidValue;
+  const int grid = layer_grid(a.H, a.I, a.E);
+  if (grid > kXferBlocks || resident_blocks(reinterpret_cast<const void*>(kern), lds) < grid)
+    return hipErrorInvalidValue;
+  kern<<<grid, kLayerThreads, lds, st>>>(sa);
   return hipGetLastError();
 }
 

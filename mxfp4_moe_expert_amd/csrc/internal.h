@@ -285,13 +285,15 @@ hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, con
 hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
 // Hand-off region of the single-launch layer, at a fixed offset at the start
-// of every workspace (zero on first use): per-block call counters, then two
-// buffers, used by alternate calls, of router scores and h columns.
+// of every workspace (zero on first use): per-block layer counters, then two
+// buffers, used by alternate layers, of router scores, h columns and (for
+// layers run back to back in one launch) the layer's input rows.
 constexpr int kXferBlocks = 256;  // blocks tracked: the largest single-launch grid
-constexpr int kXferTokens = 2, kXferCols = 16, kXferMaxI = 2048;
+constexpr int kXferTokens = 2, kXferCols = 16, kXferMaxI = 2048, kXferMaxH = 4096;
 constexpr size_t kXferScoreWords = (size_t)kXferTokens * kXferBlocks;  // [2 tokens][256 experts]
 constexpr size_t kXferHWords = (size_t)kXferCols * (kXferMaxI / 2);     // [16 columns][1024 bf16 pairs]
-constexpr size_t kXferBytes = ((size_t)kXferBlocks + 2 * (kXferScoreWords + kXferHWords)) * 4;
+constexpr size_t kXferXWords = (size_t)kXferTokens * (kXferMaxH / 2);   // [2 tokens][2048 bf16 pairs]
+constexpr size_t kXferBytes = ((size_t)kXferBlocks + 2 * (kXferScoreWords + kXferHWords + kXferXWords)) * 4;
 
 // The whole layer for T <= 2 tokens (T*(k+1) <= 16) in one launch of one
 // block per CU.
@@ -344,6 +346,22 @@ struct LinearDecArgs {
 int linear_dec_ks(int T, int K, int N, int G);  // 0: not supported
 hipError_t launch_linear_dec(const LinearDecArgs& a, hipStream_t st);
 hipError_t launch_layer_small(const LayerArgs& a, hipStream_t st);
+
+// Layers run back to back in one launch of the single-launch layer (a stack
+// of MoE layers at T <= 2): each layer's output rows go to the next through
+// the hand-off region instead of a kernel boundary. Up to kStackChunk layers
+// per launch, their arguments passed as kernel arguments: layer j > 0 of a
+// launch takes its input from layer j - 1 (its x is not read), and writes
+// out too (bf16) unless it is the launch's last layer.
+constexpr int kStackChunk = 8;
+struct StackArgs {
+  int n;  // layers in this launch, 1 .. kStackChunk
+  LayerArgs layer[kStackChunk];
+};
+// Whether launch_layer_stack has a kernel for this shape whose whole grid the
+// current device holds at once.
+bool layer_stack_supported(int H, int I, int E, int T, int k);
+hipError_t launch_layer_stack(const StackArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 // Device error flags (values of MOE_FLAG_* in moe.h), one word per GPU in

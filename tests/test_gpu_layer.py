@@ -90,3 +90,43 @@ def test_single_launch_interleaved_calls(lay):
         xh = synth.make_tokens(wl, rep=40 + T, T=T)
         _, ref = reference_rows(L, xh, np.arange(T, dtype=np.int32))
         assert_outputs_close(first[T].cpu().numpy(), ref, f"interleaved T={T}")
+
+
+@pytest.fixture(scope="module")
+def lay_stack():
+    """Three layers of the same shape (hidden 2048, 64 experts: a grid of
+    128 blocks, blocks past the experts only stream weights), the second
+    routed by a token-id table."""
+    wls = [dataclasses.replace(LAY, seed=31), dataclasses.replace(LAY, seed=32, hash_layer=True),
+           dataclasses.replace(LAY, seed=33)]
+    hosts = [synth.make_layer(wl) for wl in wls]
+    return wls, hosts, [mx.DeviceLayer.from_host(L, DEV) for L in hosts]
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_stack_of_single_launch_layers(lay_stack, T):
+    """moe_forward_stack at T <= 2 runs up to eight single-launch layers in
+    one launch, each handing its output rows to the next inside it: eleven
+    layers (two launches) equal the layers called one by one bit for bit,
+    the intermediate outputs left in act, twice in a row."""
+    wls, hosts, devs = lay_stack
+    cfg = mx.config_of(LAY)
+    order = [l % 3 for l in range(11)]
+    layers = [devs[l] for l in order]
+    x = mx.bf16_from_numpy(synth.make_tokens(LAY, rep=70 + T, T=T), DEV)
+    tids = torch.from_numpy(synth.make_token_ids(wls[1], rep=70 + T, T=T)).to(DEV)
+    act = torch.empty(2, T, LAY.H, dtype=torch.bfloat16, device=DEV)
+    print(f"[stack of single-launch layers T={T}]", flush=True)
+    out = mx.forward_stack(cfg, x, layers, token_ids=tids, out_fp32=True, act=act)
+    again = mx.forward_stack(cfg, x, layers, token_ids=tids, out_fp32=True)
+    y, outs = x, []
+    for i, l in enumerate(order):
+        y = mx.forward(cfg, y, devs[l], token_ids=tids if wls[l].hash_layer else None,
+                       out_fp32=i == len(order) - 1)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.equal(out, outs[-1])
+    assert torch.equal(again, out)
+    assert torch.equal(act[(len(order) - 2) % 2], outs[-2])
+    assert mx.device_flags() == set()

@@ -116,3 +116,51 @@ def test_stack_argument_checks(stack):
     x = torch.zeros(1, host[0].wl.H, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(mx.MoEError):  # hash layers need token ids
         mx.forward_stack(cfg, x, dev[:1])
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_stack_ten_layers_equals_layer_by_layer(stack, T):
+    """Ten layers (the four built ones in turn, hash and learned mixed) at
+    T = 1, 2: one launch runs up to eight layers, handing each layer's output
+    rows to the next inside the launch, so this crosses a launch boundary.
+    Bit for bit against the layers called one by one, with every
+    intermediate output left in act as documented."""
+    host, dev = stack
+    cfg = mx.config_of(host[0].wl)
+    order = [l % N_LAYERS for l in range(10)]
+    layers = [dev[l] for l in order]
+    _, _, x, tids = _inputs(host[0].wl, T, 560 + T)
+    act = torch.empty(2, T, host[0].wl.H, dtype=torch.bfloat16, device=DEV)
+    out = mx.forward_stack(cfg, x, layers, token_ids=tids, out_fp32=True, act=act)
+    y, outs = x, []
+    for l, D in zip(order, layers):
+        last = len(outs) == len(layers) - 1
+        y = mx.forward(cfg, y, D, token_ids=tids if host[l].wl.hash_layer else None, out_fp32=last)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.equal(out, outs[-1])
+    assert torch.equal(act[(len(layers) - 2) % 2], outs[-2])
+    assert torch.equal(act[(len(layers) - 3) % 2], outs[-3])
+    assert mx.device_flags() == set()
+
+
+def test_stack_interleaved_with_single_layers(stack):
+    """Stack calls and single-layer calls on one workspace: the hand-off
+    buffers' parity and counters stay in step whichever runs (the stack
+    advances them by its layer count)."""
+    host, dev = stack
+    cfg = mx.config_of(host[0].wl)
+    ws = mx.Workspace(torch.device(DEV))
+    _, _, x, tids = _inputs(host[0].wl, 1, 580)
+    first = mx.forward_stack(cfg, x, dev[:3], token_ids=tids, out_fp32=True, ws=ws)
+    single = mx.forward(cfg, x, dev[3], out_fp32=True, ws=ws)
+    second = mx.forward_stack(cfg, x, dev[:3], token_ids=tids, out_fp32=True, ws=ws)
+    single2 = mx.forward(cfg, x, dev[3], out_fp32=True, ws=ws)
+    third = mx.forward_stack(cfg, x, dev[:2], token_ids=tids, out_fp32=True, ws=ws)
+    two = mx.forward_stack(cfg, x, dev[:2], token_ids=tids, out_fp32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(first, second)
+    assert torch.equal(single, single2)
+    assert torch.equal(third, two)
+    assert mx.device_flags() == set()
