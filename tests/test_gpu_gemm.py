@@ -120,3 +120,36 @@ def test_forward_gemm_deterministic(mid):
     b = mx.forward(cfg, x, D, out_fp32=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_expert_ffn_gemm_unequal_runs(mid):
+    """Every token on experts 0-5 but 26 (one slot each moved to experts
+    6-31): the tile list is 192 full tiles, then 26 one-position tiles, so
+    the persistent GEMM's eight per-XCD runs of equal tile counts are
+    unequal work (the last XCD's run is nearly all one-position tiles) and
+    its blocks take tiles from the other XCDs' runs. Every row against the
+    oracle, and a second call gives the same bits."""
+    wl, L, D, cfg = mid
+    T = 4096
+    print(f"[expert_ffn mid T={T} unequal runs]", flush=True)
+    rng = np.random.default_rng(11)
+    ids_h = np.tile(np.arange(wl.k, dtype=np.int32), (T, 1))
+    movers = rng.choice(T, size=wl.E - wl.k, replace=False)
+    for e, t in zip(range(wl.k, wl.E), movers):
+        ids_h[t, rng.integers(wl.k)] = e
+    w_h = rng.uniform(0.05, 0.5, size=ids_h.shape).astype(np.float32)
+    xh, x = _x(wl, T, rep=13)
+    offsets, sorted_slots, _ = mx.permute(cfg, torch.from_numpy(ids_h).to(DEV))
+    args = (cfg, x, offsets, sorted_slots, torch.from_numpy(w_h).to(DEV), D.w13_codes, D.w13_scales, D.w2_codes,
+            D.w2_scales)
+    out = mx.expert_ffn(*args)
+    again = mx.expert_ffn(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    counts = np.bincount(ids_h.ravel(), minlength=wl.E)
+    live = int(np.sum((counts + 127) // 128))
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    assert live * (wl.I // 128) > 2 * grid, (live, grid)
+    ref = oracle.expert_ffn(xh, ids_h, w_h.astype(np.float64), L.w13_codes, L.w13_scales, L.w2_codes,
+                            L.w2_scales)
+    assert_outputs_close(out.cpu().numpy(), ref, f"expert_ffn mid T={T} unequal runs")
