@@ -37,13 +37,14 @@
 // h values) XORed with a tag that no computed word equals, so that no
 // published word is zero, with device-wide coherent stores; a consumer polls
 // the words themselves with coherent loads until none is zero. The buffers
-// are zero before a call: each block counts its calls in a word of its own
-// (every block runs once per call, so all counts agree), calls alternate
-// between two buffers by that count's parity, and each block zeroes its
-// slices of the other buffer when it is done. Every poll is bounded: past
-// the limit the output is NaN, never a silent wrong value. The waits are for
-// every block of the grid, so the launch checks with the occupancy
-// calculator that the whole grid is resident at once.
+// are zero before a layer: each block counts the layers it has run in a word
+// of its own (every block runs every layer, so all counts agree), layers
+// alternate between two buffers by that count's parity, and each block
+// zeroes its slices of the other buffer when it is done (a launch of several
+// layers, k_layer_stack, does it earlier: see layer_tail). Every poll is
+// bounded: past the limit the output is NaN, never a silent wrong value. The
+// waits are for every block of the grid, so the launch checks with the
+// occupancy calculator that the whole grid is resident at once.
 #include <algorithm>
 
 #include "device.h"
