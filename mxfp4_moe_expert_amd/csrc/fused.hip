@@ -40,8 +40,8 @@
 // are zero before a layer: each block counts the layers it has run in a word
 // of its own (every block runs every layer, so all counts agree), layers
 // alternate between two buffers by that count's parity, and each block
-// zeroes its slices of the other buffer when it is done (a launch of several
-// layers, k_layer_stack, does it earlier: see layer_tail). Every poll is
+// zeroes its slices of the other buffer, which no block reads during this
+// layer, once its h slices are published (see layer_tail). Every poll is
 // bounded: past the limit the output is NaN, never a silent wrong value. The
 // waits are for every block of the grid, so the launch checks with the
 // occupancy calculator that the whole grid is resident at once.
@@ -377,13 +377,13 @@ __device__ __forceinline__ f32x4_t layer_head(const LayerArgs& a, const LayerBlo
 
 // Steps 5-9. Q3: the routed w2 in 3-bit blocks (a.w2c codes [E][H][I/32][12],
 // a.w2s binary16 scales [E][H][I/32], a.w2tab levels [E][8] or null).
-// STACK: one of several layers in one launch. The next layer's hand-off
-// buffers are zeroed here, before the h slices are awaited, and every store
-// of that is complete before this block publishes its output rows (nothing
-// another block can see comes earlier: every block enters the next layer only
-// once it has all of this layer's rows, so none can read a stale word there);
-// the layer count is kept by the launch. publish: the output rows go to the
-// next layer through X.x_next (and to a.out, bf16).
+// The next layer's (or call's) hand-off buffers are zeroed before the h
+// slices are awaited. STACK: one of several layers in one launch; every
+// zeroing store is complete before this block publishes its output rows
+// (every block enters the next layer only once it has all of this layer's
+// rows, so none can read a stale word there), and the layer count is kept by
+// the launch. publish: the output rows go to the next layer through X.x_next
+// (and to a.out, bf16).
 template <int NH, int NI, int TT, int KK, bool Q3, bool STACK = false>
 __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<NH, NI, TT, KK>& L, const Xfer& X,
                                            uint32_t ep, f32x4_t acc_sh, const uint4 (&qs2)[2 * NI],
@@ -542,7 +542,15 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
 #pragma unroll
   for (int u = kEarly; u < NS; ++u) issue2(u);
   asm volatile("" ::: "memory");
-  if constexpr (STACK) zero_next();
+  // the other buffers and the layer count are nobody's in this layer: done
+  // here, off the tail (at the end they held up the last block's exit)
+  zero_next();
+  if constexpr (!STACK) {
+    for (int i = tid; i < (kXferBlocks + NB - 1) / NB; i += kLayerThreads) {
+      const int bb = b + NB * i;
+      if (bb < kXferBlocks) store_agent(X.epoch + bb, ep + 1);
+    }
+  }
 
   // the early routed w2 jobs' weights, converted to bf16 while the other
   // blocks' h slices are awaited (they arrived before the h publish; the
@@ -712,17 +720,6 @@ __device__ __forceinline__ void layer_tail(const LayerArgs& a, const LayerBlock<
     if (b < H / 16) {
       if (a.out_is_fp32) static_cast<float*>(a.out)[(size_t)t * H + n] = o;
       else static_cast<uint16_t*>(a.out)[(size_t)t * H + n] = f32_to_bf16(o);
-    }
-  }
-
-  // 9. for the next call: zero this block's slices of the other buffers and
-  //    count the call for blocks b, b+NB, .. (so that smaller grids keep
-  //    every count in step)
-  if constexpr (!STACK) {
-    zero_next();
-    for (int i = tid; i < (kXferBlocks + NB - 1) / NB; i += kLayerThreads) {
-      const int bb = b + NB * i;
-      if (bb < kXferBlocks) store_agent(X.epoch + bb, ep + 1);
     }
   }
 }
