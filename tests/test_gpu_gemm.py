@@ -153,3 +153,34 @@ def test_expert_ffn_gemm_unequal_runs(mid):
     ref = oracle.expert_ffn(xh, ids_h, w_h.astype(np.float64), L.w13_codes, L.w13_scales, L.w2_codes,
                             L.w2_scales)
     assert_outputs_close(out.cpu().numpy(), ref, f"expert_ffn mid T={T} unequal runs")
+
+
+LONGK = synth.Workload("longk", T=300, H=256, E=8, k=6, I=2176, V=5000, bias_sigma=0.05)
+
+
+@pytest.mark.parametrize("T", [256, 300])
+def test_forward_gemm_long_shared_k(T):
+    """Intermediate 2176 = 17 x 128: routed w2 runs an odd number of MXFP4
+    stages (17, the K loop's last stage after its stage pairs) and the
+    shared expert's int8 w2 + combine 34 stages; 17 SwiGLU column tiles of
+    w13. T=256 is two full token tiles, T=300 adds a ragged one. Every row
+    against the oracle, bf16 output equal to the rounded fp32 one, and a
+    second call repeats the bits."""
+    wl = LONGK
+    print(f"[forward longk T={T}]", flush=True)
+    L = synth.make_layer(wl)
+    D = mx.DeviceLayer.from_host(L, DEV)
+    cfg = mx.config_of(wl)
+    xh, x = _x(wl, T, rep=T + 7)
+    out, (ids, w) = mx.forward(cfg, x, D, out_fp32=True, return_routing=True)
+    again = mx.forward(cfg, x, D, out_fp32=True)
+    out_bf = mx.forward(cfg, x, D, out_fp32=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
+    rows = np.arange(T, dtype=np.int32)
+    r, ref = reference_rows(L, xh, rows)
+    rt = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), r["ids"], r["w"], r["gap"], r["next"])
+    if rt["alt_rows"]:
+        r, ref = reference_rows(L, xh, rows, routing=rt)
+    assert_outputs_close(out.cpu().numpy(), ref, f"forward longk T={T}")
