@@ -56,7 +56,7 @@
  *     (moe_workspace_init, or any zero fill): bytes 64 .. 67 count the
  *     blocks of the decode-size top-k, bytes 96 .. 239 hold the tile
  *     queues of the grouped GEMMs (MOE_SCHED_LARGE), and bytes 256 ..
- *     136447 hold the hand-off state of the single-launch layer
+ *     169215 hold the hand-off state of the single-launch layer
  *     (MOE_SCHED_SINGLE); every call leaves all three ready for the next,
  *     and every other workspace value is written before it is read. Calls
  *     that share one workspace must be ordered on one stream. If a bounded
@@ -68,6 +68,8 @@
  *   - Supported shapes: H and I multiples of 128, 1 <= top_k <= 8,
  *     top_k <= E <= 256, 0 <= T <= 65536. Device pointers must be 16-byte
  *     aligned.
+ *   - Buffers a call writes (outputs, act, workspace) must not overlap each
+ *     other or any buffer the call reads.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
