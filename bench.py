@@ -241,10 +241,12 @@ def copy_calibration():
 
 
 def measured_peaks():
-    """What plain library work reaches on this GPU, as denominators beside
-    the published peaks: a 1 GiB device copy (HBM GB/s, read + write bytes)
-    and a bf16 8192^3 matmul (TFLOP/s), each the median of 20 runs timed
-    with events."""
+    """What plain work reaches on this GPU, as denominators beside the
+    published peaks: a 1 GiB device copy (HBM GB/s, read + write bytes), a
+    1 GiB read with the library's streaming-read kernel (read bytes; the
+    decode paths only read; the best of four grid sizes) and a bf16 8192^3
+    matmul (TFLOP/s), each the median of 20 runs timed with events."""
+    import mxfp4_moe_expert_amd as mx
     import torch
 
     def timed(fn, n=20):
@@ -265,12 +267,19 @@ def measured_peaks():
     dst = torch.empty_like(src)
     ms_copy = timed(lambda: dst.copy_(src))
     del src, dst
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    read_grid = {g: timed(lambda: mx.read_probe(src, g, sink)) for g in (2048, 4096, 8192, 16384)}
+    ms_read = min(read_grid.values())
+    del src, sink
     n = 8192
     x = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     y = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     ms_mm = timed(lambda: torch.matmul(x, y))
     rec = {"copy_bytes_moved": 2 * nb, "copy_ms": round(ms_copy, 4),
            "copy_GBps": round(2 * nb / (ms_copy / 1e3) / 1e9, 1),
+           "read_bytes": nb, "read_ms": round(ms_read, 4), "read_GBps": round(nb / (ms_read / 1e3) / 1e9, 1),
+           "read_GBps_by_blocks": {str(g): round(nb / (ms / 1e3) / 1e9, 1) for g, ms in read_grid.items()},
            "matmul_bf16_n": n, "matmul_ms": round(ms_mm, 4),
            "matmul_TFLOPs": round(2.0 * n ** 3 / (ms_mm / 1e3) / 1e12, 1),
            "published": {"hbm_GBps": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS}}

@@ -117,6 +117,17 @@ enum {
  * the stream (host synchronisation): a diagnostic, not for the hot path. */
 int moe_device_flags(uint32_t* flags, int32_t clear, void* stream);
 
+/* Measurement aid, not part of the layer: reads `bytes` of device memory at
+ * `buf` once with a plain streaming kernel of `blocks` blocks of 256
+ * threads (32 KB chunks per block; 16-byte loads, 1 KB per wave-wide load,
+ * eight in flight per lane) on `stream`, so that timing it gives the HBM
+ * read rate this GPU reaches, the denominator beside the published 8 TB/s
+ * for paths that only read. sink: [blocks] u32 device words; a word is
+ * written only if the folded data of its block takes one particular value
+ * (never for a buffer of zeros or ones). buf 16-byte aligned, bytes a
+ * multiple of 16, blocks > 0, else MOE_EINVAL. */
+int moe_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(int status);
 

@@ -75,6 +75,7 @@ _SIGNATURES = {
                        ctypes.c_int),
     "moe_set_kernel_events": ([_I32, _VP, _VP], ctypes.c_int),
     "moe_device_flags": ([ctypes.POINTER(ctypes.c_uint32), _I32, _VP], ctypes.c_int),
+    "moe_read_probe": ([_VP, _SZ, _I32, _VP, _VP], ctypes.c_int),
     "moe_set_option": ([_I32, _I32], ctypes.c_int),
     "moe_get_option": ([_I32], ctypes.c_int),
     "moe_forward_schedule": ([_CFGP, _I32, _I32], ctypes.c_int),
@@ -165,6 +166,19 @@ def set_option(name: str, value: int):
 
 
 FLAGS = {"token_id": 1, "table_entry": 2, "expert_id": 4, "wait_expired": 8, "permutation": 16}
+
+
+def read_probe(buf, blocks: int, sink, device=None) -> None:
+    """Queues the library's streaming-read kernel over all of ``buf`` (a
+    contiguous device tensor, 16-byte multiple) with ``blocks`` blocks on the
+    current stream; ``sink`` is an int32/uint32 device tensor of at least
+    ``blocks`` words (a measurement aid: time it to get the read rate)."""
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
+        raise ValueError("read_probe: contiguous device tensors expected")
+    if sink.numel() * sink.element_size() < 4 * blocks:
+        raise ValueError("read_probe: sink smaller than one word per block")
+    _check(lib().moe_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(blocks), sink.data_ptr(),
+                                _stream(device)), "moe_read_probe")
 
 
 def device_flags(clear: bool = False, device=None) -> set:

@@ -161,3 +161,18 @@ def test_forward_schedule_host_logic():
     assert mx.forward_schedule(cfg, 65) == "large"
     # hidden 1024 has no single-launch kernel: the three-launch schedule
     assert mx.forward_schedule(_cfg(hidden_size=1024, moe_intermediate=512, n_routed_experts=32), 1) == "tiny"
+
+
+def test_read_probe_host_checks():
+    """The measurement aid refuses bad arguments before launching anything."""
+    L = mx.lib()
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    p16 = (p + 15) & ~15
+    EINVAL = -1
+    assert L.moe_read_probe(None, 16, 1, p16, None) == EINVAL
+    assert L.moe_read_probe(p16, 16, 1, None, None) == EINVAL
+    assert L.moe_read_probe(p16, 16, 0, p16, None) == EINVAL
+    assert L.moe_read_probe(p16, 0, 1, p16, None) == EINVAL
+    assert L.moe_read_probe(p16 + 4, 16, 1, p16, None) == EINVAL
+    assert L.moe_read_probe(p16, 24, 1, p16, None) == EINVAL
