@@ -2,8 +2,8 @@
 intermediate 2048, MXFP4 routed experts, int8 shared expert), through the C
 ABI, in the same configuration the benchmark times:
 
-  decode T=1   several fresh token batches, every row
-  decode T=64  router bias N(0, 0.05) (mild expert skew), every row
+  decode T=1   several fresh token batches, every row (and T=2)
+  decode T=3, 17, 40, 64  router bias N(0, 0.05) (mild expert skew), every row
   prefill T=8192, per-expert logit offsets N(0, 0.5): routing of every token,
                outputs of sampled rows (tokens are independent)
   hash layer T=4096, Zipf(1.1) token ids: routing exact, sampled rows
@@ -83,6 +83,19 @@ def test_decode_t2_full(full_layer):
     assert mx.forward_schedule(mx.config_of(wl), 2) == "single"
     Lv, Dv = _variant(L, D, wl)
     _run(wl, Lv, Dv, 5)
+
+
+@pytest.mark.parametrize("T", [3, 17, 40])
+def test_decode_mid_t_full(full_layer, T):
+    """Decode batches between the single launch and 64 tokens at the full
+    shape: the fused streaming launch with routed tiles of 1-6 positions and
+    shared tiles of up to 16 tokens (T=3: one of 3; T=17: 16 and 1; T=40:
+    16, 16 and 8), every token against the oracle."""
+    L, D = full_layer
+    wl = dataclasses.replace(synth.WORKLOADS["decode_t64"], name=f"decode_t{T}", T=T)
+    assert mx.forward_schedule(mx.config_of(wl), T) == "decode"
+    Lv, Dv = _variant(L, D, wl)
+    _run(wl, Lv, Dv, T)
 
 
 def test_decode_t64_full(full_layer):
