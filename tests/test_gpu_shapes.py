@@ -1,0 +1,49 @@
+"""Hidden and intermediate sizes away from the model's: multiples of 128 that
+are not multiples of 256 or 1024 (the library accepts any multiple of 128).
+They take the paths the model's shapes never take: the router fallback,
+two-launch streaming passes with 3, 5 or 10 stages of 128 K-values, the
+per-slot GEMV schedule above 64 tokens where the hidden size is not a
+multiple of 256, and grouped GEMMs with odd stage counts and 3 or 5 N tiles.
+Every token against the oracle, bf16 output equal to the rounded fp32 one."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import assert_outputs_close, compare_routing, reference_rows
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("mxfp4_moe_expert_amd")
+
+DEV = "cuda"
+SHAPES = [(384, 640), (768, 640), (1280, 384)]  # (hidden, intermediate)
+TS = [1, 2, 5, 17, 64, 65, 200]
+_layers = {}
+
+
+def _layer(H, I):
+    if (H, I) not in _layers:
+        wl = synth.Workload(f"h{H}i{I}", T=200, H=H, E=32, k=6, I=I, V=900, bias_sigma=0.05, seed=H + I)
+        L = synth.make_layer(wl)
+        _layers[(H, I)] = (wl, L, mx.DeviceLayer.from_host(L, DEV), mx.config_of(wl))
+    return _layers[(H, I)]
+
+
+@pytest.mark.parametrize("T", TS)
+@pytest.mark.parametrize("H,I", SHAPES)
+def test_forward_odd_shapes(H, I, T):
+    wl, L, D, cfg = _layer(H, I)
+    print(f"[forward H={H} I={I} T={T} schedule {mx.forward_schedule(cfg, T)}]", flush=True)
+    xh = synth.make_tokens(wl, rep=T + 11, T=T)
+    x = mx.bf16_from_numpy(xh, DEV)
+    out, (ids, w) = mx.forward(cfg, x, D, out_fp32=True, return_routing=True)
+    out_bf = mx.forward(cfg, x, D, out_fp32=False)
+    torch.cuda.synchronize()
+    rows = np.arange(T, dtype=np.int32)
+    r, ref = reference_rows(L, xh, rows)
+    rt = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), r["ids"], r["w"], r["gap"], r["next"])
+    if rt["alt_rows"]:
+        r, ref = reference_rows(L, xh, rows, routing=rt)
+    assert_outputs_close(out.cpu().numpy(), ref, f"forward H={H} I={I} T={T}")
+    assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
