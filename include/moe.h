@@ -65,8 +65,9 @@
  *     the launchers check), the outputs that depend on it are NaN, the
  *     device flag MOE_FLAG_WAIT_EXPIRED is set, and the hand-off state stays
  *     consistent for the next call.
- *   - Supported shapes: H and I multiples of 128, 1 <= top_k <= 8,
- *     top_k <= E <= 256, 0 <= T <= 65536. Device pointers must be 16-byte
+ *   - Supported shapes: H and I multiples of 128 up to 8192, 1 <= top_k <=
+ *     8, top_k <= E <= 256, 0 <= T <= 65536 (other shapes: MOE_EUNSUPPORTED,
+ *     and moe_workspace_size returns 0). Device pointers must be 16-byte
  *     aligned.
  *   - Buffers a call writes (outputs, act, workspace) must not overlap each
  *     other or any buffer the call reads.

@@ -13,6 +13,7 @@ namespace {
 using namespace moe;
 
 constexpr int kMaxT = 65536;
+constexpr int kMaxDim = 8192;  // H and I: the largest whose activation and scale tiles fit a block's LDS
 constexpr size_t kActLdsBudget = 128 * 1024;  // activation tile bytes per block
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -27,8 +28,8 @@ struct Layout {
 bool cfg_ok(const moe_config* c) {
   if (!c) return false;
   const int H = c->hidden_size, E = c->n_routed_experts, k = c->top_k, I = c->moe_intermediate;
-  if (H < 128 || H % 128 || H > 16384) return false;
-  if (I < 128 || I % 128 || I > 16384) return false;
+  if (H < 128 || H % 128 || H > kMaxDim) return false;
+  if (I < 128 || I % 128 || I > kMaxDim) return false;
   if (k < 1 || k > kMaxTopK || E < k || E > kMaxExperts) return false;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
   if (!(c->swiglu_limit == c->swiglu_limit)) return false;
@@ -73,7 +74,10 @@ int routed_tile_n(const moe_config& c, int T) {
   if (use_gemm(c, T)) return kGemmTokens;
   const int K = c.hidden_size > c.moe_intermediate ? c.hidden_size : c.moe_intermediate;
   int tn = T <= 1 ? 1 : 6;
-  while (tn > 1 && (size_t)tn * (2 * (size_t)K + 16) > kActLdsBudget) --tn;
+  // the streaming unit holds the tile's rows and its 256 weight rows' scales
+  while (tn > 1 &&
+         ((size_t)tn * (2 * (size_t)K + 16) > kActLdsBudget || stream_unit_lds(tn, K, false) > kLdsBlockMax))
+    --tn;
   return tn;
 }
 
@@ -139,7 +143,13 @@ inline int* gemm_queue(void* ws, const Layout& L, int which) {
   return at<int32_t>(ws, L.counters) + kGemmQueueInts + 9 * which;
 }
 
-int status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+// A failed launch or runtime call: HIP's error state is cleared so that it
+// does not surface in the caller's next HIP call.
+int status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  (void)hipGetLastError();
+  return MOE_EHIP;
+}
 
 // Measurement hook (moe_set_kernel_events): events recorded around one kernel.
 int g_prof_kernel = MOE_KERNEL_NONE;
@@ -538,7 +548,9 @@ RouterArgs router_args(const moe_config& c, int T, const uint16_t* x, const floa
 // Routed w2 in 3-bit blocks runs in the fused streaming launch (T <= 64; both
 // stages' K multiples of 1024) or the grouped GEMM (T > 64; H a multiple of 256).
 bool w2q3_supported(const moe_config& c, int T) {
-  if (T <= kSmallT) return c.hidden_size % 1024 == 0 && c.moe_intermediate % 1024 == 0;
+  if (T <= kSmallT)  // the fused streaming launch, whose w2 units hold binary16 scale rows
+    return c.hidden_size % 1024 == 0 && c.moe_intermediate % 1024 == 0 &&
+           stream_unit_lds(routed_tile_n(c, T), c.moe_intermediate, true) <= kLdsBlockMax;
   return use_gemm(c, T);
 }
 
@@ -568,7 +580,8 @@ int schedule(const moe_config& c, int T, bool hash) {
   if (T * (c.top_k + 1) <= 16) {
     if (layer_small_supported(c.hidden_size, c.moe_intermediate, c.n_routed_experts, T, c.top_k))
       return MOE_SCHED_SINGLE;
-    if (!hash) return MOE_SCHED_TINY;
+    // the tiny schedule's last launch holds every column's h (T k slots + T tokens)
+    if (!hash && w2_combine_small_lds(T, c.top_k, c.moe_intermediate) <= kLdsBlockMax) return MOE_SCHED_TINY;
   }
   if (T <= kSmallT) return MOE_SCHED_DECODE;
   return MOE_SCHED_LARGE;

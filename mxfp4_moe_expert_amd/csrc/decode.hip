@@ -13,6 +13,8 @@ __global__ __launch_bounds__(kThreads) void k_w2_combine_small(W2CombineArgs a) 
   w2_combine_block<kWaves, MAXU, MAXS, MAXA>(a, blockIdx.x, lds);
 }
 
+size_t w2_combine_small_lds(int T, int k, int I) { return w2c_lds_bytes(T, k, I, kWaves, false); }
+
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
   const int ncols = a.T * (a.k + 1);

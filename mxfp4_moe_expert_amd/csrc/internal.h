@@ -284,6 +284,13 @@ hipError_t launch_stream_fused(const SkinnyArgs& a13, const SkinnyArgs& b13, con
 // Tile records and queue reset for tiles built by launch_tiles_from_offsets.
 hipError_t launch_tile_records(const Perm& p, const float* slot_w, hipStream_t st);
 hipError_t launch_w2_combine_small(const W2CombineArgs& a, hipStream_t st);
+// LDS bytes of k_w2_combine_small for T tokens of k slots at intermediate I
+// (at most 160 KB fit a block).
+size_t w2_combine_small_lds(int T, int k, int I);
+// LDS bytes of one streaming unit over K input features with tile_n
+// activation rows (the routed tile, plus the unit's 256 rows of scales).
+size_t stream_unit_lds(int tile_n, int K, bool q3);
+constexpr size_t kLdsBlockMax = 160 * 1024;  // LDS one block can have on gfx950
 // Hand-off region of the single-launch layer, at a fixed offset at the start
 // of every workspace (zero on first use): per-block layer counters, then two
 // buffers, used by alternate layers, of router scores, h columns and (for

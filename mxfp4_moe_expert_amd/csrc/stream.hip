@@ -594,6 +594,10 @@ static hipError_t launch_stream_t(const SkinnyArgs& a, int a_blocks, const Skinn
   return hipGetLastError();
 }
 
+size_t stream_unit_lds(int tile_n, int K, bool q3) {
+  return (size_t)tile_n * (2 * (size_t)K + 16) + kUnitRows * (size_t)stream_scale_row(K, q3);
+}
+
 static size_t stream_lds(const SkinnyArgs& a, int a_blocks, const SkinnyArgs& b, int b_blocks) {
   size_t lds = 0;
   if (a_blocks > 0)

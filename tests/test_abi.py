@@ -176,3 +176,21 @@ def test_read_probe_host_checks():
     assert L.moe_read_probe(p16, 0, 1, p16, None) == EINVAL
     assert L.moe_read_probe(p16 + 4, 16, 1, p16, None) == EINVAL
     assert L.moe_read_probe(p16, 24, 1, p16, None) == EINVAL
+
+
+def test_shape_cap_and_schedules():
+    """H and I up to 8192 are accepted, larger ones rejected up front; where
+    the tiny schedule's w2 launch would not fit a block's LDS (large I with
+    several columns) the decode schedule is taken instead."""
+    L = mx.lib()
+    for H, I, ok in ((8192, 8192, True), (8192 + 128, 256, False), (256, 8192 + 128, False),
+                     (16384, 256, False), (256, 16384, False)):
+        cfg = _cfg(hidden_size=H, moe_intermediate=I, n_routed_experts=8, top_k=2)
+        assert (L.moe_workspace_size(ctypes.byref(cfg), 5) > 0) == ok, (H, I)
+        if not ok:
+            assert L.moe_forward_schedule(ctypes.byref(cfg), 5, 0) == mx.MOE_EUNSUPPORTED
+    small = _cfg(hidden_size=256, moe_intermediate=256, n_routed_experts=8, top_k=2)
+    big_i = _cfg(hidden_size=256, moe_intermediate=8192, n_routed_experts=8, top_k=2)
+    assert mx.forward_schedule(small, 5) == "tiny"
+    assert mx.forward_schedule(big_i, 1) == "tiny"   # 3 columns of 16 KB fit
+    assert mx.forward_schedule(big_i, 5) == "decode"  # 15 columns do not

@@ -1,5 +1,6 @@
 """Hidden and intermediate sizes away from the model's: multiples of 128 that
-are not multiples of 256 or 1024 (the library accepts any multiple of 128).
+are not multiples of 256 or 1024 (the library accepts any multiple of 128 up
+to 8192), and the largest accepted sizes.
 They take the paths the model's shapes never take: the router fallback,
 two-launch streaming passes with 3, 5 or 10 stages of 128 K-values, the
 per-slot GEMV schedule above 64 tokens where the hidden size is not a
@@ -47,3 +48,38 @@ def test_forward_odd_shapes(H, I, T):
         r, ref = reference_rows(L, xh, rows, routing=rt)
     assert_outputs_close(out.cpu().numpy(), ref, f"forward H={H} I={I} T={T}")
     assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
+
+
+# The largest accepted sizes (8192) and one just below them that is not a
+# multiple of 256: streaming units whose tile width is cut so that the
+# tile's rows and 256 rows of scales fit a block's LDS, the tiny schedule
+# only where its w2 launch fits (else the decode schedule), GEMMs with
+# K = 8192. Top-2 of 8 experts keeps the oracle quick.
+BIG = [((8192, 256), [1, 2, 5, 17, 64, 65, 130]), ((256, 8192), [1, 2, 5, 17, 64, 65, 130]),
+       ((8064, 384), [1, 17, 65, 130]), ((8192, 8192), [1, 5, 17])]
+_big = {}
+
+
+def _big_layer(H, I):
+    if (H, I) not in _big:
+        wl = synth.Workload(f"big{H}x{I}", T=130, H=H, E=8, k=2, I=I, V=900, bias_sigma=0.05, seed=H + 3 * I)
+        L = synth.make_layer(wl)
+        _big.clear()  # one large layer on the device at a time
+        _big[(H, I)] = (wl, L, mx.DeviceLayer.from_host(L, DEV), mx.config_of(wl))
+    return _big[(H, I)]
+
+
+@pytest.mark.parametrize("H,I,T", [(h, i, t) for (h, i), ts in BIG for t in ts])
+def test_forward_largest_shapes(H, I, T):
+    wl, L, D, cfg = _big_layer(H, I)
+    print(f"[forward H={H} I={I} T={T} schedule {mx.forward_schedule(cfg, T)}]", flush=True)
+    xh = synth.make_tokens(wl, rep=T + 13, T=T)
+    x = mx.bf16_from_numpy(xh, DEV)
+    out, (ids, w) = mx.forward(cfg, x, D, out_fp32=True, return_routing=True)
+    torch.cuda.synchronize()
+    rows = np.arange(T, dtype=np.int32)
+    r, ref = reference_rows(L, xh, rows)
+    rt = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), r["ids"], r["w"], r["gap"], r["next"])
+    if rt["alt_rows"]:
+        r, ref = reference_rows(L, xh, rows, routing=rt)
+    assert_outputs_close(out.cpu().numpy(), ref, f"forward H={H} I={I} T={T}")
