@@ -104,29 +104,43 @@ hipError_t launch_w13_deep(const SkinnyArgs& a, int blocks, hipStream_t st) {
 // ---------------------------------------------------------------- combine
 
 // out[t][n] = sum_{j<k} ybuf[t*k+j][n] (+ zbuf[t][n]), slots in order; ybuf
-// fp32, or bf16 (y_bf16) as the large-batch GEMMs write it.
+// fp32, or bf16 (y_bf16) as the large-batch GEMMs write it. The slot count
+// is a template argument so that a thread requests all of its k slot pieces
+// and its shared piece before the first add: with a loop over a run-time k,
+// each piece was requested only after the previous one had arrived (seven
+// dependent memory round trips per thread at k = 6). The additions keep the
+// slot order, then the shared piece, so the sums are unchanged.
+template <int KS>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
   const size_t n4 = (size_t)a.T * a.H / 4;
   if (i4 >= n4) return;
   const size_t t = i4 * 4 / a.H, n = i4 * 4 - t * a.H;
+  float4 y[KS];
+  if (a.y_bf16) {
+    uint2 v[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      v[j] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ybuf) + (t * KS + j) * a.H + n);
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      y[j] = make_float4(bf16_to_f32(v[j].x & 0xffffu), bf16_to_f32(v[j].x >> 16), bf16_to_f32(v[j].y & 0xffffu),
+                         bf16_to_f32(v[j].y >> 16));
+  } else {
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      y[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.ybuf) + (t * KS + j) * a.H + n);
+  }
+  const float4 z = a.zbuf ? *reinterpret_cast<const float4*>(a.zbuf + t * a.H + n) : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < a.k; ++j) {
-    float4 y;
-    if (a.y_bf16) {
-      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ybuf) + (t * a.k + j) * a.H + n);
-      y = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffffu),
-                      bf16_to_f32(v.y >> 16));
-    } else {
-      y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.ybuf) + (t * a.k + j) * a.H + n);
-    }
-    acc.x += y.x;
-    acc.y += y.y;
-    acc.z += y.z;
-    acc.w += y.w;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    acc.x += y[j].x;
+    acc.y += y[j].y;
+    acc.z += y[j].z;
+    acc.w += y[j].w;
   }
   if (a.zbuf) {
-    const float4 z = *reinterpret_cast<const float4*>(a.zbuf + t * a.H + n);
     acc.x += z.x;
     acc.y += z.y;
     acc.z += z.z;
@@ -145,7 +159,18 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const size_t n4 = (size_t)a.T * a.H / 4;
   if (n4 == 0) return hipSuccess;
-  k_combine<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a);
+  const unsigned blocks = (unsigned)((n4 + 255) / 256);
+  switch (a.k) {
+    case 1: k_combine<1><<<blocks, 256, 0, st>>>(a); break;
+    case 2: k_combine<2><<<blocks, 256, 0, st>>>(a); break;
+    case 3: k_combine<3><<<blocks, 256, 0, st>>>(a); break;
+    case 4: k_combine<4><<<blocks, 256, 0, st>>>(a); break;
+    case 5: k_combine<5><<<blocks, 256, 0, st>>>(a); break;
+    case 6: k_combine<6><<<blocks, 256, 0, st>>>(a); break;
+    case 7: k_combine<7><<<blocks, 256, 0, st>>>(a); break;
+    case 8: k_combine<8><<<blocks, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
