@@ -177,13 +177,25 @@ __global__ __launch_bounds__(kDecExperts * 64) void k_router_dec(RouterArgs a) {
 #pragma unroll
   for (int j = 0; j < per; ++j) *reinterpret_cast<uint4*>(xs + (size_t)(tid + kDecExperts * 64 * j) * 8) = v[j];
   __syncthreads();
+  // token t's row pieces are read from LDS while token t-1's products are
+  // formed (a scheduling barrier keeps the reads there: left alone, the
+  // compiler requested two pieces at a time and waited for each pair)
   float acc[kDecTokens];
+  uint4 xb[2][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) xb[0][c] = *reinterpret_cast<const uint4*>(xs + c * 512 + lane * 8);
 #pragma unroll
   for (int t = 0; t < kDecTokens; ++t) {
+    if (t + 1 < kDecTokens) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        xb[(t + 1) & 1][c] = *reinterpret_cast<const uint4*>(xs + (t + 1) * H + c * 512 + lane * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     acc[t] = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * H + c * 512 + lane * 8);
+      const uint4 xv = xb[t & 1][c];
       const float4 w0 = w[2 * c], w1 = w[2 * c + 1];
       float s = acc[t];
       s += bf16_to_f32(xv.x & 0xffff) * w0.x;
@@ -349,51 +361,92 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_dec(RouterArgs a, Perm p,
 // ---------------------------------------------------------------- hash router
 
 // One wave per token: ids from the table row, scores of those experts only.
+// NC = ceil(H / 512): lane l holds elements 512 c + 8 l .. +8 (c < NC) of the
+// token row and of one expert's router row. The k table entries come in one
+// load (lane j < k reads entry j), and each expert's row pieces are requested
+// together, the next expert's before this one's products are formed (one
+// expert at a time when NC > 8: two rows of 16 pieces would not fit the
+// registers). Before, the loop over a run-time H and the per-expert table
+// loads made about 50 dependent memory round trips per wave (47 us at 4096
+// tokens). The products are added in the same order as before; lanes past H
+// add zeros.
+template <int NC>
 __global__ __launch_bounds__(256) void k_hash_route(HashArgs a) {
+  constexpr int NB = NC <= 8 ? 2 : 1;  // router rows in flight
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= a.T) return;
+  const int H = a.H, k = a.k;
   // a token id outside [0, V) or a table entry outside [0, E) is flagged;
   // the token then reads table row 0 / router row 0 (nothing is indexed out
   // of range), keeps in-range ids and gets NaN weights
   const int tok = a.token_ids[t];
   const bool tok_ok = (unsigned)tok < (unsigned)a.V;
-  const int32_t* row = a.tid2eid + (size_t)(tok_ok ? tok : 0) * a.k;
-  const uint16_t* xt = a.x + (size_t)t * a.H;
-  float s[kMaxTopK];
+  const int32_t* row = a.tid2eid + (size_t)(tok_ok ? tok : 0) * k;
+  const int my_e = lane < k ? row[lane] : 0;
+  const uint16_t* xt = a.x + (size_t)t * H;
+  // pieces past H (H a multiple of 128, not of 512) read in-range addresses
+  // and take zero activations, so every load is unconditional (per-lane
+  // branches around them made the compiler wait for every load at each one)
+  // and the extra products add zeros
+  uint4 xv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k0 = c * 512 + lane * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + min(k0, H - 8));
+    xv[c] = k0 < H ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
   int ids[kMaxTopK];
   bool ent_ok = true;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    ids[j] = 0;
+    if (j >= k) continue;  // uniform
+    const int e = __builtin_amdgcn_readlane(my_e, j);
+    const bool e_ok = (unsigned)e < (unsigned)a.E;
+    ent_ok = ent_ok && e_ok;
+    ids[j] = e_ok ? e : 0;
+  }
+  float4 wr[NB][NC][2];
+  auto request = [&](int j, float4 (&w)[NC][2]) __attribute__((always_inline)) {
+    const float* we = a.gate_w + (size_t)ids[j] * H;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k0 = min(c * 512 + lane * 8, H - 8);
+      w[c][0] = *reinterpret_cast<const float4*>(we + k0);
+      w[c][1] = *reinterpret_cast<const float4*>(we + k0 + 4);
+    }
+  };
+  request(0, wr[0]);
+  float s[kMaxTopK];
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     s[j] = 0.0f;
-    ids[j] = 0;
-    if (j >= a.k) continue;
-    const int e = row[j];
-    const bool e_ok = (unsigned)e < (unsigned)a.E;
-    ent_ok = ent_ok && e_ok;
-    ids[j] = e_ok ? e : 0;
-    const float* we = a.gate_w + (size_t)ids[j] * a.H;
+    if (j >= k) continue;
+    if (NB == 2 && j + 1 < k) request(j + 1, wr[(j + 1) % NB]);
+    __builtin_amdgcn_sched_barrier(0);
     float acc = 0.0f;
-    for (int k0 = lane * 8; k0 < a.H; k0 += 512) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xt + k0);
-      const float4 w0 = *reinterpret_cast<const float4*>(we + k0);
-      const float4 w1 = *reinterpret_cast<const float4*>(we + k0 + 4);
-      acc += bf16_to_f32(xv.x & 0xffff) * w0.x;
-      acc += bf16_to_f32(xv.x >> 16) * w0.y;
-      acc += bf16_to_f32(xv.y & 0xffff) * w0.z;
-      acc += bf16_to_f32(xv.y >> 16) * w0.w;
-      acc += bf16_to_f32(xv.z & 0xffff) * w1.x;
-      acc += bf16_to_f32(xv.z >> 16) * w1.y;
-      acc += bf16_to_f32(xv.w & 0xffff) * w1.z;
-      acc += bf16_to_f32(xv.w >> 16) * w1.w;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 x = xv[c];
+      const float4 w0 = wr[j % NB][c][0], w1 = wr[j % NB][c][1];
+      acc += bf16_to_f32(x.x & 0xffff) * w0.x;
+      acc += bf16_to_f32(x.x >> 16) * w0.y;
+      acc += bf16_to_f32(x.y & 0xffff) * w0.z;
+      acc += bf16_to_f32(x.y >> 16) * w0.w;
+      acc += bf16_to_f32(x.z & 0xffff) * w1.x;
+      acc += bf16_to_f32(x.z >> 16) * w1.y;
+      acc += bf16_to_f32(x.w & 0xffff) * w1.z;
+      acc += bf16_to_f32(x.w >> 16) * w1.w;
     }
+    if (NB == 1 && j + 1 < k) request(j + 1, wr[0]);
     s[j] = sqrtf(softplus(wave_sum(acc)));
     sum += s[j];
   }
   const bool ok = tok_ok && ent_ok;
   if (!ok && lane == 0 && a.flags) atomicOr(a.flags, (tok_ok ? 0u : kFlagTokenId) | (ent_ok ? 0u : kFlagTableEntry));
-  if (lane < a.k) {
+  if (lane < k) {
     float sj = s[0];
     int ej = ids[0];
 #pragma unroll
@@ -402,8 +455,8 @@ __global__ __launch_bounds__(256) void k_hash_route(HashArgs a) {
         sj = s[j];
         ej = ids[j];
       }
-    a.ids[(size_t)t * a.k + lane] = ej;
-    a.w[(size_t)t * a.k + lane] = ok ? a.scale * sj / sum : __builtin_nanf("");
+    a.ids[(size_t)t * k + lane] = ej;
+    a.w[(size_t)t * k + lane] = ok ? a.scale * sj / sum : __builtin_nanf("");
   }
 }
 
@@ -458,7 +511,26 @@ hipError_t launch_topk_permute_small(const RouterArgs& r, const Perm& p, int* ar
 
 hipError_t launch_hash_route(const HashArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
-  k_hash_route<<<(a.T + 3) / 4, 256, 0, st>>>(a);
+  const unsigned blocks = (unsigned)((a.T + 3) / 4);
+  switch ((a.H + 511) / 512) {
+    case 1: k_hash_route<1><<<blocks, 256, 0, st>>>(a); break;
+    case 2: k_hash_route<2><<<blocks, 256, 0, st>>>(a); break;
+    case 3: k_hash_route<3><<<blocks, 256, 0, st>>>(a); break;
+    case 4: k_hash_route<4><<<blocks, 256, 0, st>>>(a); break;
+    case 5: k_hash_route<5><<<blocks, 256, 0, st>>>(a); break;
+    case 6: k_hash_route<6><<<blocks, 256, 0, st>>>(a); break;
+    case 7: k_hash_route<7><<<blocks, 256, 0, st>>>(a); break;
+    case 8: k_hash_route<8><<<blocks, 256, 0, st>>>(a); break;
+    case 9: k_hash_route<9><<<blocks, 256, 0, st>>>(a); break;
+    case 10: k_hash_route<10><<<blocks, 256, 0, st>>>(a); break;
+    case 11: k_hash_route<11><<<blocks, 256, 0, st>>>(a); break;
+    case 12: k_hash_route<12><<<blocks, 256, 0, st>>>(a); break;
+    case 13: k_hash_route<13><<<blocks, 256, 0, st>>>(a); break;
+    case 14: k_hash_route<14><<<blocks, 256, 0, st>>>(a); break;
+    case 15: k_hash_route<15><<<blocks, 256, 0, st>>>(a); break;
+    case 16: k_hash_route<16><<<blocks, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -153,20 +153,34 @@ __global__ __launch_bounds__(kRmThreads) void k_router_mfma(RouterMfmaArgs a) {
 }
 
 // One wave per token: logits from the partial sums, then scores, selection
-// values and the top-k.
-__global__ __launch_bounds__(256) void k_topk_sum(RouterArgs a, const float* __restrict__ plog, int KS) {
+// values and the top-k. The slice count is a template argument so that a
+// lane requests all of its partial logits, offsets and biases before the
+// first add: with a loop over a run-time count each load was issued only
+// after the previous one had arrived (20 dependent round trips per wave at
+// four slices). The sums keep the slice order, then the offset.
+template <int KS>
+__global__ __launch_bounds__(256) void k_topk_sum(RouterArgs a, const float* __restrict__ plog) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;
-  TopkRow row;
+  float part[4][KS], off[4], bias[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = min(lane + 64 * q, a.E - 1);  // surplus lanes get key 0 inside the selection
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) part[q][ks] = plog[((size_t)ks * a.T + t) * a.E + e];
+    off[q] = a.logit_offset ? a.logit_offset[e] : 0.0f;
+    bias[q] = a.bias[e];
+  }
+  TopkRow row;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
     float logit = 0.0f;
-    for (int ks = 0; ks < KS; ++ks) logit += plog[((size_t)ks * a.T + t) * a.E + e];
-    if (a.logit_offset) logit += a.logit_offset[e];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) logit += part[q][ks];
+    if (a.logit_offset) logit += off[q];
     row.s[q] = sqrtf(softplus(logit));
-    row.b[q] = row.s[q] + a.bias[e];
+    row.b[q] = row.s[q] + bias[q];
   }
   wave_topk_row(row, a.E, a.k, a.scale, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, nullptr);
 }
@@ -197,7 +211,14 @@ hipError_t launch_router_mfma(const RouterArgs& r, uint16_t* wsplit, float* plog
   k_router_mfma<<<(unsigned)(tiles * a.KS), kRmThreads, 0, st>>>(a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  k_topk_sum<<<(unsigned)((r.T + 3) / 4), 256, 0, st>>>(r, plog, a.KS);
+  const unsigned blocks = (unsigned)((r.T + 3) / 4);
+  switch (a.KS) {
+    case 1: k_topk_sum<1><<<blocks, 256, 0, st>>>(r, plog); break;
+    case 2: k_topk_sum<2><<<blocks, 256, 0, st>>>(r, plog); break;
+    case 4: k_topk_sum<4><<<blocks, 256, 0, st>>>(r, plog); break;
+    case 8: k_topk_sum<8><<<blocks, 256, 0, st>>>(r, plog); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -83,3 +83,34 @@ def test_forward_largest_shapes(H, I, T):
     if rt["alt_rows"]:
         r, ref = reference_rows(L, xh, rows, routing=rt)
     assert_outputs_close(out.cpu().numpy(), ref, f"forward H={H} I={I} T={T}")
+
+
+# Hash layers above 64 tokens at hidden sizes that are not multiples of 512:
+# the hash router's last row piece is partly past the hidden size on some
+# lanes (those lanes read in-range addresses and add zero products). Ids
+# bit-exact with the table, weights within 1e-5, every token's output
+# against the oracle.
+@pytest.mark.parametrize("T", [65, 200])
+@pytest.mark.parametrize("H,I", SHAPES)
+def test_hash_odd_hidden(H, I, T):
+    import dataclasses
+
+    import oracle
+
+    wl, L, D, cfg = _layer(H, I)
+    wlh = dataclasses.replace(wl, name=f"h{H}i{I}hash", hash_layer=True)
+    Lh = synth.make_layer(wlh)
+    Dh = mx.DeviceLayer.from_host(Lh, DEV)
+    cfgh = mx.config_of(wlh)
+    print(f"[hash H={H} I={I} T={T} schedule {mx.forward_schedule(cfgh, T, hash_layer=True)}]", flush=True)
+    xh = synth.make_tokens(wlh, rep=T + 5, T=T)
+    tid_h = synth.make_token_ids(wlh, rep=T + 5, T=T)
+    x = mx.bf16_from_numpy(xh, DEV)
+    tids = torch.from_numpy(tid_h).to(DEV)
+    out, (ids, w) = mx.forward(cfgh, x, Dh, token_ids=tids, out_fp32=True, return_routing=True)
+    torch.cuda.synchronize()
+    r = oracle.forward(Lh, xh, token_ids=tid_h)
+    assert np.array_equal(ids.cpu().numpy(), Lh.tid2eid[tid_h])
+    assert np.array_equal(r["ids"], Lh.tid2eid[tid_h])
+    assert np.abs(w.cpu().numpy() - r["w"]).max() <= 1e-5
+    assert_outputs_close(out.cpu().numpy(), r["out"], f"hash H={H} I={I} T={T}")
