@@ -330,6 +330,77 @@ def _write_bytes(path, match):
     return 32 * (n["TCC_EA0_WRREQ_sum"] - w64) + 64 * w64, n
 
 
+# Algorithmic flops of the grouped-GEMM launches of the large-batch schedule,
+# by the template arguments rocprofv3 prints (<format, mode>: format 0 MXFP4,
+# 1 int8, 2 3-bit; mode 0 w13 + SwiGLU, 1 routed w2, 2 shared w2 + combine)
+# and the learned router's MFMA launch (three bf16 planes: 3x executed).
+def _gemm_flops(kernel, wl):
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    m = re.search(r"k_gemm<(\d), (\d)>", kernel)
+    if m:
+        fmt, mode = int(m.group(1)), int(m.group(2))
+        rows = T * k if fmt != 1 else T  # routed slots or tokens (shared expert)
+        return 2.0 * rows * H * 2 * I if mode == 0 else 2.0 * rows * I * H
+    if "k_router_mfma" in kernel:
+        return 2.0 * T * E * H
+    return None
+
+
+def per_kernel_counters(workload, outdir, r_fac, w_fac, stats, commands):
+    """profiles/<workload>_counters_per_kernel.md: for every library kernel of
+    the counter runs, the mean per dispatch of MfmaUtil, executed bf16 MFMA
+    flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), LDS bank-conflict and active
+    cycles and HBM bytes (EA request counts by size, copy-calibrated), with
+    the kernel-trace duration and, for the grouped GEMMs and the router, the
+    algorithmic TFLOP/s and its fraction of the 2.5 PFLOP/s bf16 peak."""
+    import synth
+
+    wl = synth.WORKLOADS[workload]
+    rd = _csv_rows(_find(outdir, "pmc_read", "counter_collection.csv"))
+    wr = _csv_rows(_find(outdir, "pmc_write", "counter_collection.csv"))
+    vals = {}
+    for rows in (rd, wr):
+        for r in rows:
+            if "moe::" in r["Kernel_Name"]:
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    dur = {}
+    for r in stats or []:
+        dur[r["Name"]] = float(r["AverageNs"]) / 1e3
+    lines = [f"# Counters per kernel, moe_forward, workload {workload}", "",
+             "Mean per dispatch. HBM bytes: 32/64/128-byte EA read requests and 32/64-byte write requests, "
+             f"each scaled by what the same counters read for a copy of {COPY_CAL_BYTES} bytes "
+             f"(read factor {r_fac:.4f}, write factor {w_fac:.4f}). Executed bf16 flops count every MFMA "
+             "the kernel issued (the router's three planes, padded tile positions); algorithmic flops are "
+             "the layer's own (2 per multiply-add of the routed slots or tokens).", "",
+             "Commands:", "", "```"] + [commands[c] for c in ("pmc_read", "pmc_write", "kernel_trace") if c in commands] + [
+             "```", "",
+             "| kernel | dispatches | us (trace) | MfmaUtil % | executed bf16 TFLOP/s | algorithmic TFLOP/s | "
+             "frac of 2.5 PF | LDS conflict cycles | LDS active cycles | HBM read MB | HBM write MB |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    order = sorted(vals, key=lambda k: -dur.get(k, 0.0))
+    for kname in order:
+        v = {c: sum(x) / len(x) for c, x in vals[kname].items()}
+        n = len(vals[kname].get("MfmaUtil", vals[kname][next(iter(vals[kname]))]))
+        us = dur.get(kname)
+        rb = (32 * v.get("TCC_EA0_RDREQ_32B_sum", 0) + 64 * v.get("TCC_EA0_RDREQ_64B_sum", 0)
+              + 128 * v.get("TCC_EA0_RDREQ_128B_sum", 0)) * r_fac
+        w64 = v.get("TCC_EA0_WRREQ_64B_sum", 0)
+        wb = (32 * (v.get("TCC_EA0_WRREQ_sum", 0) - w64) + 64 * w64) * w_fac
+        ex = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512.0
+        alg = _gemm_flops(kname, wl)
+        name = kname.split("(")[0].replace("void ", "")
+        cells = [f"`{name}`", str(n), f"{us:.1f}" if us else "-", f"{v.get('MfmaUtil', 0):.1f}",
+                 f"{ex / (us * 1e6):.1f}" if us and ex else "-",
+                 f"{alg / (us * 1e6):.1f}" if us and alg else "-",
+                 f"{alg / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12):.3f}" if us and alg else "-",
+                 f"{v.get('SQ_LDS_BANK_CONFLICT', 0):.0f}", f"{v.get('SQ_LDS_IDX_ACTIVE', 0):.0f}",
+                 f"{rb / 1e6:.1f}", f"{wb / 1e6:.1f}"]
+        lines.append("| " + " | ".join(cells) + " |")
+    with open(os.path.join(ROOT, "profiles", f"{workload}_counters_per_kernel.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize(workload, outdir, commands):
     """Turn one workload's rocprofv3 runs into the committed summaries:
     profiles/moe_forward_<workload>_kernels.md (per-kernel durations) and,
@@ -396,6 +467,7 @@ def summarize(workload, outdir, commands):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+    per_kernel_counters(workload, outdir, r_fac, w_fac, stats, commands)
 
 
 def cpu_leg(layer, batches, tids, budget_s, gpu_out32, gpu_ids, fwd=None):
