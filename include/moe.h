@@ -314,7 +314,9 @@ int moe_forward_stack(const moe_config* cfg, int32_t n_layers, const moe_layer_w
  * in the library's device memory, one per GPU, held until the process ends
  * (moe_noalloc_max_bytes() bytes, 16 MiB: enough for T <= 64 at the full
  * shape). The first call on a device zero-fills it on `stream` (and waits,
- * unless the stream is being captured). It allocates nothing and calls no
+ * unless the stream is being captured), and so does the first call after one
+ * that returned MOE_EHIP (a failed launch can leave its counters non-zero).
+ * It allocates nothing and calls no
  * allocating routine. Every call on one GPU shares that GPU's scratch: calls
  * that overlap in time on one GPU (different streams, no ordering) race;
  * order them on one stream. Returns MOE_EWORKSPACE, launching nothing, when

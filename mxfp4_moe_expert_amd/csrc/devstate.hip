@@ -49,24 +49,35 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 void* g_scratch_ptr[kMaxDevices];
+// a call on this device failed after it may have launched kernels: counters
+// in the scratch may be left non-zero, so the next call zero-fills it again
+bool g_scratch_dirty[kMaxDevices];
 }  // namespace
 
 // The current device's scratch address, set up on first use: the symbol's
 // address, then one zero fill (the workspace contract: zero before its first
-// use), queued on `st` and, unless `st` is being captured, waited for.
-static void* scratch_for_current_device(hipStream_t st) {
+// use), queued on `st` and, unless `st` is being captured, waited for. The
+// fill is repeated on the first call after a failed one.
+static void* scratch_for_current_device(hipStream_t st, int* dev_out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  *dev_out = dev;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
-  void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  if (g_scratch_ptr[dev] && !g_scratch_dirty[dev]) return g_scratch_ptr[dev];
+  void* p = g_scratch_ptr[dev];
+  if (!p && (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)) return nullptr;
   if (launch_fill_zero(p, kScratchBytes, st) != hipSuccess) return nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cs) != hipSuccess) return nullptr;
   if (cs == hipStreamCaptureStatusNone && hipStreamSynchronize(st) != hipSuccess) return nullptr;
   g_scratch_ptr[dev] = p;
+  g_scratch_dirty[dev] = false;
   return p;
+}
+
+static void mark_scratch_dirty(int dev) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_scratch_dirty[dev] = true;
 }
 
 }  // namespace moe
@@ -87,9 +98,12 @@ extern "C" int moe_forward_noalloc(const moe_config* cfg, int32_t T, const uint1
   if (need > moe::kScratchBytes) return MOE_EWORKSPACE;  // beyond the fixed scratch: use moe_forward
   if (T == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  void* ws = moe::scratch_for_current_device(st);
+  int dev = 0;
+  void* ws = moe::scratch_for_current_device(st, &dev);
   if (!ws) return MOE_EHIP;
-  return moe_forward(cfg, T, x, gate_w, bias, logit_offset, token_ids, tid2eid, V, w13_codes, w13_scales, w2_codes,
-                     w2_scales, sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, out, out_is_fp32, topk_ids_out, topk_w_out,
-                     ws, moe::kScratchBytes, stream);
+  const int rc = moe_forward(cfg, T, x, gate_w, bias, logit_offset, token_ids, tid2eid, V, w13_codes, w13_scales,
+                             w2_codes, w2_scales, sh_w13, sh_w13_scale, sh_w2, sh_w2_scale, out, out_is_fp32,
+                             topk_ids_out, topk_w_out, ws, moe::kScratchBytes, stream);
+  if (rc == MOE_EHIP) moe::mark_scratch_dirty(dev);
+  return rc;
 }
