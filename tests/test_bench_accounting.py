@@ -54,3 +54,26 @@ def test_prefill_and_hash_flops():
         assert a["layer_flops"] == 2 * T * (K + 1) * (H * 2 * I + I * H)
         assert a["layer_flops"] == want
         assert a["w13_flops"] == 2 * T * K * H * 2 * I
+
+
+def test_per_kernel_gemm_flops_sum_to_the_layer():
+    """The per-kernel counter table prices each grouped GEMM of the large-batch
+    schedule by its template arguments (format, mode): routed w13 and w2 over
+    T*k slots, shared w13 and w2 + combine over T tokens. Their sum is the
+    layer's expert flops, and the routed w13 figure is the dominant kernel's;
+    the router is 2 flop per multiply-add of T x E x H."""
+    wl = synth.WORKLOADS["prefill_t8192"]
+    T = wl.T
+    ids = np.zeros((1, T, K), dtype=np.int32)
+    a = bench.algorithmic(wl, ids)
+    names = {k: f"void moe::k_gemm<{k[0]}, {k[1]}>(moe::GemmArgs)" for k in ((0, 0), (0, 1), (1, 0), (1, 2))}
+    f = {k: bench._gemm_flops(n, wl) for k, n in names.items()}
+    assert f[(0, 0)] == a["w13_flops"] == 2.0 * T * K * H * 2 * I
+    assert f[(0, 1)] == a["w2_flops"] == 2.0 * T * K * I * H
+    assert f[(1, 0)] == 2.0 * T * H * 2 * I
+    assert f[(1, 2)] == 2.0 * T * I * H
+    assert sum(f.values()) == a["layer_flops"]
+    assert bench._gemm_flops("moe::k_router_mfma(moe::RouterMfmaArgs)", wl) == a["router_flops"]
+    # the 3-bit routed w2 GEMM (format 2) is priced as the MXFP4 one
+    assert bench._gemm_flops("void moe::k_gemm<2, 1>(moe::GemmArgs)", wl) == f[(0, 1)]
+    assert bench._gemm_flops("moe::k_perm_count(moe::PermArgs)", wl) is None
