@@ -62,3 +62,29 @@ def test_forward_max_tokens():
     print(f"[forward T={T}] oracle outputs for {len(rows)} rows", flush=True)
     _, ref = reference_rows(L, xh, rows, routing=rt)
     assert_outputs_close(out.cpu().numpy()[rows], ref, f"forward T={T}")
+
+
+def test_forward_two_router_slices():
+    """20,000 tokens (157 token tiles): the learned router's GEMM splits K in
+    two slices, the only batch sizes (16,257-32,640 tokens) where it does, and
+    the top-k adds the two partial logits. Routing of every token against the
+    oracle, outputs of 256 evenly spread rows, a second call repeats the bits."""
+    T2 = 20000
+    wl = synth.Workload("tiny_t20000", T=T2, H=256, E=16, k=6, I=128, V=1000, bias_sigma=0.05, seed=5)
+    L = synth.make_layer(wl)
+    D = mx.DeviceLayer.from_host(L, DEV)
+    cfg = mx.config_of(wl)
+    assert mx.forward_schedule(cfg, T2) == "large"
+    print(f"[forward T={T2}] gpu", flush=True)
+    xh = synth.make_tokens(wl, rep=2, T=T2)
+    x = mx.bf16_from_numpy(xh, DEV)
+    out, (ids, w) = mx.forward(cfg, x, D, out_fp32=True, return_routing=True)
+    again = mx.forward(cfg, x, D, out_fp32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    print(f"[forward T={T2}] routing of every token", flush=True)
+    oi, ow, og, on = oracle.route(xh, L.gate_w, L.bias, L.logit_offset, k=wl.k)
+    rt = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), oi, ow, og, on)
+    rows = np.unique(np.linspace(0, T2 - 1, 256).astype(np.int32))
+    _, ref = reference_rows(L, xh, rows, routing=rt)
+    assert_outputs_close(out.cpu().numpy()[rows], ref, f"forward T={T2}")

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 mx = pytest.importorskip("mxfp4_moe_expert_amd")
 
 DEV = "cuda"
-CASES = [(1, 8), (2, 16), (4, 64), (8, 64), (8, 256)]  # (top_k, experts)
+CASES = [(1, 8), (2, 16), (3, 32), (4, 64), (5, 64), (7, 128), (8, 64), (8, 256)]  # (top_k, experts)
 TS = [1, 3, 17, 64, 65, 300]
 _layers = {}
 
