@@ -87,22 +87,20 @@ def test_forward_largest_shapes(H, I, T):
 
 # Hash layers above 64 tokens at hidden sizes that are not multiples of 512:
 # the hash router's last row piece is partly past the hidden size on some
-# lanes (those lanes read in-range addresses and add zero products). Ids
-# bit-exact with the table, weights within 1e-5, every token's output
-# against the oracle.
-@pytest.mark.parametrize("T", [65, 200])
-@pytest.mark.parametrize("H,I", SHAPES)
-def test_hash_odd_hidden(H, I, T):
+# lanes (those lanes read in-range addresses and add zero products); and at
+# the largest hidden sizes (8064, 8192), where it requests one expert's row
+# at a time. Ids bit-exact with the table, weights within 1e-5, every
+# token's output against the oracle.
+def _check_hash(wl, T):
     import dataclasses
 
     import oracle
 
-    wl, L, D, cfg = _layer(H, I)
-    wlh = dataclasses.replace(wl, name=f"h{H}i{I}hash", hash_layer=True)
+    wlh = dataclasses.replace(wl, name=f"{wl.name}hash", hash_layer=True)
     Lh = synth.make_layer(wlh)
     Dh = mx.DeviceLayer.from_host(Lh, DEV)
     cfgh = mx.config_of(wlh)
-    print(f"[hash H={H} I={I} T={T} schedule {mx.forward_schedule(cfgh, T, hash_layer=True)}]", flush=True)
+    print(f"[hash H={wl.H} I={wl.I} T={T} schedule {mx.forward_schedule(cfgh, T, hash_layer=True)}]", flush=True)
     xh = synth.make_tokens(wlh, rep=T + 5, T=T)
     tid_h = synth.make_token_ids(wlh, rep=T + 5, T=T)
     x = mx.bf16_from_numpy(xh, DEV)
@@ -113,4 +111,17 @@ def test_hash_odd_hidden(H, I, T):
     assert np.array_equal(ids.cpu().numpy(), Lh.tid2eid[tid_h])
     assert np.array_equal(r["ids"], Lh.tid2eid[tid_h])
     assert np.abs(w.cpu().numpy() - r["w"]).max() <= 1e-5
-    assert_outputs_close(out.cpu().numpy(), r["out"], f"hash H={H} I={I} T={T}")
+    assert_outputs_close(out.cpu().numpy(), r["out"], f"hash H={wl.H} I={wl.I} T={T}")
+
+
+@pytest.mark.parametrize("T", [65, 200])
+@pytest.mark.parametrize("H,I", SHAPES)
+def test_hash_odd_hidden(H, I, T):
+    _check_hash(_layer(H, I)[0], T)
+
+
+@pytest.mark.parametrize("T", [65, 130])
+@pytest.mark.parametrize("H,I", [(8192, 256), (8064, 384)])
+def test_hash_largest_hidden(H, I, T):
+    wl = synth.Workload(f"bigh{H}x{I}", T=130, H=H, E=8, k=2, I=I, V=900, seed=H + 5 * I)
+    _check_hash(wl, T)
